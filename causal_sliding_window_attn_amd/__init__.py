@@ -1,0 +1,237 @@
+"""Causal sliding-window attention on AMD MI355X (gfx950): thin Python binding of libswattn.so.
+
+Every step of the computation runs in the HIP kernels behind the C ABI (include/swattn.h); this
+module only checks tensor metadata, allocates outputs/workspaces with torch and passes raw device
+pointers plus torch's current HIP stream.  The functions ``attn_*`` mirror the C entry points one to
+one; ``attention`` (autograd) and ``KVCache`` (Engine prefill/decode) are conveniences built on them.
+
+Operations: the windowed attention kernel of the "nanochat: GPT-2-grade LLM for <<$100" post
+(web3.cnoyu.life, "Jan29" entry; list of the largest improvements, item 1) and the KV-cache Engine's
+prefill and decode (followin.io walkthrough, section "Pretraining", Engine paragraph).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import SWATTN_BF16, SWATTN_F32, check, last_error, load
+
+__all__ = [
+    "attn_abi_version", "attn_last_error", "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes",
+    "attn_prefill", "attn_kv_append", "attn_decode", "attn_decode_workspace_bytes", "attention",
+    "KVCache", "FULL",
+]
+
+FULL = 2 ** 31 - 1  # a window that is never smaller than the sequence: full causal attention
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _win(window, n: int) -> int:
+    if window is None:
+        return FULL
+    window = int(window)
+    if window < 1:
+        raise ValueError("window must be >= 1 (None = full causal)")
+    return min(window, FULL)
+
+
+def attn_abi_version() -> int:
+    return load().attn_abi_version()
+
+
+def attn_last_error() -> str:
+    return last_error()
+
+
+def attn_bwd_workspace_bytes(B: int, H: int, T: int, D: int) -> int:
+    return load().attn_bwd_workspace_bytes(B, H, T, D)
+
+
+def attn_decode_workspace_bytes(B: int, H: int, Lcap: int, D: int) -> int:
+    return load().attn_decode_workspace_bytes(B, H, Lcap, D)
+
+
+def attn_fwd(q, k, v, o=None, lse=None, window=None, want_lse=True):
+    """Forward over [B, T, H, D] (bf16 or fp32).  Returns (o, lse[B, H, T] float32 or None)."""
+    B, T, H, D = q.shape
+    dt = q.dtype
+    if dt not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"q must be bfloat16 or float32 (got {dt})")
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, n, (B, T, H, D), dt)
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", (B, T, H, D), dt)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, T), device=q.device, dtype=torch.float32)
+    if lse is not None:
+        _need(lse, "lse", (B, H, T), torch.float32)
+    rc = load().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse), B, H, T,
+                         D, _win(window, T), SWATTN_F32 if dt == torch.float32 else SWATTN_BF16,
+                         _stream(q))
+    check(rc, "attn_fwd")
+    return o, lse
+
+
+def attn_bwd(q, k, v, o, lse, dout, window=None, dq=None, dk=None, dv=None, ws=None):
+    """Backward (bf16).  Returns (dq, dk, dv)."""
+    B, T, H, D = q.shape
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _need(t, n, (B, T, H, D), torch.bfloat16)
+    _need(lse, "lse", (B, H, T), torch.float32)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _need(t, n, (B, T, H, D), torch.bfloat16)
+    need = attn_bwd_workspace_bytes(B, H, T, D)
+    if ws is None:
+        ws = torch.empty(need, device=q.device, dtype=torch.uint8)
+    rc = load().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                         dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, T, D,
+                         _win(window, T), SWATTN_BF16, ws.data_ptr(), ws.numel() * ws.element_size(),
+                         _stream(q))
+    check(rc, "attn_bwd")
+    return dq, dk, dv
+
+
+def attn_prefill(q, kcache, vcache, lens, o=None, lse=None, window=None, want_lse=False):
+    """Ragged prefill: q [B, Tq, H, D], caches [B, Lcap, H, D], lens int32 [B] on the device."""
+    B, Tq, H, D = q.shape
+    Lcap = kcache.shape[1]
+    _need(q, "q", None, torch.bfloat16)
+    _need(kcache, "kcache", (B, Lcap, H, D), torch.bfloat16)
+    _need(vcache, "vcache", (B, Lcap, H, D), torch.bfloat16)
+    _need(lens, "lens", (B,), torch.int32)
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", (B, Tq, H, D), torch.bfloat16)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Tq), device=q.device, dtype=torch.float32)
+    if lse is not None:
+        _need(lse, "lse", (B, H, Tq), torch.float32)
+    rc = load().attn_prefill(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), lens.data_ptr(),
+                             o.data_ptr(), _ptr(lse), B, H, Tq, Lcap, D, _win(window, Tq),
+                             _stream(q))
+    check(rc, "attn_prefill")
+    return o, lse
+
+
+def attn_kv_append(kcache, vcache, knew, vnew, pos):
+    """kcache[b, pos[b]] = knew[b] (and v); pos int32 [B] on the device."""
+    B, Lcap, H, D = kcache.shape
+    _need(kcache, "kcache", None, torch.bfloat16)
+    _need(vcache, "vcache", (B, Lcap, H, D), torch.bfloat16)
+    _need(knew, "knew", (B, H, D), torch.bfloat16)
+    _need(vnew, "vnew", (B, H, D), torch.bfloat16)
+    _need(pos, "pos", (B,), torch.int32)
+    rc = load().attn_kv_append(kcache.data_ptr(), vcache.data_ptr(), knew.data_ptr(),
+                               vnew.data_ptr(), pos.data_ptr(), B, H, Lcap, D, _stream(kcache))
+    check(rc, "attn_kv_append")
+
+
+def attn_decode(q, kcache, vcache, lens, o=None, lse=None, window=None, ws=None, want_lse=False):
+    """Decode: q [B, H, D], caches [B, Lcap, H, D], lens int32 [B] (including the new token)."""
+    B, H, D = q.shape
+    Lcap = kcache.shape[1]
+    _need(q, "q", None, torch.bfloat16)
+    _need(kcache, "kcache", (B, Lcap, H, D), torch.bfloat16)
+    _need(vcache, "vcache", (B, Lcap, H, D), torch.bfloat16)
+    _need(lens, "lens", (B,), torch.int32)
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", (B, H, D), torch.bfloat16)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), device=q.device, dtype=torch.float32)
+    if lse is not None:
+        _need(lse, "lse", (B, H), torch.float32)
+    need = attn_decode_workspace_bytes(B, H, Lcap, D)
+    if ws is None:
+        ws = torch.empty(need, device=q.device, dtype=torch.uint8)
+    rc = load().attn_decode(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), lens.data_ptr(),
+                            o.data_ptr(), _ptr(lse), B, H, Lcap, D, _win(window, Lcap),
+                            ws.data_ptr(), ws.numel() * ws.element_size(), _stream(q))
+    check(rc, "attn_decode")
+    return o, lse
+
+
+class _Attention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, window):
+        o, lse = attn_fwd(q, k, v, window=window)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.window = window
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = attn_bwd(q, k, v, o, lse, do.contiguous(), window=ctx.window)
+        return dq, dk, dv, None
+
+
+def attention(q, k, v, window=None):
+    """Differentiable windowed causal attention over [B, T, H, D] bf16 tensors."""
+    return _Attention.apply(q, k, v, window)
+
+
+class KVCache:
+    """Per-layer KV cache [n_layer][B, Lcap, H, D] bf16 with Engine prefill / decode.
+
+    ``lens`` (device int32 [B]) counts the cached tokens; ``decode`` appends the new token at row
+    ``lens`` and then attends with ``lens + 1`` keys.  The same ``lens`` serves every layer, so
+    advance it with ``step()`` once per generated token after the last layer.
+    """
+
+    def __init__(self, n_layer, B, Lcap, H, D, device="cuda", windows=None):
+        self.n_layer, self.B, self.Lcap, self.H, self.D = n_layer, B, Lcap, H, D
+        shape = (n_layer, B, Lcap, H, D)
+        self.k = torch.zeros(shape, device=device, dtype=torch.bfloat16)
+        self.v = torch.zeros(shape, device=device, dtype=torch.bfloat16)
+        self.lens = torch.zeros(B, device=device, dtype=torch.int32)
+        self.windows = list(windows) if windows is not None else [None] * n_layer
+        self._ws = torch.empty(attn_decode_workspace_bytes(B, H, Lcap, D), device=device,
+                               dtype=torch.uint8)
+        self._next = torch.empty_like(self.lens)
+
+    def prefill(self, layer, q, k, v, lens):
+        """Write prompts (padded [B, Tq, H, D]) into the cache and attend causally."""
+        Tq = q.shape[1]
+        if Tq > self.Lcap:
+            raise ValueError("prompt longer than the cache")
+        self.k[layer, :, :Tq].copy_(k)
+        self.v[layer, :, :Tq].copy_(v)
+        self.lens.copy_(lens)
+        o, _ = attn_prefill(q, self.k[layer], self.v[layer], self.lens,
+                            window=self.windows[layer])
+        return o
+
+    def decode(self, layer, q, k_new, v_new):
+        torch.add(self.lens, 1, out=self._next)
+        attn_kv_append(self.k[layer], self.v[layer], k_new, v_new, self.lens)
+        o, _ = attn_decode(q, self.k[layer], self.v[layer], self._next,
+                           window=self.windows[layer], ws=self._ws)
+        return o
+
+    def step(self):
+        self.lens.add_(1)

@@ -1,0 +1,264 @@
+// C ABI of libswattn.so (declared in include/swattn.h): argument validation, workspace sizing and
+// kernel launch on the caller's stream.  Every check runs before the first HIP call, so a bad
+// call fails identically with or without a GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/swattn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return SWATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_ptr(const void* p, const char* name, bool nullable = false) {
+  if (!p) return nullable ? SWATTN_OK : fail(SWATTN_EINVAL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(SWATTN_EINVAL, "%s is not 16-byte aligned", name);
+  return SWATTN_OK;
+}
+
+int check_dims(const char* what, int B, int H, int T, const char* tname, int D, int window) {
+  if (B < 1) return fail(SWATTN_EINVAL, "%s: B = %d must be >= 1", what, B);
+  if (H < 1) return fail(SWATTN_EINVAL, "%s: H = %d must be >= 1", what, H);
+  if (T < 1) return fail(SWATTN_EINVAL, "%s: %s = %d must be >= 1", what, tname, T);
+  if (window < 1) return fail(SWATTN_EINVAL, "%s: window = %d must be >= 1", what, window);
+  if (D != 64 && D != 128)
+    return fail(SWATTN_EUNSUPPORTED, "%s: head dim D = %d is not supported (64 or 128)", what, D);
+  // launch grids: B and H are grid dimensions of the decode (<= 65535 each); the tiled kernels
+  // launch (T / 128 + 1) * B * H workgroups on one 31-bit grid dimension
+  if (B > 65535 || H > 65535)
+    return fail(SWATTN_EINVAL, "%s: B = %d and H = %d must be <= 65535", what, B, H);
+  if ((int64_t)(T / 128 + 1) * B * H >= ((int64_t)1 << 31))
+    return fail(SWATTN_EINVAL, "%s: (%s/128 + 1) * B * H exceeds 2^31", what, tname);
+  return SWATTN_OK;
+}
+
+#define TRY(x)                       \
+  do {                               \
+    int rc_ = (x);                   \
+    if (rc_ != SWATTN_OK) return rc_; \
+  } while (0)
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SWATTN_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+float scale_log2_for(int D) { return (float)(1.4426950408889634 / sqrt((double)D)); }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int decode_chunks(int Lcap) { return (Lcap + swattn::kDecodeChunk - 1) / swattn::kDecodeChunk; }
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return SWATTN_ABI_VERSION; }
+
+const char* attn_last_error(void) { return g_err; }
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int T,
+             int D, int window, int dtype, void* stream) {
+  TRY(check_dims("attn_fwd", B, H, T, "T", D, window));
+  if (dtype != SWATTN_BF16 && dtype != SWATTN_F32)
+    return fail(SWATTN_EUNSUPPORTED, "attn_fwd: dtype %d is not supported", dtype);
+  TRY(check_ptr(q, "q"));
+  TRY(check_ptr(k, "k"));
+  TRY(check_ptr(v, "v"));
+  TRY(check_ptr(o, "o"));
+  TRY(check_ptr(lse, "lse", true));
+  swattn::FwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.lens = nullptr;
+  a.q_bstride = a.kv_bstride = (int64_t)T * H * D;
+  a.row_stride = H * D;
+  a.H = H;
+  a.BH = B * H;
+  a.D = D;
+  a.T = T;
+  a.kv_len = T;
+  a.window = window;
+  a.lse_T = T;
+  a.scale_log2 = scale_log2_for(D);
+  (void)hipGetLastError();
+  return hip_status(swattn::launch_fwd(a, dtype == SWATTN_F32, static_cast<hipStream_t>(stream)),
+                    "attn_fwd launch");
+}
+
+size_t attn_bwd_workspace_bytes(int B, int H, int T, int D) {
+  if (B < 1 || H < 1 || T < 1 || (D != 64 && D != 128)) return 0;
+  return align256((size_t)B * H * T * sizeof(float));
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, int B, int H, int T, int D, int window,
+             int dtype, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_dims("attn_bwd", B, H, T, "T", D, window));
+  if (dtype != SWATTN_BF16)
+    return fail(SWATTN_EUNSUPPORTED, "attn_bwd: only bf16 (dtype 0) is implemented, got %d", dtype);
+  TRY(check_ptr(q, "q"));
+  TRY(check_ptr(k, "k"));
+  TRY(check_ptr(v, "v"));
+  TRY(check_ptr(o, "o"));
+  TRY(check_ptr(lse, "lse"));
+  TRY(check_ptr(dout, "dout"));
+  TRY(check_ptr(dq, "dq"));
+  TRY(check_ptr(dk, "dk"));
+  TRY(check_ptr(dv, "dv"));
+  const size_t need = attn_bwd_workspace_bytes(B, H, T, D);
+  if (!ws) return fail(SWATTN_EWORKSPACE, "attn_bwd: workspace is NULL (%zu bytes needed)", need);
+  if (!aligned16(ws)) return fail(SWATTN_EINVAL, "attn_bwd: workspace is not 16-byte aligned");
+  if (ws_bytes < need)
+    return fail(SWATTN_EWORKSPACE, "attn_bwd: workspace of %zu bytes < %zu needed", ws_bytes, need);
+  swattn::BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.lse = lse;
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.delta = static_cast<float*>(ws);
+  a.bstride = (int64_t)T * H * D;
+  a.row_stride = H * D;
+  a.H = H;
+  a.BH = B * H;
+  a.D = D;
+  a.T = T;
+  a.window = window;
+  a.scale = (float)(1.0 / sqrt((double)D));
+  a.scale_log2 = scale_log2_for(D);
+  (void)hipGetLastError();
+  return hip_status(swattn::launch_bwd(a, static_cast<hipStream_t>(stream)), "attn_bwd launch");
+}
+
+int attn_prefill(const void* q, const void* kcache, const void* vcache, const int* lens, void* o,
+                 float* lse, int B, int H, int Tq, int Lcap, int D, int window, void* stream) {
+  TRY(check_dims("attn_prefill", B, H, Tq, "Tq", D, window));
+  if (Lcap < 1) return fail(SWATTN_EINVAL, "attn_prefill: Lcap = %d must be >= 1", Lcap);
+  TRY(check_ptr(q, "q"));
+  TRY(check_ptr(kcache, "kcache"));
+  TRY(check_ptr(vcache, "vcache"));
+  if (!lens) return fail(SWATTN_EINVAL, "lens is NULL");
+  if (reinterpret_cast<uintptr_t>(lens) & 3u) return fail(SWATTN_EINVAL, "lens is not 4-byte aligned");
+  TRY(check_ptr(o, "o"));
+  TRY(check_ptr(lse, "lse", true));
+  swattn::FwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(kcache);
+  a.v = static_cast<const uint16_t*>(vcache);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.lens = lens;
+  a.q_bstride = (int64_t)Tq * H * D;
+  a.kv_bstride = (int64_t)Lcap * H * D;
+  a.row_stride = H * D;
+  a.H = H;
+  a.BH = B * H;
+  a.D = D;
+  a.T = Tq;
+  a.kv_len = Tq < Lcap ? Tq : Lcap;
+  a.window = window;
+  a.lse_T = Tq;
+  a.scale_log2 = scale_log2_for(D);
+  (void)hipGetLastError();
+  return hip_status(swattn::launch_fwd(a, false, static_cast<hipStream_t>(stream)),
+                    "attn_prefill launch");
+}
+
+int attn_kv_append(void* kcache, void* vcache, const void* knew, const void* vnew, const int* pos,
+                   int B, int H, int Lcap, int D, void* stream) {
+  TRY(check_dims("attn_kv_append", B, H, Lcap, "Lcap", D, 1));
+  TRY(check_ptr(kcache, "kcache"));
+  TRY(check_ptr(vcache, "vcache"));
+  TRY(check_ptr(knew, "knew"));
+  TRY(check_ptr(vnew, "vnew"));
+  if (!pos) return fail(SWATTN_EINVAL, "pos is NULL");
+  if (reinterpret_cast<uintptr_t>(pos) & 3u) return fail(SWATTN_EINVAL, "pos is not 4-byte aligned");
+  swattn::AppendArgs a{};
+  a.kc = static_cast<uint16_t*>(kcache);
+  a.vc = static_cast<uint16_t*>(vcache);
+  a.kn = static_cast<const uint16_t*>(knew);
+  a.vn = static_cast<const uint16_t*>(vnew);
+  a.pos = pos;
+  a.B = B;
+  a.H = H;
+  a.D = D;
+  a.Lcap = Lcap;
+  (void)hipGetLastError();
+  return hip_status(swattn::launch_append(a, static_cast<hipStream_t>(stream)),
+                    "attn_kv_append launch");
+}
+
+size_t attn_decode_workspace_bytes(int B, int H, int Lcap, int D) {
+  if (B < 1 || H < 1 || Lcap < 1 || (D != 64 && D != 128)) return 0;
+  const size_t slots = (size_t)B * H * decode_chunks(Lcap);
+  return align256(slots * D * sizeof(float)) + align256(slots * 2 * sizeof(float));
+}
+
+int attn_decode(const void* q, const void* kcache, const void* vcache, const int* lens, void* o,
+                float* lse, int B, int H, int Lcap, int D, int window, void* ws, size_t ws_bytes,
+                void* stream) {
+  TRY(check_dims("attn_decode", B, H, Lcap, "Lcap", D, window));
+  TRY(check_ptr(q, "q"));
+  TRY(check_ptr(kcache, "kcache"));
+  TRY(check_ptr(vcache, "vcache"));
+  if (!lens) return fail(SWATTN_EINVAL, "lens is NULL");
+  if (reinterpret_cast<uintptr_t>(lens) & 3u) return fail(SWATTN_EINVAL, "lens is not 4-byte aligned");
+  TRY(check_ptr(o, "o"));
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(SWATTN_EINVAL, "lse is not 4-byte aligned");
+  const size_t need = attn_decode_workspace_bytes(B, H, Lcap, D);
+  if (!ws) return fail(SWATTN_EWORKSPACE, "attn_decode: workspace is NULL (%zu bytes needed)", need);
+  if (!aligned16(ws)) return fail(SWATTN_EINVAL, "attn_decode: workspace is not 16-byte aligned");
+  if (ws_bytes < need)
+    return fail(SWATTN_EWORKSPACE, "attn_decode: workspace of %zu bytes < %zu needed", ws_bytes,
+                need);
+  const int nc_max = decode_chunks(Lcap);
+  const size_t slots = (size_t)B * H * nc_max;
+  swattn::DecArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kc = static_cast<const uint16_t*>(kcache);
+  a.vc = static_cast<const uint16_t*>(vcache);
+  a.lens = lens;
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.ws_o = static_cast<float*>(ws);
+  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + align256(slots * D * sizeof(float)));
+  a.B = B;
+  a.H = H;
+  a.D = D;
+  a.Lcap = Lcap;
+  a.window = window;
+  a.nc_max = nc_max;
+  a.scale_log2 = scale_log2_for(D);
+  (void)hipGetLastError();
+  return hip_status(swattn::launch_decode(a, static_cast<hipStream_t>(stream)),
+                    "attn_decode launch");
+}
+
+}  // extern "C"

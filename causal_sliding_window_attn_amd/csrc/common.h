@@ -1,0 +1,133 @@
+// Device-side building blocks shared by the attention kernels (gfx950 / CDNA4, wave64).
+//
+// MFMA fragment conventions used everywhere (v_mfma_f32_32x32x16_bf16):
+//   A operand (32 x 16): lane l holds row (l % 32) and 8 consecutive k-slots of half (l / 32).
+//   B operand (16 x 32): lane l holds column (l % 32) and the same 8 k-slots of half (l / 32).
+//   C (32 x 32, fp32):   lane l holds column (l % 32); accumulator r holds row
+//                        8 * (r / 4) + 4 * (l / 32) + (r % 4).
+// The hardware sums over (half, slot); which logical k a slot stands for is our choice, as long
+// as A and B agree.  We exploit that twice: contraction over D uses slot s of half h = element
+// 8h + s of a 16-wide chunk, and contraction over the sequence reuses the C layout of a previous
+// product directly as the B operand (slot s of half h = row 8 * (s / 4) + 4h + (s % 4) of a
+// 16-row step), with the other operand's LDS copy laid out in the same permuted order.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32_f32(float a, float b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Round-to-nearest-even fp32 -> bf16 pair (hardware v_cvt_pk_bf16_f32), packed in 32 bits.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Eight fp32 values (accumulator slots 8u .. 8u+7) -> one bf16x8 B-operand fragment.
+__device__ __forceinline__ uint4 pack_frag(const f32x16& acc, int u) {
+  uint4 r;
+  r.x = pack_bf16x2(acc[8 * u + 0], acc[8 * u + 1]);
+  r.y = pack_bf16x2(acc[8 * u + 2], acc[8 * u + 3]);
+  r.z = pack_bf16x2(acc[8 * u + 4], acc[8 * u + 5]);
+  r.w = pack_bf16x2(acc[8 * u + 6], acc[8 * u + 7]);
+  return r;
+}
+
+// v_permlane32_swap(x, x) returns {x of lanes 0-31 | x of lane l-32, x of lane l+32 | x of lanes
+// 32-63}: each lane sees its own value in one slot and lane (l ^ 32)'s in the other.
+__device__ __forceinline__ float max_with_partner(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_with_partner(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
+__device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// ---------------------------------------------------------------------------------------------
+// LDS tile layouts for a tile of R sequence rows x D features (bf16).
+//
+// Row-major tile ("normal"): row r, 16-byte chunk c stored at chunk (c ^ (r % (D/8))) of row r,
+// so the 32 rows read by one MFMA operand load fall on distinct banks.
+//
+// Transposed tile: feature d is a row of R sequence positions.  Inside every group of 16 rows the
+// sequence position k is stored at slot perm16(k) = 8 * ((k >> 2) & 1) + 4 * (k >> 3) + (k & 3),
+// so the 8 positions one lane half feeds to an MFMA sit in one 16-byte chunk; chunk index is
+// XOR-swizzled with (d % 8).
+// ---------------------------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int normal_off(int row, int chunk) {
+  return row * D + 8 * (chunk ^ (row & (D / 8 - 1)));
+}
+
+template <int R>
+__device__ __forceinline__ int trans_off(int d, int chunk) {
+  return d * R + 8 * (chunk ^ (d & 7));
+}
+
+// Store 4 consecutive sequence rows (4g .. 4g+3) x 8 features (8c .. 8c+7), held as four 16-byte
+// row chunks, into both the normal and (optionally) the transposed LDS tile.
+template <int D, int R, bool NORMAL, bool TRANS>
+__device__ __forceinline__ void store_group(uint16_t* sN, uint16_t* sT, int g, int c,
+                                            const uint4 (&x)[4]) {
+  if (NORMAL) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4*>(sN + normal_off<D>(4 * g + i, c)) = x[i];
+  }
+  if (TRANS) {
+    // Rows 4g..4g+3 occupy 4 consecutive transposed slots: group-of-16 (g / 4), lane half (g & 1),
+    // j' = (g >> 1) & 1.
+    const int chunk = 2 * (g >> 2) + (g & 1);
+    const int sub = ((g >> 1) & 1) * 4;
+    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&x[0]);
+    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&x[1]);
+    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&x[2]);
+    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&x[3]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint2 lo, hi;  // feature 8c + 2e (low halves) and 8c + 2e + 1 (high halves)
+      lo.x = (w0[e] & 0xffffu) | (w1[e] << 16);
+      lo.y = (w2[e] & 0xffffu) | (w3[e] << 16);
+      hi.x = (w0[e] >> 16) | (w1[e] & 0xffff0000u);
+      hi.y = (w2[e] >> 16) | (w3[e] & 0xffff0000u);
+      const int d0 = 8 * c + 2 * e;
+      *reinterpret_cast<uint2*>(sT + trans_off<R>(d0, chunk) + sub) = lo;
+      *reinterpret_cast<uint2*>(sT + trans_off<R>(d0 + 1, chunk) + sub) = hi;
+    }
+  }
+}
+
+}  // namespace swattn

@@ -1,0 +1,222 @@
+// Engine decode and KV-cache append for gfx950.
+//
+// Operation: the Engine's decode phase over its KV cache (followin.io walkthrough, section
+// "Pretraining", Engine paragraph; nanochat launch post, feature list): each sequence's one new
+// query attends to cache rows max(0, p - w + 1) .. p with p = L - 1, where L counts the cached
+// tokens including the new one.
+//
+// Design: decode is a matrix-vector product per (sequence, head) -- about one flop per byte of
+// cache -- so it is HBM-bound and uses VALU dot products, not MFMA.  The visible key range is
+// split into 64-key chunks; one wave per (chunk, head, sequence) issues all of its chunk's K and V
+// loads (16-byte, D/8 lanes per key row) before using any of them, reduces q.k over the row's
+// lanes with DPP, and writes the chunk's (max, sum, unnormalised output) in fp32.  A second
+// kernel merges the chunks with the log-sum-exp rule and writes O (bf16) and LSE.
+#include "common.h"
+#include "launch.h"
+
+namespace swattn {
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of N lanes (N in {8, 16}); every lane of the group receives the sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N == 16) {
+    x += dpp_f<0x128>(x);  // row_ror:8
+    x += dpp_f<0x124>(x);  // row_ror:4
+    x += dpp_f<0x122>(x);  // row_ror:2
+    x += dpp_f<0x121>(x);  // row_ror:1
+  } else {
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 1);
+  }
+  return x;
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_split_kernel(DecArgs p) {
+  constexpr int LPK = D / 8;      // lanes per key row (16 bytes each)
+  constexpr int KPI = 64 / LPK;   // key rows per load instruction
+  constexpr int C = kDecodeChunk;
+  constexpr int NL = C / KPI;     // loads per lane per tensor
+
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int L = min(max(p.lens[b], 0), p.Lcap);
+  if (L == 0) return;
+  const int nvis = min(p.window, L);
+  const int j0 = L - nvis;
+  const int nc = (nvis + C - 1) / C;
+  if (c >= nc) return;
+  const int cs = j0 + c * C;
+  const int ce = min(cs + C, L);
+
+  const int lane = threadIdx.x;
+  const int kq = lane / LPK, dc = lane % LPK;
+  const int64_t rowstride = (int64_t)p.H * D;
+  const uint16_t* kb = p.kc + ((int64_t)b * p.Lcap) * rowstride + h * D + 8 * dc;
+  const uint16_t* vb = p.vc + ((int64_t)b * p.Lcap) * rowstride + h * D + 8 * dc;
+
+  uint4 kr[NL], vr[NL];
+#pragma unroll
+  for (int r = 0; r < NL; ++r) {
+    const int j = cs + r * KPI + kq;
+    if (j < ce) {
+      kr[r] = ldg16(kb + j * rowstride);
+      vr[r] = ldg16(vb + j * rowstride);
+    } else {
+      kr[r] = make_uint4(0, 0, 0, 0);
+      vr[r] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  float qv[8];
+  {
+    const uint4 qq = ldg16(p.q + ((int64_t)b * p.H + h) * D + 8 * dc);
+    const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qq);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qv[2 * e] = bf16_lo(qw[e]) * p.scale_log2;
+      qv[2 * e + 1] = bf16_hi(qw[e]) * p.scale_log2;
+    }
+  }
+
+  float sc[NL];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < NL; ++r) {
+    const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kr[r]);
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(qv[2 * e], bf16_lo(kw[e]), acc);
+      acc = fmaf(qv[2 * e + 1], bf16_hi(kw[e]), acc);
+    }
+    acc = group_sum<LPK>(acc);
+    const int j = cs + r * KPI + kq;
+    sc[r] = (j < ce) ? acc : -INFINITY;
+    mx = fmaxf(mx, sc[r]);
+  }
+  // chunk max over all key rows (groups of LPK lanes differ in kq)
+#pragma unroll
+  for (int off = LPK; off < 32; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  mx = max_with_partner(mx);
+
+  float lsum = 0.f;
+  float ov[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ov[e] = 0.f;
+#pragma unroll
+  for (int r = 0; r < NL; ++r) {
+    const float pr = __builtin_amdgcn_exp2f(sc[r] - mx);
+    lsum += pr;
+    const uint32_t* vw = reinterpret_cast<const uint32_t*>(&vr[r]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ov[2 * e] = fmaf(pr, bf16_lo(vw[e]), ov[2 * e]);
+      ov[2 * e + 1] = fmaf(pr, bf16_hi(vw[e]), ov[2 * e + 1]);
+    }
+  }
+  // reduce over the key-row groups: lanes with equal dc
+#pragma unroll
+  for (int off = LPK; off < 32; off <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ov[e] += __shfl_xor(ov[e], off);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ov[e] = sum_with_partner(ov[e]);
+  // lsum: each group of LPK lanes holds the same partial (one per kq); count it once per group
+  lsum = (dc == 0) ? lsum : 0.f;
+  for (int off = 1; off < 32; off <<= 1) lsum += __shfl_xor(lsum, off);
+  lsum = sum_with_partner(lsum);
+
+  const int64_t slot = ((int64_t)b * p.H + h) * p.nc_max + c;
+  if (kq == 0) {
+    float4* dst = reinterpret_cast<float4*>(p.ws_o + slot * D + 8 * dc);
+    dst[0] = make_float4(ov[0], ov[1], ov[2], ov[3]);
+    dst[1] = make_float4(ov[4], ov[5], ov[6], ov[7]);
+  }
+  if (lane == 0) {
+    p.ws_ml[2 * slot] = mx;
+    p.ws_ml[2 * slot + 1] = lsum;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_combine_kernel(DecArgs p) {
+  constexpr int DPL = D / 64;  // features per lane
+  const int bh = blockIdx.x;
+  const int b = bh / p.H;
+  const int lane = threadIdx.x;
+  const int L = min(max(p.lens[b], 0), p.Lcap);
+  uint16_t* ob = p.o + (int64_t)bh * D + lane * DPL;
+  if (L == 0) {
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) ob[e] = 0;
+    if (p.lse && lane == 0) p.lse[bh] = -INFINITY;
+    return;
+  }
+  const int nvis = min(p.window, L);
+  const int nc = (nvis + kDecodeChunk - 1) / kDecodeChunk;
+  const int64_t slot0 = (int64_t)bh * p.nc_max;
+  float M = -INFINITY;
+  for (int c = 0; c < nc; ++c) M = fmaxf(M, p.ws_ml[2 * (slot0 + c)]);
+  float Ls = 0.f, acc[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+  for (int c = 0; c < nc; ++c) {
+    const float sc = __builtin_amdgcn_exp2f(p.ws_ml[2 * (slot0 + c)] - M);
+    Ls = fmaf(p.ws_ml[2 * (slot0 + c) + 1], sc, Ls);
+    const float* src = p.ws_o + (slot0 + c) * D + lane * DPL;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] = fmaf(src[e], sc, acc[e]);
+  }
+  const float inv = 1.f / Ls;
+  if constexpr (DPL == 2) {
+    *reinterpret_cast<uint32_t*>(ob) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  } else {
+    ob[0] = __builtin_bit_cast(uint16_t, (__bf16)(acc[0] * inv));
+  }
+  if (p.lse && lane == 0) p.lse[bh] = (M + __log2f(Ls)) * kLn2;
+}
+
+__global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs p) {
+  const int chunks = p.D / 8;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)p.B * p.H * chunks) return;
+  const int c = (int)(idx % chunks);
+  const int bh = (int)(idx / chunks);
+  const int b = bh / p.H, h = bh % p.H;
+  const int pos = p.pos[b];
+  if (pos < 0 || pos >= p.Lcap) return;
+  const int64_t dst = (((int64_t)b * p.Lcap + pos) * p.H + h) * p.D + 8 * c;
+  const int64_t src = (int64_t)bh * p.D + 8 * c;
+  *reinterpret_cast<uint4*>(p.kc + dst) = ldg16(p.kn + src);
+  *reinterpret_cast<uint4*>(p.vc + dst) = ldg16(p.vn + src);
+}
+
+template <int D>
+static hipError_t launch_decode_d(const DecArgs& a, hipStream_t s) {
+  const int vis_max = a.window < a.Lcap ? a.window : a.Lcap;
+  const int nc = (vis_max + kDecodeChunk - 1) / kDecodeChunk;
+  hipLaunchKernelGGL((decode_split_kernel<D>), dim3(nc, a.H, a.B), dim3(64), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.H), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecArgs& a, hipStream_t s) {
+  return a.D == 64 ? launch_decode_d<64>(a, s) : launch_decode_d<128>(a, s);
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.B * a.H * (a.D / 8);
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  hipLaunchKernelGGL(kv_append_kernel, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace swattn

@@ -1,0 +1,341 @@
+// Forward attention (training forward and Engine prefill) for gfx950.
+//
+// Operation: exact softmax causal attention with a per-layer sliding window -- the attention
+// kernel with a window_size keyword credited in the "nanochat: GPT-2-grade LLM for <<$100" post
+// (web3.cnoyu.life, "Jan29" entry), list of the largest improvements, item 1; the same kernel
+// serves the Engine's prefill phase (followin.io walkthrough, section "Pretraining", Engine
+// paragraph).  Query i sees key j iff j <= i and i - j < w; scale 1/sqrt(D).
+//
+// Design (bf16): one workgroup = NW waves x 32 queries of one (batch, head).  Each wave keeps its
+// queries' Q in registers as MFMA B fragments and computes S^T = K Q^T per 64-key tile, so a lane
+// owns one query column: the row max / row sum of the online softmax are lane-local plus a single
+// v_permlane32_swap.  O^T = V^T P^T reuses the S^T accumulators (rounded to bf16) directly as the
+// B operand; V is written to LDS transposed, in the matching permuted key order.  K/V tiles
+// outside [q0 - w + 1, q_end] are never loaded; per wave, tiles wholly outside the window are
+// skipped and only tiles crossing the diagonal or the window edge evaluate the mask.
+#include "common.h"
+#include "launch.h"
+
+namespace swattn {
+
+constexpr int kFwdBC = 64;  // keys per tile
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs p) {
+  constexpr int BR = 32 * NW;
+  constexpr int BC = kFwdBC;
+  constexpr int NT = 64 * NW;
+  constexpr int DK = D / 16;             // MFMA k-steps over D
+  constexpr int MB = D / 32;             // 32-row blocks of O^T
+  constexpr int NB = BC / 32;            // 32-key blocks per tile
+  constexpr int GROUPS = (BC / 4) * (D / 8);  // (4 keys x 8 features) load items per tile
+  constexpr int ITEMS = (GROUPS + NT - 1) / NT;
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK[BC * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * BC];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+
+  const int bid = blockIdx.x;
+  const int qt = p.n_qtiles - 1 - bid / p.BH;  // longest query tiles first
+  const int bh = bid % p.BH;
+  const int b = bh / p.H, h = bh % p.H;
+
+  int L = p.kv_len;
+  if (p.lens) L = min(max(p.lens[b], 0), p.kv_len);
+  const int q0 = qt * BR;
+  if (q0 >= L) return;
+  const int w = min(p.window, L);
+  const int kstart = max(0, q0 - w + 1);
+  const int qend = min(q0 + BR, L);
+  const int kt_begin = kstart / BC, kt_end = (qend - 1) / BC;
+
+  const uint16_t* qb = p.q + (int64_t)b * p.q_bstride + h * D;
+  const uint16_t* kb = p.k + (int64_t)b * p.kv_bstride + h * D;
+  const uint16_t* vb = p.v + (int64_t)b * p.kv_bstride + h * D;
+  const int rs = p.row_stride;
+
+  const int qa = q0 + 32 * wave;  // this wave's first query
+  const int qi = qa + l32;        // this lane's query
+  const bool qvalid = qi < L;
+
+  uint4 qf[DK];
+#pragma unroll
+  for (int t = 0; t < DK; ++t)
+    qf[t] = qvalid ? ldg16(qb + (int64_t)qi * rs + 16 * t + 8 * half) : make_uint4(0, 0, 0, 0);
+
+  f32x16 oacc[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) oacc[m] = zero16();
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = p.scale_log2;
+
+  uint4 kr[ITEMS][4], vr[ITEMS][4];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+      const int idx = tid + it * NT;
+      if (idx < GROUPS) {
+        const int g = idx / (D / 8), c = idx % (D / 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = kt * BC + 4 * g + i;
+          if (j < L) {
+            kr[it][i] = ldg16(kb + (int64_t)j * rs + 8 * c);
+            vr[it][i] = ldg16(vb + (int64_t)j * rs + 8 * c);
+          } else {
+            kr[it][i] = make_uint4(0, 0, 0, 0);
+            vr[it][i] = make_uint4(0, 0, 0, 0);
+          }
+        }
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+      const int idx = tid + it * NT;
+      if (idx < GROUPS) {
+        const int g = idx / (D / 8), c = idx % (D / 8);
+        store_group<D, BC, true, false>(sK, nullptr, g, c, kr[it]);
+        store_group<D, BC, false, true>(nullptr, sVt, g, c, vr[it]);
+      }
+    }
+  };
+
+  load_tile(kt_begin);
+  for (int kt = kt_begin; kt <= kt_end; ++kt) {
+    if (kt != kt_begin) __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (kt < kt_end) load_tile(kt + 1);
+
+    const int k_lo = kt * BC, k_hi = k_lo + BC - 1;
+    const int qz = qa + 31;
+    const bool skip = (qa >= L) || (k_lo > qz) || (qa - k_hi >= w);
+    if (skip) continue;
+    const bool need_mask = !(k_hi <= qa && qz - k_lo < w);
+
+    // S^T (keys x queries) for the tile.
+    f32x16 s[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      s[nb] = zero16();
+      const int row = nb * 32 + l32;
+#pragma unroll
+      for (int t = 0; t < DK; ++t) {
+        const uint4 a = *reinterpret_cast<const uint4*>(sK + normal_off<D>(row, 2 * t + half));
+        s[nb] = mfma32(a, qf[t], s[nb]);
+      }
+    }
+
+    // Online softmax in the log2 domain; this lane owns query qi.
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = s[nb][r] * sl2;
+        if (need_mask) {
+          const int key = k_lo + nb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key > qi || qi - key >= w) x = -INFINITY;
+        }
+        s[nb][r] = x;
+        mloc = fmaxf(mloc, x);
+      }
+    }
+    const float m_new = fmaxf(m_run, max_with_partner(mloc));
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float lsum = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(s[nb][r] - m_use);
+        s[nb][r] = e;
+        lsum += e;
+      }
+    }
+    l_run = l_run * alpha + lsum;
+    m_run = m_new;
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[m][r] *= alpha;
+
+    // O^T += V^T P^T
+    uint4 pf[NB][2];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      pf[nb][0] = pack_frag(s[nb], 0);
+      pf[nb][1] = pack_frag(s[nb], 1);
+    }
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      const int d = m * 32 + l32;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const uint4 a =
+              *reinterpret_cast<const uint4*>(sVt + trans_off<BC>(d, 2 * (2 * nb + u) + half));
+          oacc[m] = mfma32(a, pf[nb][u], oacc[m]);
+        }
+    }
+  }
+
+  const float l_tot = sum_with_partner(l_run);
+  if (!qvalid) return;
+  const float inv = 1.f / l_tot;
+  uint16_t* ob = p.o + (int64_t)b * p.q_bstride + h * D + (int64_t)qi * rs;
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint2 st;
+      st.x = pack_bf16x2(oacc[m][4 * j + 0] * inv, oacc[m][4 * j + 1] * inv);
+      st.y = pack_bf16x2(oacc[m][4 * j + 2] * inv, oacc[m][4 * j + 3] * inv);
+      *reinterpret_cast<uint2*>(ob + m * 32 + 8 * j + 4 * half) = st;
+    }
+  if (p.lse && half == 0)
+    p.lse[(int64_t)bh * p.lse_T + qi] = (m_run + __log2f(l_tot)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------------------------
+// fp32 forward (fp32 in, fp32 out, fp32 MFMA v_mfma_f32_32x32x2f32).  Same structure as above;
+// each MFMA k-step carries one value per lane half, so V is read row-major straight from LDS and
+// P^T feeds the PV product one accumulator slot at a time without rounding.
+// ---------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs p) {
+  constexpr int NW = 4, BR = 32 * NW, BC = 32, NT = 64 * NW, MB = D / 32;
+  constexpr int SK = D + 1;  // padded row stride (floats) against bank conflicts
+  __shared__ float sK[BC * SK];
+  __shared__ float sV[BC * D];
+
+  const float* qg = reinterpret_cast<const float*>(p.q);
+  const float* kg = reinterpret_cast<const float*>(p.k);
+  const float* vg = reinterpret_cast<const float*>(p.v);
+  float* og = reinterpret_cast<float*>(p.o);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int bid = blockIdx.x;
+  const int qt = p.n_qtiles - 1 - bid / p.BH;
+  const int bh = bid % p.BH;
+  const int b = bh / p.H, h = bh % p.H;
+  int L = p.kv_len;
+  if (p.lens) L = min(max(p.lens[b], 0), p.kv_len);
+  const int q0 = qt * BR;
+  if (q0 >= L) return;
+  const int w = min(p.window, L);
+  const int kstart = max(0, q0 - w + 1);
+  const int qend = min(q0 + BR, L);
+  const int kt_begin = kstart / BC, kt_end = (qend - 1) / BC;
+  const float* qb = qg + (int64_t)b * p.q_bstride + h * D;
+  const float* kb = kg + (int64_t)b * p.kv_bstride + h * D;
+  const float* vb = vg + (int64_t)b * p.kv_bstride + h * D;
+  const int rs = p.row_stride;
+  const int qa = q0 + 32 * wave;
+  const int qi = qa + l32;
+  const bool qvalid = qi < L;
+
+  float qf[D / 2];
+#pragma unroll
+  for (int t = 0; t < D / 2; ++t) qf[t] = qvalid ? qb[(int64_t)qi * rs + 2 * t + half] : 0.f;
+  f32x16 oacc[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) oacc[m] = zero16();
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int kt = kt_begin; kt <= kt_end; ++kt) {
+    __syncthreads();
+    for (int idx = tid; idx < BC * D; idx += NT) {
+      const int r = idx / D, d = idx % D;
+      const int j = kt * BC + r;
+      const bool ok = j < L;
+      sK[r * SK + d] = ok ? kb[(int64_t)j * rs + d] : 0.f;
+      sV[r * D + d] = ok ? vb[(int64_t)j * rs + d] : 0.f;
+    }
+    __syncthreads();
+    const int k_lo = kt * BC, k_hi = k_lo + BC - 1, qz = qa + 31;
+    if ((qa >= L) || (k_lo > qz) || (qa - k_hi >= w)) continue;
+
+    f32x16 s = zero16();
+#pragma unroll
+    for (int t = 0; t < D / 2; ++t) s = mfma32_f32(sK[l32 * SK + 2 * t + half], qf[t], s);
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = k_lo + 8 * (r >> 2) + 4 * half + (r & 3);
+      float x = s[r] * p.scale_log2;
+      if (key > qi || qi - key >= w) x = -INFINITY;
+      s[r] = x;
+      mloc = fmaxf(mloc, x);
+    }
+    const float m_new = fmaxf(m_run, max_with_partner(mloc));
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    float lsum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = exp2f(s[r] - m_use);
+      lsum += s[r];
+    }
+    l_run = l_run * alpha + lsum;
+    m_run = m_new;
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[m][r] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * half + (r & 3);
+        oacc[m] = mfma32_f32(sV[key * D + m * 32 + l32], s[r], oacc[m]);
+      }
+    }
+  }
+  const float l_tot = sum_with_partner(l_run);
+  if (!qvalid) return;
+  const float inv = 1.f / l_tot;
+  float* ob = og + (int64_t)b * p.q_bstride + h * D + (int64_t)qi * rs;
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float4 st = make_float4(oacc[m][4 * j] * inv, oacc[m][4 * j + 1] * inv,
+                              oacc[m][4 * j + 2] * inv, oacc[m][4 * j + 3] * inv);
+      *reinterpret_cast<float4*>(ob + m * 32 + 8 * j + 4 * half) = st;
+    }
+  if (p.lse && half == 0) p.lse[(int64_t)bh * p.lse_T + qi] = (m_run + log2f(l_tot)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------------------------
+template <int D, int NW>
+static hipError_t launch_bf16(const FwdArgs& a, hipStream_t s) {
+  FwdArgs p = a;
+  p.n_qtiles = (p.T + 32 * NW - 1) / (32 * NW);
+  const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.BH;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW>), dim3(grid), dim3(64 * NW), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_f32(const FwdArgs& a, hipStream_t s) {
+  FwdArgs p = a;
+  p.n_qtiles = (p.T + 127) / 128;
+  const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.BH;
+  hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3(grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdArgs& a, bool f32, hipStream_t s) {
+  if (f32) return a.D == 64 ? launch_f32<64>(a, s) : launch_f32<128>(a, s);
+  return a.D == 64 ? launch_bf16<64, 4>(a, s) : launch_bf16<128, 4>(a, s);
+}
+
+}  // namespace swattn

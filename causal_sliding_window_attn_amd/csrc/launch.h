@@ -1,0 +1,76 @@
+// Internal host-side launch interface between the C ABI (api.cpp) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swattn {
+
+// Forward / prefill.  Pointers are bf16 (uint16_t) or fp32 (reinterpreted by the fp32 kernel).
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;          // [BH, lse_T] or null
+  const int* lens;     // per-batch valid length (prefill) or null (training: every row valid)
+  int64_t q_bstride;   // elements between batches of q / o
+  int64_t kv_bstride;  // elements between batches of k / v
+  int row_stride;      // elements between consecutive tokens (H * D)
+  int H, BH, D;
+  int T;               // query rows per batch
+  int kv_len;          // keys per batch (training: T; prefill: min(Tq, Lcap), lens clamp)
+  int window;          // >= 1
+  int lse_T;
+  int n_qtiles;        // filled by the launcher
+  float scale_log2;    // log2(e) / sqrt(D)
+};
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;  // [BH, T]
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* delta;      // [BH, T] workspace
+  int64_t bstride;   // T * H * D
+  int row_stride;    // H * D
+  int H, BH, D, T, window;
+  int n_tiles;       // filled by the launcher
+  float scale;       // 1 / sqrt(D)
+  float scale_log2;  // log2(e) / sqrt(D)
+};
+
+struct DecArgs {
+  const uint16_t* q;   // [B, H, D]
+  const uint16_t* kc;  // [B, Lcap, H, D]
+  const uint16_t* vc;
+  const int* lens;
+  uint16_t* o;         // [B, H, D]
+  float* lse;          // [B, H] or null
+  float* ws_o;         // [B*H, nc_max, D]
+  float* ws_ml;        // [B*H, nc_max, 2]
+  int B, H, D, Lcap, window, nc_max;
+  float scale_log2;
+};
+
+struct AppendArgs {
+  uint16_t* kc;
+  uint16_t* vc;
+  const uint16_t* kn;
+  const uint16_t* vn;
+  const int* pos;
+  int B, H, D, Lcap;
+};
+
+constexpr int kDecodeChunk = 64;  // keys per split of the decode
+
+hipError_t launch_fwd(const FwdArgs& a, bool f32, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecArgs& a, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+
+}  // namespace swattn

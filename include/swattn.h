@@ -1,0 +1,131 @@
+/*
+ * swattn.h -- C ABI of libswattn.so: exact softmax causal self-attention with an optional sliding
+ * window, for AMD Instinct MI355X (gfx950).
+ *
+ * What the operations are
+ *   The training attention with a per-layer window: "nanochat: GPT-2-grade LLM for <<$100" post
+ *   (web3.cnoyu.life, the "Jan29" entry), list of the largest improvements, item 1 -- attention
+ *   kernels whose window_size keyword lets layers alternate short and long attention patterns.
+ *   The KV-cache Engine with its prefill and decode phases: walkthrough "A fully hand-made copy of
+ *   ChatGPT for $100 and 8,000 lines of code" (followin.io), section "Pretraining", closing
+ *   paragraph; nanochat launch post (web3.ouchyi.army), feature list.
+ *   Shapes of the d20 layer (1280 channels = 10 heads x 128; 32 x 2048 tokens per GPU): same
+ *   walkthrough, section "Pretraining".
+ *
+ * Definition (the pages give no formula; this is the textbook one, with the window read as
+ * counting the query's own key):
+ *   query i sees key j iff 0 <= j <= i and i - j < w;  any w >= T is full causal attention.
+ *   s_ij = q_i . k_j / sqrt(D);  LSE_i = ln sum_j exp(s_ij);  P_ij = exp(s_ij - LSE_i);
+ *   O_i = sum_j P_ij v_j.   Backward (no gradient into LSE):
+ *   dV_j = sum_i P_ij dO_i;  dS_ij = P_ij (dO_i.v_j - dO_i.O_i);
+ *   dQ_i = sum_j dS_ij k_j / sqrt(D);  dK_j = sum_i dS_ij q_i / sqrt(D).
+ *
+ * Conventions shared by every entry point
+ *   Layout:    activations [B, T, H, D] row-major, D fastest (what a fused QKV projection yields);
+ *              KV cache [B, Lcap, H, D]; LSE [B, H, T] float32 (natural log).
+ *   Types:     bf16 storage with fp32 accumulation; the forward also accepts fp32 (SWATTN_F32).
+ *   Pointers:  device memory owned by the caller; the library allocates nothing and keeps no state
+ *              besides a read-only per-device property cache.  All pointers must be 16-byte aligned.
+ *   Streams:   `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue and return; the
+ *              caller keeps every buffer alive until the stream has passed the kernels.
+ *   Errors:    every check below runs on the host before any HIP call.  A failing call returns a
+ *              negative status, launches nothing and sets attn_last_error() (thread-local text,
+ *              valid until the next call on that thread).  Faults inside kernels surface at the
+ *              caller's next synchronisation.  No entry point throws.
+ *   Window:    window >= 1; any window >= the sequence length means full causal attention.
+ *   Head dim:  D in {64, 128}.
+ *   Threads:   entry points are re-entrant; concurrent calls may share nothing they write.
+ */
+#ifndef SWATTN_H
+#define SWATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SWATTN_ABI_VERSION 1
+
+typedef enum { SWATTN_BF16 = 0, SWATTN_F32 = 1 } swattn_dtype;
+
+enum {
+  SWATTN_OK = 0,
+  SWATTN_EINVAL = -1,       /* null pointer, size < 1, window < 1, misaligned pointer          */
+  SWATTN_EUNSUPPORTED = -2, /* D not 64/128, or a dtype the entry point does not implement      */
+  SWATTN_EWORKSPACE = -3,   /* workspace pointer null or smaller than the *_workspace_bytes size */
+  SWATTN_EHIP = -4          /* the HIP runtime refused the launch (message in attn_last_error)  */
+};
+
+/* ABI version of the loaded library (SWATTN_ABI_VERSION at build time). */
+int attn_abi_version(void);
+
+/* Text of the last failure on the calling thread ("" after a successful call). */
+const char* attn_last_error(void);
+
+/*
+ * Training forward (the "Jan29" post's attention kernel with window_size).
+ *   q, k, v  [B, T, H, D] in `dtype` (read).        o [B, T, H, D] in `dtype` (written).
+ *   lse      [B, H, T] float32 (written), may be NULL when no backward will follow.
+ *   window   keys visible to each query, counting itself (>= T: full causal).
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int T,
+             int D, int window, int dtype, void* stream);
+
+/* Bytes of device workspace attn_bwd needs (the per-row Delta_i = dO_i . O_i, float32). */
+size_t attn_bwd_workspace_bytes(int B, int H, int T, int D);
+
+/*
+ * Training backward, split into a dQ pass and a dK/dV pass that both recompute P from LSE.
+ *   q, k, v, o, dout [B, T, H, D] bf16 (read); lse [B, H, T] float32 from attn_fwd (read).
+ *   dq, dk, dv [B, T, H, D] bf16 (written, fully overwritten; no accumulation into them).
+ *   ws / ws_bytes: caller-owned device scratch of at least attn_bwd_workspace_bytes(); its
+ *   contents on entry do not matter.  dtype must be SWATTN_BF16 (fp32 returns -2).
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, int B, int H, int T, int D, int window,
+             int dtype, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Engine prefill over a KV cache (walkthrough, section "Pretraining", Engine paragraph).
+ *   q       [B, Tq, H, D] bf16: prompt b's queries at positions 0..L_b-1 (read).
+ *   kcache, vcache [B, Lcap, H, D] bf16: prompt b's keys/values already in rows 0..L_b-1 (read).
+ *   lens    device int32 [B]: prompt lengths L_b; values are clamped to [0, min(Tq, Lcap)].
+ *   o       [B, Tq, H, D] bf16: rows t < L_b written; rows t >= L_b left untouched.
+ *   lse     [B, H, Tq] float32 or NULL; same rows written.
+ *   window  keys visible to each query, counting itself (>= L_b: full causal).
+ */
+int attn_prefill(const void* q, const void* kcache, const void* vcache, const int* lens, void* o,
+                 float* lse, int B, int H, int Tq, int Lcap, int D, int window, void* stream);
+
+/*
+ * Engine KV-cache append: kcache[b, pos[b], h, :] = knew[b, h, :] (same for v).
+ *   knew, vnew [B, H, D] bf16 (read); pos device int32 [B]; rows with pos[b] outside [0, Lcap)
+ *   are skipped (nothing is written for them).
+ */
+int attn_kv_append(void* kcache, void* vcache, const void* knew, const void* vnew, const int* pos,
+                   int B, int H, int Lcap, int D, void* stream);
+
+/* Bytes of device workspace attn_decode needs (split-K partial results, float32). */
+size_t attn_decode_workspace_bytes(int B, int H, int Lcap, int D);
+
+/*
+ * Engine decode: one new query per sequence attends to its cache (split-K over the cache length,
+ * then a log-sum-exp merge of the partial results).
+ *   q      [B, H, D] bf16 (read); kcache, vcache [B, Lcap, H, D] bf16 (read).
+ *   lens   device int32 [B]: cached tokens including the new one (append first, then decode);
+ *          the query sits at position L_b - 1.  Values are clamped to [0, Lcap]; L_b = 0 gives
+ *          o = 0 and lse = -inf.
+ *   o      [B, H, D] bf16 (written);  lse [B, H] float32 or NULL.
+ *   window keys visible to the query, counting itself.
+ *   ws / ws_bytes: caller-owned device scratch of at least attn_decode_workspace_bytes().
+ */
+int attn_decode(const void* q, const void* kcache, const void* vcache, const int* lens, void* o,
+                float* lse, int B, int H, int Lcap, int D, int window, void* ws, size_t ws_bytes,
+                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWATTN_H */

@@ -1,0 +1,148 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol, and rejects bad
+arguments with the documented status before any HIP call (so no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swattn.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return re.findall(r"^\s*(?:int|size_t|const char\*)\s+(attn_\w+)\s*\(", src, re.M)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from causal_sliding_window_attn_amd import _lib
+
+    if not os.path.exists(_lib.LIB_PATH):
+        from causal_sliding_window_attn_amd import build
+
+        build.build()
+    return _lib.load()
+
+
+def test_header_declares_the_entry_points():
+    names = set(declared_functions())
+    assert {"attn_fwd", "attn_bwd", "attn_decode", "attn_prefill", "attn_kv_append",
+            "attn_bwd_workspace_bytes", "attn_decode_workspace_bytes", "attn_last_error",
+            "attn_abi_version"} == names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    from causal_sliding_window_attn_amd import _lib
+
+    assert set(_lib.SIGNATURES) == set(declared_functions())
+
+
+def test_nm_lists_only_c_symbols(lib):
+    import subprocess
+
+    from causal_sliding_window_attn_amd import _lib
+
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for name in declared_functions():
+        assert name in exported
+
+
+def test_abi_version(lib):
+    assert lib.attn_abi_version() == 1
+
+
+P = 4096  # an aligned, non-null stand-in pointer: validation must fail before it is ever used
+
+
+def err(lib):
+    return lib.attn_last_error().decode()
+
+
+@pytest.mark.parametrize("B,H,T,D,w,code", [
+    (0, 1, 8, 128, 8, -1), (1, 0, 8, 128, 8, -1), (1, 1, 0, 128, 8, -1), (1, 1, 8, 128, 0, -1),
+    (1, 1, 8, 96, 8, -2), (1, 1, 8, 32, 8, -2), (-3, 1, 8, 64, 8, -1), (1, 1, 8, 64, -5, -1),
+    (70000, 1, 8, 64, 8, -1),
+])
+def test_fwd_rejects_bad_dims(lib, B, H, T, D, w, code):
+    rc = lib.attn_fwd(P, P, P, P, None, B, H, T, D, w, 0, None)
+    assert rc == code and err(lib)
+
+
+def test_fwd_rejects_bad_pointers_and_dtype(lib):
+    assert lib.attn_fwd(None, P, P, P, None, 1, 1, 8, 64, 8, 0, None) == -1
+    assert "q" in err(lib)
+    assert lib.attn_fwd(P, P, P + 2, P, None, 1, 1, 8, 64, 8, 0, None) == -1
+    assert "aligned" in err(lib)
+    assert lib.attn_fwd(P, P, P, P, P + 4, 1, 1, 8, 64, 8, 0, None) == -1
+    assert lib.attn_fwd(P, P, P, P, None, 1, 1, 8, 64, 8, 7, None) == -2
+
+
+def test_bwd_validation(lib):
+    need = lib.attn_bwd_workspace_bytes(2, 3, 100, 128)
+    assert need >= 2 * 3 * 100 * 4 and need % 256 == 0
+    assert lib.attn_bwd_workspace_bytes(0, 3, 100, 128) == 0
+    args = [P] * 9
+    assert lib.attn_bwd(*args, 2, 3, 100, 128, 8, 0, None, need, None) == -3
+    assert lib.attn_bwd(*args, 2, 3, 100, 128, 8, 0, P, need - 1, None) == -3
+    assert "workspace" in err(lib)
+    assert lib.attn_bwd(*args, 2, 3, 100, 128, 8, 1, P, need, None) == -2  # fp32 backward
+    bad = list(args)
+    bad[5] = None  # dout
+    assert lib.attn_bwd(*bad, 2, 3, 100, 128, 8, 0, P, need, None) == -1
+    assert lib.attn_bwd(*args, 2, 3, 100, 100, 8, 0, P, need, None) == -2
+
+
+def test_prefill_append_decode_validation(lib):
+    assert lib.attn_prefill(P, P, P, None, P, None, 2, 2, 16, 32, 128, 8, None) == -1
+    assert lib.attn_prefill(P, P, P, P + 2, P, None, 2, 2, 16, 32, 128, 8, None) == -1
+    assert lib.attn_prefill(P, P, P, P, P, None, 2, 2, 16, 0, 128, 8, None) == -1
+    assert lib.attn_prefill(P, P, P, P, P, None, 2, 2, 16, 32, 64, 0, None) == -1
+    assert lib.attn_kv_append(P, P, P, P, None, 2, 2, 32, 128, None) == -1
+    assert lib.attn_kv_append(P, P, P, P, P, 2, 2, 32, 80, None) == -2
+    need = lib.attn_decode_workspace_bytes(2, 2, 100, 128)
+    assert need > 0
+    assert lib.attn_decode(P, P, P, P, P, None, 2, 2, 100, 128, 8, P, need - 1, None) == -3
+    assert lib.attn_decode(P, P, P, P, P, None, 2, 2, 100, 128, 8, None, need, None) == -3
+    assert lib.attn_decode(P, P, P, P, P, None, 2, 2, 100, 128, 0, P, need, None) == -1
+    assert lib.attn_decode(P, P, P, None, P, None, 2, 2, 100, 128, 8, P, need, None) == -1
+
+
+def test_last_error_is_thread_local(lib):
+    import threading
+
+    lib.attn_fwd(None, P, P, P, None, 1, 1, 8, 64, 8, 0, None)
+    here = err(lib)
+    seen = []
+
+    def other():
+        seen.append(lib.attn_last_error().decode())
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert here and seen == [""]
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+
+    import causal_sliding_window_attn_amd as sw
+
+    q = torch.zeros(1, 8, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sw.attn_fwd(q, q, q)
+    with pytest.raises(ValueError):
+        sw.attention(q, q, q, window=0)
+
+
+def test_binding_exposes_c_names():
+    import causal_sliding_window_attn_amd as sw
+
+    for name in declared_functions():
+        assert callable(getattr(sw, name)), name

@@ -1,0 +1,363 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle on the same seeded inputs.
+
+Bars (bf16 in, fp32 accumulate): O max-abs <= 1e-2 over valid elements; dQ, dK, dV relative
+Frobenius error <= 2e-2 each; LSE max-abs <= 1e-3 (reported bar).  Full-size workloads compare
+every element of sampled (batch, head) pairs; the oracle computes those heads exactly.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import attention as ref
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 1e-2
+G_TOL = 2e-2
+LSE_TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def sw():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import causal_sliding_window_attn_amd as m
+
+    m.load()
+    return m
+
+
+DEV = "cuda"
+
+
+def f64(t):
+    return t.detach().double().cpu().numpy()
+
+
+def rel_fro(a, b):
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+
+
+def check_fwd(o, lse, o_r, lse_r, heads=None, tag=""):
+    o, lse = f64(o), f64(lse) if lse is not None else None
+    if heads is not None:
+        for b, h in heads:
+            e = np.abs(o[b, :, h] - o_r[b, :, h]).max()
+            assert e <= O_TOL, f"{tag} O max-abs {e} at head {(b, h)}"
+            if lse is not None:
+                el = np.abs(lse[b, h] - lse_r[b, h]).max()
+                assert el <= LSE_TOL, f"{tag} LSE max-abs {el} at head {(b, h)}"
+        return
+    e = np.abs(o - o_r).max()
+    assert e <= O_TOL, f"{tag} O max-abs {e}"
+    if lse is not None:
+        el = np.abs(lse - lse_r).max()
+        assert el <= LSE_TOL, f"{tag} LSE max-abs {el}"
+
+
+def check_grads(gs, rs, heads=None, tag=""):
+    for name, g, r in zip(("dQ", "dK", "dV"), gs, rs):
+        g = f64(g)
+        if heads is not None:
+            g = np.stack([g[b, :, h] for b, h in heads])
+            r = np.stack([r[b, :, h] for b, h in heads])
+        e = rel_fro(g, r)
+        assert e <= G_TOL, f"{tag} {name} rel-Frobenius {e}"
+
+
+def run_fwd_bwd(sw, q, k, v, do, window):
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    o, lse = sw.attn_fwd(qd, kd, vd, window=window)
+    grads = None
+    if do is not None:
+        grads = sw.attn_bwd(qd, kd, vd, o, lse, do.to(DEV), window=window)
+    torch.cuda.synchronize()
+    return o, lse, grads
+
+
+def test_single_hip_runtime(sw):
+    maps = open("/proc/self/maps").read()
+    libs = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
+    assert len(libs) == 1, libs
+
+
+# --------------------------------------------------------------------------- the five workloads
+def test_tiny_fp32_forward(sw):
+    q, k, v = W.attn_inputs(W.TINY_F32)
+    o, lse, _ = run_fwd_bwd(sw, q, k, v, None, W.TINY_F32.window)
+    o_r, lse_r = ref.forward(f64(q), f64(k), f64(v), W.TINY_F32.window)
+    check_fwd(o, lse, o_r, lse_r, tag="tiny-fp32")
+    assert np.abs(f64(o) - o_r).max() < 1e-4  # fp32 end to end
+
+
+def test_small_bf16_window128(sw):
+    c = W.SMALL_W128
+    q, k, v, do = W.attn_inputs(c)
+    o, lse, g = run_fwd_bwd(sw, q, k, v, do, c.window)
+    Q, K, V, DO = (f64(t) for t in (q, k, v, do))
+    o_r, lse_r = ref.forward(Q, K, V, c.window)
+    check_fwd(o, lse, o_r, lse_r, tag=c.name)
+    check_grads(g, ref.backward(Q, K, V, DO, c.window), tag=c.name)
+
+
+D20_HEADS = [(0, 0), (7, 3), (19, 9), (31, 5)]
+
+
+@pytest.mark.slow
+def test_d20_layer_sampled_heads(sw):
+    c = W.D20_LAYER
+    q, k, v, do = W.attn_inputs(c)
+    o, lse, g = run_fwd_bwd(sw, q, k, v, do, c.window)
+    Q, K, V, DO = (f64(t) for t in (q, k, v, do))
+    o_r, lse_r = ref.forward(Q, K, V, c.window, heads=D20_HEADS)
+    check_fwd(o, lse, o_r, lse_r, heads=D20_HEADS, tag=c.name)
+    check_grads(g, ref.backward(Q, K, V, DO, c.window, heads=D20_HEADS), heads=D20_HEADS,
+                tag=c.name)
+    # properties that hold for every head at any size
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    for t in g:
+        assert torch.isfinite(t).all()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("layer", [0, 1, 2, 3])
+def test_d26_alternating_layer(sw, layer):
+    window = W.D26_WINDOWS[layer]
+    q, k, v, do = W.d26_layer_inputs(layer)
+    o, lse, g = run_fwd_bwd(sw, q, k, v, do, window)
+    heads = [(0, 0), (5, 12), (15, 6)]
+    Q, K, V, DO = (f64(t) for t in (q, k, v, do))
+    o_r, lse_r = ref.forward(Q, K, V, window, heads=heads)
+    check_fwd(o, lse, o_r, lse_r, heads=heads, tag=f"d26 layer {layer}")
+    check_grads(g, ref.backward(Q, K, V, DO, window, heads=heads), heads=heads,
+                tag=f"d26 layer {layer}")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("layer", [0, 1])
+def test_d30_engine_prefill_and_decode(sw, layer):
+    E = W.D30_ENGINE
+    window = E.window(layer)
+    lens = W.engine_lens(E)
+    Tq = int(lens.max())
+    qp, kp, vp = W.engine_prefill_packed(layer, lens, E)
+    q = W.pad_prompts(qp, lens, Tq)
+    kc = W.pad_prompts(kp, lens, E.Lcap)
+    vc = W.pad_prompts(vp, lens, E.Lcap)
+    qd, kcd, vcd, lensd = q.to(DEV), kc.to(DEV), vc.to(DEV), lens.to(DEV)
+    sentinel = torch.full_like(qd, 7.0)
+    o, lse = sw.attn_prefill(qd, kcd, vcd, lensd, o=sentinel.clone(), window=window,
+                             want_lse=True)
+    torch.cuda.synchronize()
+    o_r, lse_r = ref.prefill(f64(q), f64(kc), f64(vc), lens.numpy(), window)
+    of, lf = f64(o), f64(lse)
+    for b in range(E.B):
+        L = int(lens[b])
+        e = np.abs(of[b, :L] - o_r[b, :L]).max()
+        assert e <= O_TOL, f"prefill b={b} max-abs {e}"
+        assert np.abs(lf[b, :, :L] - lse_r[b, :, :L]).max() <= LSE_TOL
+        assert np.all(of[b, L:] == 7.0), "rows past the prompt must stay untouched"
+    # decode steps: append, then attend with lens + 1
+    kc_ref, vc_ref = f64(kc), f64(vc)
+    cur = lens.clone()
+    ws = torch.empty(sw.attn_decode_workspace_bytes(E.B, E.H, E.Lcap, E.D), device=DEV,
+                     dtype=torch.uint8)
+    worst = 0.0
+    for s in range(E.steps):
+        qn, kn, vn = W.engine_decode_step(s, layer, E)
+        pos = cur.to(DEV)
+        sw.attn_kv_append(kcd, vcd, kn.to(DEV), vn.to(DEV), pos)
+        od, lsed = sw.attn_decode(qn.to(DEV), kcd, vcd, (cur + 1).to(DEV), window=window, ws=ws,
+                                  want_lse=True)
+        torch.cuda.synchronize()
+        for b in range(E.B):
+            kc_ref[b, int(cur[b])] = f64(kn[b])
+            vc_ref[b, int(cur[b])] = f64(vn[b])
+        od_r, lse_dr = ref.decode(f64(qn), kc_ref, vc_ref, (cur + 1).numpy(), window)
+        e = float(np.abs(f64(od) - od_r).max())
+        worst = max(worst, e)
+        assert e <= O_TOL, f"decode step {s} max-abs {e}"
+        assert np.abs(f64(lsed) - lse_dr).max() <= LSE_TOL
+        cur += 1
+    # the device cache holds exactly what the reference appended
+    assert np.array_equal(f64(kcd), kc_ref) and np.array_equal(f64(vcd), vc_ref)
+
+
+# --------------------------------------------------------------------------- edge sweep
+EDGE_T = [1, 17, 63, 64, 65, 127, 128, 129, 300]
+
+
+def edge_windows(T):
+    return sorted({1, 2, 63, 64, 65, 127, 128, max(1, T - 1), T, T + 5, 2 ** 31 - 1})
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T", EDGE_T)
+def test_edge_sweep_bf16(sw, T, D):
+    q, k, v, do = W.random_attn(1, T, 2, D, seed=1000 + T + D)
+    Q, K, V, DO = (f64(t) for t in (q, k, v, do))
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    for w in edge_windows(T):
+        o, lse = sw.attn_fwd(qd, kd, vd, window=w)
+        g = sw.attn_bwd(qd, kd, vd, o, lse, dod, window=w)
+        torch.cuda.synchronize()
+        o_r, lse_r = ref.forward(Q, K, V, w, threads=1)
+        check_fwd(o, lse, o_r, lse_r, tag=f"T={T} D={D} w={w}")
+        check_grads(g, ref.backward(Q, K, V, DO, w, threads=1), tag=f"T={T} D={D} w={w}")
+
+
+@pytest.mark.parametrize("T,w,D", [(1, 1, 64), (65, 7, 64), (129, 129, 128), (300, 64, 128),
+                                   (257, 2 ** 31 - 1, 64)])
+def test_edge_sweep_fp32(sw, T, w, D):
+    q, k, v = W.random_attn(2, T, 3, D, seed=2000 + T, dtype=torch.float32, with_do=False)
+    o, lse, _ = run_fwd_bwd(sw, q, k, v, None, w)
+    o_r, lse_r = ref.forward(f64(q), f64(k), f64(v), w, threads=1)
+    check_fwd(o, lse, o_r, lse_r, tag=f"fp32 T={T} w={w} D={D}")
+    assert np.abs(f64(o) - o_r).max() < 1e-4
+
+
+def test_multi_batch_head_strides(sw):
+    """B, H > 1 with a ragged tail: every (b, h) slice is addressed correctly."""
+    q, k, v, do = W.random_attn(3, 150, 5, 128, seed=42)
+    o, lse, g = run_fwd_bwd(sw, q, k, v, do, 40)
+    Q, K, V, DO = (f64(t) for t in (q, k, v, do))
+    o_r, lse_r = ref.forward(Q, K, V, 40)
+    check_fwd(o, lse, o_r, lse_r, tag="B3 H5 T150")
+    check_grads(g, ref.backward(Q, K, V, DO, 40), tag="B3 H5 T150")
+
+
+# --------------------------------------------------------------------------- Engine edge cases
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_edge_lengths(sw, D):
+    B, H, Lcap = 8, 3, 200
+    lens = torch.tensor([0, 1, 63, 64, 65, 128, 199, 200], dtype=torch.int32)
+    g = torch.Generator().manual_seed(5 + D)
+    kc = torch.randn(B, Lcap, H, D, generator=g).to(torch.bfloat16)
+    vc = torch.randn(B, Lcap, H, D, generator=g).to(torch.bfloat16)
+    q = torch.randn(B, H, D, generator=g).to(torch.bfloat16)
+    kcd, vcd = kc.to(DEV), vc.to(DEV)
+    for window in (None, 1, 2, 64, 65, 100, 10 ** 6):
+        o, lse = sw.attn_decode(q.to(DEV), kcd, vcd, lens.to(DEV), window=window, want_lse=True)
+        torch.cuda.synchronize()
+        o_r, lse_r = ref.decode(f64(q), f64(kc), f64(vc), lens.numpy(), window)
+        assert np.abs(f64(o) - o_r).max() <= O_TOL, f"window {window}"
+        lf = f64(lse)
+        assert np.all(f64(o)[0] == 0) and np.all(np.isneginf(lf[0]))
+        assert np.abs(lf[1:] - lse_r[1:]).max() <= LSE_TOL
+
+
+def test_prefill_ragged_and_window_noop(sw):
+    B, H, D, Lcap = 5, 2, 128, 160
+    lens = torch.tensor([1, 64, 65, 130, 0], dtype=torch.int32)
+    Tq = 130
+    g = torch.Generator().manual_seed(77)
+    q = torch.randn(B, Tq, H, D, generator=g).to(torch.bfloat16)
+    kc = torch.randn(B, Lcap, H, D, generator=g).to(torch.bfloat16)
+    vc = torch.randn(B, Lcap, H, D, generator=g).to(torch.bfloat16)
+    qd, kcd, vcd, ld = q.to(DEV), kc.to(DEV), vc.to(DEV), lens.to(DEV)
+    for window in (None, 3, 64, 130):
+        o, lse = sw.attn_prefill(qd, kcd, vcd, ld, o=torch.full_like(qd, -3.0), window=window,
+                                 want_lse=True)
+        torch.cuda.synchronize()
+        o_r, lse_r = ref.prefill(f64(q), f64(kc), f64(vc), lens.numpy(), window, threads=1)
+        of = f64(o)
+        for b in range(B):
+            L = int(lens[b])
+            if L:
+                assert np.abs(of[b, :L] - o_r[b, :L]).max() <= O_TOL, (window, b)
+                assert np.abs(f64(lse)[b, :, :L] - lse_r[b, :, :L]).max() <= LSE_TOL
+            assert np.all(of[b, L:] == -3.0)
+    # every prompt is <= 130 keys: window 130 equals full causal bit for bit
+    o_full, _ = sw.attn_prefill(qd, kcd, vcd, ld, window=None)
+    o_w, _ = sw.attn_prefill(qd, kcd, vcd, ld, window=130)
+    for b in range(B):
+        L = int(lens[b])
+        assert torch.equal(o_full[b, :L], o_w[b, :L])
+
+
+def test_append_skips_out_of_range_rows(sw):
+    B, H, D, Lcap = 3, 2, 64, 10
+    kc = torch.zeros(B, Lcap, H, D, dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    kn = torch.ones(B, H, D, dtype=torch.bfloat16, device=DEV)
+    pos = torch.tensor([0, 10, -1], dtype=torch.int32, device=DEV)
+    sw.attn_kv_append(kc, vc, kn, kn * 2, pos)
+    torch.cuda.synchronize()
+    assert torch.all(kc[0, 0] == 1) and torch.all(vc[0, 0] == 2)
+    assert kc[0, 1:].abs().sum() == 0 and kc[1:].abs().sum() == 0
+
+
+# --------------------------------------------------------------------------- invariants
+def test_determinism_and_full_window_bitwise(sw):
+    q, k, v, do = W.random_attn(2, 333, 3, 128, seed=9)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    outs = []
+    for _ in range(3):
+        o, lse = sw.attn_fwd(qd, kd, vd, window=100)
+        outs.append((o, lse) + sw.attn_bwd(qd, kd, vd, o, lse, dod, window=100))
+    torch.cuda.synchronize()
+    for rep in outs[1:]:
+        for a, b in zip(outs[0], rep):
+            assert torch.equal(a, b)
+    full = sw.attn_fwd(qd, kd, vd, window=None)
+    eq = sw.attn_fwd(qd, kd, vd, window=333)
+    big = sw.attn_fwd(qd, kd, vd, window=10 ** 9)
+    assert torch.equal(full[0], eq[0]) and torch.equal(full[0], big[0])
+    assert torch.equal(full[1], eq[1])
+    gf = sw.attn_bwd(qd, kd, vd, full[0], full[1], dod, window=None)
+    ge = sw.attn_bwd(qd, kd, vd, eq[0], eq[1], dod, window=333)
+    for a, b in zip(gf, ge):
+        assert torch.equal(a, b)
+
+
+def test_gradient_sum_invariants(sw):
+    q, k, v, do = W.random_attn(1, 256, 2, 128, seed=10)
+    o, lse, (dq, dk, dv) = run_fwd_bwd(sw, q, k, v, do, 50)
+    dk64, dv64, do64 = f64(dk), f64(dv), f64(do)
+    scale = np.abs(dk64).sum(1).max()
+    assert np.abs(dk64.sum(1)).max() <= 2e-2 * scale
+    assert np.abs(dv64.sum(1) - do64.sum(1)).max() <= 2e-2 * np.abs(do64).sum(1).max()
+
+
+def test_decode_matches_prefill_last_row(sw):
+    B, H, D, Lcap = 4, 3, 128, 256
+    lens = torch.tensor([1, 70, 129, 256], dtype=torch.int32)
+    g = torch.Generator().manual_seed(11)
+    q = torch.randn(B, 256, H, D, generator=g).to(torch.bfloat16)
+    kc = torch.randn(B, Lcap, H, D, generator=g).to(torch.bfloat16)
+    vc = torch.randn(B, Lcap, H, D, generator=g).to(torch.bfloat16)
+    qd, kcd, vcd, ld = q.to(DEV), kc.to(DEV), vc.to(DEV), lens.to(DEV)
+    for window in (None, 17):
+        o, _ = sw.attn_prefill(qd, kcd, vcd, ld, window=window)
+        qlast = torch.stack([qd[b, int(lens[b]) - 1] for b in range(B)])
+        od, _ = sw.attn_decode(qlast.contiguous(), kcd, vcd, ld, window=window)
+        torch.cuda.synchronize()
+        for b in range(B):
+            a = o[b, int(lens[b]) - 1].float()
+            assert (a - od[b].float()).abs().max().item() <= 1e-2
+
+
+def test_autograd_wrapper_and_kvcache(sw):
+    q, k, v, do = W.random_attn(1, 96, 2, 64, seed=12)
+    qd, kd, vd = (t.to(DEV).requires_grad_() for t in (q, k, v))
+    o = sw.attention(qd, kd, vd, window=32)
+    o.backward(do.to(DEV))
+    g_r = ref.backward(f64(q), f64(k), f64(v), f64(do), 32)
+    check_grads((qd.grad, kd.grad, vd.grad), g_r, tag="autograd")
+
+    cache = sw.KVCache(2, 2, 64, 2, 64, windows=[None, 8])
+    lens = torch.tensor([3, 10], dtype=torch.int32, device=DEV)
+    g = torch.Generator().manual_seed(13)
+    qp, kp, vp = (torch.randn(2, 10, 2, 64, generator=g).to(torch.bfloat16).to(DEV)
+                  for _ in range(3))
+    for layer in range(2):
+        cache.prefill(layer, qp, kp, vp, lens)
+    qn, kn, vn = (torch.randn(2, 2, 64, generator=g).to(torch.bfloat16).to(DEV) for _ in range(3))
+    od = cache.decode(1, qn, kn, vn)
+    torch.cuda.synchronize()
+    kc, vc = f64(cache.k[1]), f64(cache.v[1])
+    od_r, _ = ref.decode(f64(qn), kc, vc, np.array([4, 11]), 8)
+    assert np.abs(f64(od) - od_r).max() <= O_TOL
