@@ -60,6 +60,20 @@ __device__ __forceinline__ uint4 pack_frag(const f32x16& acc, int u) {
   return r;
 }
 
+// Eight fp32 values -> two bf16x8 fragments hi + lo with hi = bf16(x) and lo = bf16(x - hi), so
+// hi + lo carries x to about 2^-17 relative (one bf16 alone keeps only 2^-9).
+__device__ __forceinline__ void pack_frag_split(const f32x16& acc, int u, uint4& hi, uint4& lo) {
+  uint32_t* h = reinterpret_cast<uint32_t*>(&hi);
+  uint32_t* l = reinterpret_cast<uint32_t*>(&lo);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a = acc[8 * u + 2 * e], b = acc[8 * u + 2 * e + 1];
+    const uint32_t w = pack_bf16x2(a, b);
+    h[e] = w;
+    l[e] = pack_bf16x2(a - __uint_as_float(w << 16), b - __uint_as_float(w & 0xffff0000u));
+  }
+}
+
 // v_permlane32_swap(x, x) returns {x of lanes 0-31 | x of lane l-32, x of lane l+32 | x of lanes
 // 32-63}: each lane sees its own value in one slot and lane (l ^ 32)'s in the other.
 __device__ __forceinline__ float max_with_partner(float x) {

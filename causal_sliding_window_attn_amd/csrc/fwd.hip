@@ -9,8 +9,9 @@
 // Design (bf16): one workgroup = NW waves x 32 queries of one (batch, head).  Each wave keeps its
 // queries' Q in registers as MFMA B fragments and computes S^T = K Q^T per 64-key tile, so a lane
 // owns one query column: the row max / row sum of the online softmax are lane-local plus a single
-// v_permlane32_swap.  O^T = V^T P^T reuses the S^T accumulators (rounded to bf16) directly as the
-// B operand; V is written to LDS transposed, in the matching permuted key order.  K/V tiles
+// v_permlane32_swap.  O^T = V^T P^T reuses the S^T accumulators directly as the B operand (P split
+// into bf16 hi + lo, two MFMAs on one V fragment); V is written to LDS transposed, in the matching
+// permuted key order.  K/V tiles
 // outside [q0 - w + 1, q_end] are never loaded; per wave, tiles wholly outside the window are
 // skipped and only tiles crossing the diagonal or the window edge evaluate the mask.
 #include "common.h"
@@ -166,12 +167,13 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[m][r] *= alpha;
 
-    // O^T += V^T P^T
-    uint4 pf[NB][2];
+    // O^T += V^T P^T, with P carried as bf16 hi + lo: the output is stored in bf16, whose rounding
+    // alone costs up to half an ulp, so P must not add another 2^-9 relative error on top.
+    uint4 ph[NB][2], pl[NB][2];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      pf[nb][0] = pack_frag(s[nb], 0);
-      pf[nb][1] = pack_frag(s[nb], 1);
+      pack_frag_split(s[nb], 0, ph[nb][0], pl[nb][0]);
+      pack_frag_split(s[nb], 1, ph[nb][1], pl[nb][1]);
     }
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
@@ -182,7 +184,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs p) {
         for (int u = 0; u < 2; ++u) {
           const uint4 a =
               *reinterpret_cast<const uint4*>(sVt + trans_off<BC>(d, 2 * (2 * nb + u) + half));
-          oacc[m] = mfma32(a, pf[nb][u], oacc[m]);
+          oacc[m] = mfma32(a, ph[nb][u], oacc[m]);
+          oacc[m] = mfma32(a, pl[nb][u], oacc[m]);
         }
     }
   }

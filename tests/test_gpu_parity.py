@@ -64,6 +64,12 @@ def check_grads(gs, rs, heads=None, tag=""):
         if heads is not None:
             g = np.stack([g[b, :, h] for b, h in heads])
             r = np.stack([r[b, :, h] for b, h in heads])
+        if not np.any(r):
+            # closed-form zero gradient (window 1 gives dQ = dK = 0 exactly): relative error is
+            # undefined, so bound the rounding residue absolutely instead
+            e = float(np.abs(g).max())
+            assert e <= 1e-3, f"{tag} {name} should be 0, max-abs {e}"
+            continue
         e = rel_fro(g, r)
         assert e <= G_TOL, f"{tag} {name} rel-Frobenius {e}"
 
@@ -162,6 +168,7 @@ def test_d30_engine_prefill_and_decode(sw, layer):
         assert np.all(of[b, L:] == 7.0), "rows past the prompt must stay untouched"
     # decode steps: append, then attend with lens + 1
     kc_ref, vc_ref = f64(kc), f64(vc)
+    kc_bf, vc_bf = kc.clone(), vc.clone()
     cur = lens.clone()
     ws = torch.empty(sw.attn_decode_workspace_bytes(E.B, E.H, E.Lcap, E.D), device=DEV,
                      dtype=torch.uint8)
@@ -176,6 +183,8 @@ def test_d30_engine_prefill_and_decode(sw, layer):
         for b in range(E.B):
             kc_ref[b, int(cur[b])] = f64(kn[b])
             vc_ref[b, int(cur[b])] = f64(vn[b])
+            kc_bf[b, int(cur[b])] = kn[b]
+            vc_bf[b, int(cur[b])] = vn[b]
         od_r, lse_dr = ref.decode(f64(qn), kc_ref, vc_ref, (cur + 1).numpy(), window)
         e = float(np.abs(f64(od) - od_r).max())
         worst = max(worst, e)
@@ -183,7 +192,7 @@ def test_d30_engine_prefill_and_decode(sw, layer):
         assert np.abs(f64(lsed) - lse_dr).max() <= LSE_TOL
         cur += 1
     # the device cache holds exactly what the reference appended
-    assert np.array_equal(f64(kcd), kc_ref) and np.array_equal(f64(vcd), vc_ref)
+    assert torch.equal(kcd.cpu(), kc_bf) and torch.equal(vcd.cpu(), vc_bf)
 
 
 # --------------------------------------------------------------------------- edge sweep
