@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Benchmark of the windowed causal attention hot path on one MI355X.
+
+One step is one pass over every part of the path, on synthetic data of the pages' shapes:
+  * the d20 training layer (B=32, T=2048, H=10, D=128, bf16, full causal): forward, dQ pass,
+    dK/dV pass;
+  * one Engine decode step of the d30-style model (30 layers, B=64, H=15, D=128, cache 2048,
+    prompts U[32,1024], window 1024 on odd layers): per layer, KV append + split-K decode;
+  * one Engine prefill layer (the same prompts, layer step % 30).
+Every part is bracketed by HIP events on the stream the kernels run on.
+
+The headline ``value`` is the d20 fwd+bwd rate in TFLOP/s counting unmasked FLOPs only (4D per
+visible (query, key) pair forward, 10D backward).  ``decode`` reports algorithmic HBM GB/s (every
+visible cache row read once, plus q and o), ``prefill`` TFLOP/s.  ``roofline`` describes the
+longest-running MFMA kernel; ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
+d20 workload on the host cores.  One JSON line goes to stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd+bwd TFLOP/s (unmasked FLOPs) & % bf16 MFMA peak; decode HBM GB/s"
+PEAK_MFMA_BF16 = 2500.0  # TFLOP/s, MI355X dense bf16 (published)
+PEAK_HBM = 8000.0        # GB/s, MI355X HBM3E (published)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def pairs(T: int, w) -> int:
+    """Visible (query, key) pairs of one causal head with window w (None = full)."""
+    w = T if w is None else min(int(w), T)
+    return w * (w + 1) // 2 + (T - w) * w
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "causal_sliding_window_attn_amd", "csrc", "*"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(case, q, k, v, do, n_heads: int):
+    """The fp64 oracle, as it stands, on n_heads (b, h) heads of the d20 layer, fwd + bwd."""
+    import torch
+
+    from oracle import attention as ref
+
+    B, H = case.B, case.H
+    heads = [(i % B, (i * 7 + i // B) % H) for i in range(n_heads)]
+    pick = lambda t: torch.stack([t[b, :, h] for b, h in heads])[:, :, None, :].double().numpy()  # noqa: E731
+    Q, K, V, DO = pick(q), pick(k), pick(v), pick(do)
+    threads = min(16, len(os.sched_getaffinity(0)))
+    t0 = time.perf_counter()
+    ref.forward(Q, K, V, case.window, threads=threads)
+    ref.backward(Q, K, V, DO, case.window, threads=threads)
+    dt = time.perf_counter() - t0
+    flops = 14 * case.D * pairs(case.T, case.window) * n_heads
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"fp64 oracle fwd+bwd on {n_heads} of the {B * H} (b,h) heads of the d20 layer "
+                  f"(T={case.T}, D={case.D}, full causal), same seeded inputs; {dt:.2f} s wall",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-heads", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=1024,
+                    help="after the timed region, one plain device copy of this size (the "
+                         "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures a single GPU: this attention path is data parallel over "
+              "(batch, head) with no exchange between GPUs, and only the one-GPU figure is "
+              "measured here (run with --gpus 1).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import causal_sliding_window_attn_amd as sw
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sw.load()
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device: {props.name}, {props.multi_processor_count} CUs")
+
+    # ------------------------------------------------------------------ d20 training layer
+    case = W.D20_LAYER
+    log("drawing d20 inputs ...")
+    q_c, k_c, v_c, do_c = W.attn_inputs(case)
+    q, k, v, do = (t.to(dev) for t in (q_c, k_c, v_c, do_c))
+    B, T, H, D = case.B, case.T, case.H, case.D
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), device=dev, dtype=torch.float32)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_b = torch.empty(sw.attn_bwd_workspace_bytes(B, H, T, D), device=dev, dtype=torch.uint8)
+    P20 = pairs(T, case.window) * B * H
+    F_fwd = 4 * D * P20
+    F_dq = 2 * D * P20
+    F_dkdv = 8 * D * P20
+
+    # ------------------------------------------------------------------ d30 Engine
+    E = W.D30_ENGINE
+    lens0 = W.engine_lens(E)
+    Tq = int(lens0.max())
+    log(f"allocating Engine caches: {E.n_layer} layers x 2 x {E.B}x{E.Lcap}x{E.H}x{E.D} bf16 ...")
+    g = torch.Generator(device=dev).manual_seed(E.seed)
+    kcache = [torch.randn((E.B, E.Lcap, E.H, E.D), device=dev, dtype=torch.bfloat16, generator=g)
+              for _ in range(E.n_layer)]
+    vcache = [torch.randn((E.B, E.Lcap, E.H, E.D), device=dev, dtype=torch.bfloat16, generator=g)
+              for _ in range(E.n_layer)]
+    qn = torch.randn((E.n_layer, E.B, E.H, E.D), device=dev, dtype=torch.bfloat16, generator=g)
+    kn = torch.randn((E.n_layer, E.B, E.H, E.D), device=dev, dtype=torch.bfloat16, generator=g)
+    vn = torch.randn((E.n_layer, E.B, E.H, E.D), device=dev, dtype=torch.bfloat16, generator=g)
+    on = torch.empty((E.B, E.H, E.D), device=dev, dtype=torch.bfloat16)
+    qp = torch.randn((E.B, Tq, E.H, E.D), device=dev, dtype=torch.bfloat16, generator=g)
+    op = torch.empty_like(qp)
+    steps_tab = torch.arange(E.steps, dtype=torch.int32)[:, None]
+    pos_tab = (lens0[None, :] + steps_tab).to(dev).contiguous()        # append row of step s
+    len_tab = (lens0[None, :] + steps_tab + 1).to(dev).contiguous()    # keys after the append
+    lens0_d = lens0.to(dev)
+    ws_d = torch.empty(sw.attn_decode_workspace_bytes(E.B, E.H, E.Lcap, E.D), device=dev,
+                       dtype=torch.uint8)
+
+    def decode_bytes(s: int) -> int:
+        tot = 0
+        for l in range(E.n_layer):
+            w = E.window(l)
+            for b in range(E.B):
+                L = int(lens0[b]) + s + 1
+                tot += E.H * (min(L, w) if w else L) * E.D * 2 * 2
+            tot += 2 * E.B * E.H * E.D * 2  # q read, o written
+        return tot
+
+    def prefill_flops(layer: int) -> int:
+        w = E.window(layer)
+        return 4 * E.D * E.H * sum(pairs(int(L), w) for L in lens0)
+
+    # ------------------------------------------------------------------ timed loop
+    n_total = args.warmup + args.steps
+    Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    ev = [[Ev() for _ in range(6)] for _ in range(n_total)]
+    ev_dec = [[(Ev(), Ev()) for _ in range(E.n_layer)] for _ in range(n_total)]
+    win = case.window
+
+    def step(i: int):
+        e = ev[i]
+        s = i % E.steps
+        e[0].record()
+        sw.attn_fwd(q, k, v, o=o, lse=lse, window=win)
+        e[1].record()
+        sw.attn_bwd_dq(q, k, v, o, lse, do, ws_b, window=win, dq=dq)
+        e[2].record()
+        sw.attn_bwd_dkdv(q, k, v, lse, do, ws_b, window=win, dk=dk, dv=dv)
+        e[3].record()
+        for l in range(E.n_layer):
+            sw.attn_kv_append(kcache[l], vcache[l], kn[l], vn[l], pos_tab[s])
+            a, b_ = ev_dec[i][l]
+            a.record()
+            sw.attn_decode(qn[l], kcache[l], vcache[l], len_tab[s], o=on, window=E.window(l),
+                           ws=ws_d)
+            b_.record()
+        e[4].record()
+        pl = i % E.n_layer
+        sw.attn_prefill(qp, kcache[pl], vcache[pl], lens0_d, o=op, window=E.window(pl))
+        e[5].record()
+
+    log(f"warmup {args.warmup} steps ...")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps ...")
+    t0 = time.perf_counter()
+    for i in range(args.warmup, n_total):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log("timed region done")
+
+    K = args.steps
+    timed = range(args.warmup, n_total)
+    t_fwd = sum(ev[i][0].elapsed_time(ev[i][1]) for i in timed) / K * 1e-3
+    t_dq = sum(ev[i][1].elapsed_time(ev[i][2]) for i in timed) / K * 1e-3
+    t_dkdv = sum(ev[i][2].elapsed_time(ev[i][3]) for i in timed) / K * 1e-3
+    t_dec = sum(a.elapsed_time(b) for i in timed for a, b in ev_dec[i]) / K * 1e-3
+    t_pre = sum(ev[i][4].elapsed_time(ev[i][5]) for i in timed) / K * 1e-3
+    dec_bytes = sum(decode_bytes(i % E.steps) for i in timed) / K
+    pre_flops = sum(prefill_flops(i % E.n_layer) for i in timed) / K
+    t_fb = t_fwd + t_dq + t_dkdv
+    value = (F_fwd + F_dq + F_dkdv) / t_fb / 1e12
+
+    kernels = {
+        "fwd_bf16_kernel": (F_fwd, t_fwd),
+        "bwd_dq_kernel": (F_dq, t_dq),
+        "bwd_dkdv_kernel": (F_dkdv, t_dkdv),
+    }
+    dom = max(kernels, key=lambda n: kernels[n][1])
+    f_dom, t_dom = kernels[dom]
+    achieved = f_dom / t_dom / 1e12
+    traffic = None
+    src_hash = kernel_source_hash()
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        ent = tr.get("kernels", {}).get(dom)
+        if ent and tr.get("source_hash") == src_hash:
+            traffic = ent["hbm_bytes_per_launch"]
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": PEAK_MFMA_BF16, "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_BF16, 4),
+                "traffic": traffic, "avg_launch_us": round(t_dom * 1e6, 2),
+                "algorithmic_flops_per_launch": f_dom}
+
+    # plain copy kernel of known size (rocprofv3 counter calibration); outside the timed region
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_heads} heads ...")
+        cpu = cpu_baseline(case, q_c, k_c, v_c, do_c, args.cpu_heads)
+
+    dec_gbs = dec_bytes / t_dec / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "d20 training layer B32 T2048 H10 D128 bf16 full causal fwd+bwd; d30 "
+                        "Engine B64 H15 D128 Lcap2048 prompts U[32,1024], 30 layers, window "
+                        "1024 on odd layers: one decode step + one prefill layer per step",
+            "B": B, "T": T, "H": H, "D": D, "window": None,
+        },
+        "frac_of_peak": round(value / PEAK_MFMA_BF16, 4),
+        "fwd": {"TFLOP/s": round(F_fwd / t_fwd / 1e12, 2), "ms": round(t_fwd * 1e3, 4)},
+        "bwd": {"TFLOP/s": round((F_dq + F_dkdv) / (t_dq + t_dkdv) / 1e12, 2),
+                "ms_dq": round(t_dq * 1e3, 4), "ms_dkdv": round(t_dkdv * 1e3, 4)},
+        "decode": {"GB/s": round(dec_gbs, 1), "frac_of_hbm_peak": round(dec_gbs / PEAK_HBM, 4),
+                   "us_per_layer_step": round(t_dec / E.n_layer * 1e6, 2),
+                   "bytes_per_layer_step": round(dec_bytes / E.n_layer)},
+        "prefill": {"TFLOP/s": round(pre_flops / t_pre / 1e12, 2), "ms_per_layer": round(t_pre * 1e3, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "device": props.name,
+        "kernel_source_hash": src_hash,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -17,7 +17,8 @@ from . import _lib
 from ._lib import SWATTN_BF16, SWATTN_F32, check, last_error, load
 
 __all__ = [
-    "attn_abi_version", "attn_last_error", "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes",
+    "attn_abi_version", "attn_last_error", "attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv",
+    "attn_bwd_workspace_bytes",
     "attn_prefill", "attn_kv_append", "attn_decode", "attn_decode_workspace_bytes", "attention",
     "KVCache", "FULL",
 ]
@@ -113,6 +114,50 @@ def attn_bwd(q, k, v, o, lse, dout, window=None, dq=None, dk=None, dv=None, ws=N
                          _stream(q))
     check(rc, "attn_bwd")
     return dq, dk, dv
+
+
+def _bwd_ws(q, ws):
+    B, T, H, D = q.shape
+    need = attn_bwd_workspace_bytes(B, H, T, D)
+    if ws is None:
+        ws = torch.empty(need, device=q.device, dtype=torch.uint8)
+    return ws, ws.numel() * ws.element_size()
+
+
+def attn_bwd_dq(q, k, v, o, lse, dout, ws, window=None, dq=None):
+    """First backward pass: Delta into ``ws`` (keep it for attn_bwd_dkdv) and dq."""
+    B, T, H, D = q.shape
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _need(t, n, (B, T, H, D), torch.bfloat16)
+    _need(lse, "lse", (B, H, T), torch.float32)
+    dq = torch.empty_like(q) if dq is None else dq
+    _need(dq, "dq", (B, T, H, D), torch.bfloat16)
+    ws, nbytes = _bwd_ws(q, ws)
+    rc = load().attn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            dout.data_ptr(), dq.data_ptr(), B, H, T, D, _win(window, T),
+                            SWATTN_BF16, ws.data_ptr(), nbytes, _stream(q))
+    check(rc, "attn_bwd_dq")
+    return dq
+
+
+def attn_bwd_dkdv(q, k, v, lse, dout, ws, window=None, dk=None, dv=None):
+    """Second backward pass: reads Delta from ``ws`` (left by attn_bwd_dq), writes dk, dv."""
+    B, T, H, D = q.shape
+    for n, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _need(t, n, (B, T, H, D), torch.bfloat16)
+    _need(lse, "lse", (B, H, T), torch.float32)
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for n, t in (("dk", dk), ("dv", dv)):
+        _need(t, n, (B, T, H, D), torch.bfloat16)
+    if ws is None:
+        raise ValueError("attn_bwd_dkdv needs the workspace filled by attn_bwd_dq")
+    _, nbytes = _bwd_ws(q, ws)
+    rc = load().attn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(),
+                              dout.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, T, D,
+                              _win(window, T), SWATTN_BF16, ws.data_ptr(), nbytes, _stream(q))
+    check(rc, "attn_bwd_dkdv")
+    return dk, dv
 
 
 def attn_prefill(q, kcache, vcache, lens, o=None, lse=None, window=None, want_lse=False):

@@ -112,26 +112,35 @@ size_t attn_bwd_workspace_bytes(int B, int H, int T, int D) {
   return align256((size_t)B * H * T * sizeof(float));
 }
 
-int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-             const void* dout, void* dq, void* dk, void* dv, int B, int H, int T, int D, int window,
-             int dtype, void* ws, size_t ws_bytes, void* stream) {
-  TRY(check_dims("attn_bwd", B, H, T, "T", D, window));
+}  // extern "C"
+
+namespace {
+
+enum BwdPass { kBoth, kDq, kDkdv };
+
+int bwd_common(const char* what, BwdPass pass, const void* q, const void* k, const void* v,
+               const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+               int B, int H, int T, int D, int window, int dtype, void* ws, size_t ws_bytes,
+               void* stream) {
+  TRY(check_dims(what, B, H, T, "T", D, window));
   if (dtype != SWATTN_BF16)
-    return fail(SWATTN_EUNSUPPORTED, "attn_bwd: only bf16 (dtype 0) is implemented, got %d", dtype);
+    return fail(SWATTN_EUNSUPPORTED, "%s: only bf16 (dtype 0) is implemented, got %d", what, dtype);
   TRY(check_ptr(q, "q"));
   TRY(check_ptr(k, "k"));
   TRY(check_ptr(v, "v"));
-  TRY(check_ptr(o, "o"));
+  if (pass != kDkdv) TRY(check_ptr(o, "o"));
   TRY(check_ptr(lse, "lse"));
   TRY(check_ptr(dout, "dout"));
-  TRY(check_ptr(dq, "dq"));
-  TRY(check_ptr(dk, "dk"));
-  TRY(check_ptr(dv, "dv"));
+  if (pass != kDkdv) TRY(check_ptr(dq, "dq"));
+  if (pass != kDq) {
+    TRY(check_ptr(dk, "dk"));
+    TRY(check_ptr(dv, "dv"));
+  }
   const size_t need = attn_bwd_workspace_bytes(B, H, T, D);
-  if (!ws) return fail(SWATTN_EWORKSPACE, "attn_bwd: workspace is NULL (%zu bytes needed)", need);
-  if (!aligned16(ws)) return fail(SWATTN_EINVAL, "attn_bwd: workspace is not 16-byte aligned");
+  if (!ws) return fail(SWATTN_EWORKSPACE, "%s: workspace is NULL (%zu bytes needed)", what, need);
+  if (!aligned16(ws)) return fail(SWATTN_EINVAL, "%s: workspace is not 16-byte aligned", what);
   if (ws_bytes < need)
-    return fail(SWATTN_EWORKSPACE, "attn_bwd: workspace of %zu bytes < %zu needed", ws_bytes, need);
+    return fail(SWATTN_EWORKSPACE, "%s: workspace of %zu bytes < %zu needed", what, ws_bytes, need);
   swattn::BwdArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -152,8 +161,39 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   a.window = window;
   a.scale = (float)(1.0 / sqrt((double)D));
   a.scale_log2 = scale_log2_for(D);
+  hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  return hip_status(swattn::launch_bwd(a, static_cast<hipStream_t>(stream)), "attn_bwd launch");
+  if (pass != kDkdv) {
+    const int rc = hip_status(swattn::launch_bwd_dq(a, s), what);
+    if (rc != SWATTN_OK) return rc;
+  }
+  if (pass != kDq) return hip_status(swattn::launch_bwd_dkdv(a, s), what);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, int B, int H, int T, int D, int window,
+             int dtype, void* ws, size_t ws_bytes, void* stream) {
+  return bwd_common("attn_bwd", kBoth, q, k, v, o, lse, dout, dq, dk, dv, B, H, T, D, window, dtype,
+                    ws, ws_bytes, stream);
+}
+
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dout, void* dq, int B, int H, int T, int D, int window, int dtype,
+                void* ws, size_t ws_bytes, void* stream) {
+  return bwd_common("attn_bwd_dq", kDq, q, k, v, o, lse, dout, dq, nullptr, nullptr, B, H, T, D,
+                    window, dtype, ws, ws_bytes, stream);
+}
+
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                  void* dk, void* dv, int B, int H, int T, int D, int window, int dtype, void* ws,
+                  size_t ws_bytes, void* stream) {
+  return bwd_common("attn_bwd_dkdv", kDkdv, q, k, v, nullptr, lse, dout, nullptr, dk, dv, B, H, T,
+                    D, window, dtype, ws, ws_bytes, stream);
 }
 
 int attn_prefill(const void* q, const void* kcache, const void* vcache, const int* lens, void* o,

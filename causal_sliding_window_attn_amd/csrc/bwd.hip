@@ -344,21 +344,31 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs p) {
 }
 
 template <int D>
-static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
+static hipError_t launch_dq_d(const BwdArgs& a, hipStream_t s) {
   constexpr int NW = 4;
   BwdArgs p = a;
   p.n_tiles = (p.T + 32 * NW - 1) / (32 * NW);
-  const unsigned grid_q = (unsigned)p.n_tiles * (unsigned)p.BH;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, NW>), dim3(grid_q), dim3(64 * NW), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const unsigned grid_k = (unsigned)((p.T + 32 * NW - 1) / (32 * NW)) * (unsigned)p.BH;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW>), dim3(grid_k), dim3(64 * NW), 0, s, p);
+  const unsigned grid = (unsigned)p.n_tiles * (unsigned)p.BH;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, NW>), dim3(grid), dim3(64 * NW), 0, s, p);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
-  return a.D == 64 ? launch_bwd_d<64>(a, s) : launch_bwd_d<128>(a, s);
+template <int D>
+static hipError_t launch_dkdv_d(const BwdArgs& a, hipStream_t s) {
+  constexpr int NW = 4;
+  BwdArgs p = a;
+  p.n_tiles = (p.T + 32 * NW - 1) / (32 * NW);
+  const unsigned grid = (unsigned)p.n_tiles * (unsigned)p.BH;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW>), dim3(grid), dim3(64 * NW), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s) {
+  return a.D == 64 ? launch_dq_d<64>(a, s) : launch_dq_d<128>(a, s);
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t s) {
+  return a.D == 64 ? launch_dkdv_d<64>(a, s) : launch_dkdv_d<128>(a, s);
 }
 
 }  // namespace swattn

@@ -69,7 +69,8 @@ struct AppendArgs {
 constexpr int kDecodeChunk = 64;  // keys per split of the decode
 
 hipError_t launch_fwd(const FwdArgs& a, bool f32, hipStream_t s);
-hipError_t launch_bwd(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecArgs& a, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 

@@ -87,6 +87,22 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              int dtype, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The two passes of attn_bwd, for callers that schedule or time them separately.  attn_bwd is
+ * exactly attn_bwd_dq followed by attn_bwd_dkdv on the same stream with the same arguments.
+ *   attn_bwd_dq:   writes Delta_i = dO_i . O_i into ws and dq.
+ *   attn_bwd_dkdv: reads Delta from ws as left there by attn_bwd_dq for the same (q, k, v, o, lse,
+ *                  dout, shapes, window) and writes dk, dv.  Called without that, results are
+ *                  undefined (but every access stays inside the buffers).
+ * Arguments, layouts, validation and status codes are those of attn_bwd.
+ */
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dout, void* dq, int B, int H, int T, int D, int window, int dtype,
+                void* ws, size_t ws_bytes, void* stream);
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                  void* dk, void* dv, int B, int H, int T, int D, int window, int dtype, void* ws,
+                  size_t ws_bytes, void* stream);
+
+/*
  * Engine prefill over a KV cache (walkthrough, section "Pretraining", Engine paragraph).
  *   q       [B, Tq, H, D] bf16: prompt b's queries at positions 0..L_b-1 (read).
  *   kcache, vcache [B, Lcap, H, D] bf16: prompt b's keys/values already in rows 0..L_b-1 (read).

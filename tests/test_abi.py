@@ -28,7 +28,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = set(declared_functions())
-    assert {"attn_fwd", "attn_bwd", "attn_decode", "attn_prefill", "attn_kv_append",
+    assert {"attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_decode", "attn_prefill", "attn_kv_append",
             "attn_bwd_workspace_bytes", "attn_decode_workspace_bytes", "attn_last_error",
             "attn_abi_version"} == names
 
@@ -96,6 +96,15 @@ def test_bwd_validation(lib):
     bad[5] = None  # dout
     assert lib.attn_bwd(*bad, 2, 3, 100, 128, 8, 0, P, need, None) == -1
     assert lib.attn_bwd(*args, 2, 3, 100, 100, 8, 0, P, need, None) == -2
+
+
+def test_bwd_pass_validation(lib):
+    need = lib.attn_bwd_workspace_bytes(2, 3, 100, 128)
+    assert lib.attn_bwd_dq(P, P, P, P, P, P, P, 2, 3, 100, 128, 8, 0, P, need - 1, None) == -3
+    assert lib.attn_bwd_dq(P, P, P, None, P, P, P, 2, 3, 100, 128, 8, 0, P, need, None) == -1
+    assert lib.attn_bwd_dkdv(P, P, P, P, P, None, P, 2, 3, 100, 128, 8, 0, P, need, None) == -1
+    assert lib.attn_bwd_dkdv(P, P, P, P, P, P, P, 2, 3, 100, 128, 8, 1, P, need, None) == -2
+    assert lib.attn_bwd_dkdv(P, P, P, P, P, P, P, 2, 3, 0, 128, 8, 0, P, need, None) == -1
 
 
 def test_prefill_append_decode_validation(lib):

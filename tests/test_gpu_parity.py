@@ -322,6 +322,19 @@ def test_determinism_and_full_window_bitwise(sw):
         assert torch.equal(a, b)
 
 
+def test_split_passes_equal_attn_bwd(sw):
+    q, k, v, do = W.random_attn(2, 200, 3, 128, seed=14)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = sw.attn_fwd(qd, kd, vd, window=70)
+    g = sw.attn_bwd(qd, kd, vd, o, lse, dod, window=70)
+    ws = torch.empty(sw.attn_bwd_workspace_bytes(2, 3, 200, 128), device=DEV, dtype=torch.uint8)
+    dq = sw.attn_bwd_dq(qd, kd, vd, o, lse, dod, ws, window=70)
+    dk, dv = sw.attn_bwd_dkdv(qd, kd, vd, lse, dod, ws, window=70)
+    torch.cuda.synchronize()
+    for a, b in zip(g, (dq, dk, dv)):
+        assert torch.equal(a, b)
+
+
 def test_gradient_sum_invariants(sw):
     q, k, v, do = W.random_attn(1, 256, 2, 128, seed=10)
     o, lse, (dq, dk, dv) = run_fwd_bwd(sw, q, k, v, do, 50)
