@@ -144,4 +144,60 @@ __device__ __forceinline__ void store_group(uint16_t* sN, uint16_t* sT, int g, i
   }
 }
 
+
+// ---------------------------------------------------------------------------------------------
+// Direct global -> LDS tile streaming (global_load_lds_dwordx4) and transposed LDS reads
+// (ds_read_b64_tr_b16), with the lane semantics measured on gfx950:
+//   global_load_lds 16 B: lane l's 16 bytes land at (wave-uniform LDS base) + 16 * l.
+//   ds_read_tr16_b64: within each group of 16 lanes, lane i receives in slot j element (i % 4) of
+//   the 8-byte row addressed by lane 4 * j + i / 4 of that group.
+// ---------------------------------------------------------------------------------------------
+#define SWATTN_AS3 __attribute__((address_space(3)))
+#define SWATTN_AS1 __attribute__((address_space(1)))
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void g2lds16(const uint16_t* gsrc, uint16_t* lds_base) {
+  __builtin_amdgcn_global_load_lds((const SWATTN_AS1 void*)gsrc, (SWATTN_AS3 void*)lds_base, 16, 0,
+                                   0);
+}
+
+__device__ __forceinline__ uint2 lds_tr16(const uint16_t* p) {
+  v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SWATTN_AS3 v4i16*)p);
+  return __builtin_bit_cast(uint2, r);
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt / lgkmcnt left open).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Physical 16-byte chunk of logical chunk c in row r of a row-major [rows][D] bf16 tile.
+// K-like tiles (read one 16-byte chunk per lane, 32 consecutive rows): XOR with the row.
+template <int D>
+__device__ __forceinline__ int swz_rowread(int r, int c) {
+  return c ^ (r & (D / 8 - 1));
+}
+// V-like tiles (read with ds_read_tr16_b64: 4 consecutive rows x 64 bytes per 32 lanes): move
+// each of 4 consecutive rows to a different 64-byte bank segment.
+template <int D>
+__device__ __forceinline__ int swz_trread(int r, int c) {
+  return D == 128 ? (c ^ (4 * (r & 3))) : (c ^ (4 * ((r >> 1) & 1)));
+}
+
+// One MFMA A fragment of V^T for d-rows 32 * mb .. +32 and the 16 sequence rows starting at
+// `row0`, read from a row-major tile swizzled with swz_trread: slot s of lane (d, half) holds
+// row row0 + 8 * (s / 4) + 4 * half + (s % 4).
+template <int D>
+__device__ __forceinline__ uint4 tr_frag(const uint16_t* tile, int row0, int mb, int lane) {
+  const int g = lane >> 4, j = (lane >> 2) & 3, c = lane & 3, h = g >> 1;
+  const int d = 32 * mb + 16 * (g & 1) + 4 * c;  // first of the 4 features this lane addresses
+  const int r1 = row0 + 4 * h + j, r2 = r1 + 8;
+  const int ch = d >> 3, sub = d & 7;
+  const uint2 lo = lds_tr16(tile + r1 * D + 8 * swz_trread<D>(r1, ch) + sub);
+  const uint2 hi = lds_tr16(tile + r2 * D + 8 * swz_trread<D>(r2, ch) + sub);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
 }  // namespace swattn

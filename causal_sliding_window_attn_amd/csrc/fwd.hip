@@ -6,14 +6,16 @@
 // serves the Engine's prefill phase (followin.io walkthrough, section "Pretraining", Engine
 // paragraph).  Query i sees key j iff j <= i and i - j < w; scale 1/sqrt(D).
 //
-// Design (bf16): one workgroup = NW waves x 32 queries of one (batch, head).  Each wave keeps its
-// queries' Q in registers as MFMA B fragments and computes S^T = K Q^T per 64-key tile, so a lane
-// owns one query column: the row max / row sum of the online softmax are lane-local plus a single
-// v_permlane32_swap.  O^T = V^T P^T reuses the S^T accumulators directly as the B operand (P split
-// into bf16 hi + lo, two MFMAs on one V fragment); V is written to LDS transposed, in the matching
-// permuted key order.  K/V tiles
-// outside [q0 - w + 1, q_end] are never loaded; per wave, tiles wholly outside the window are
-// skipped and only tiles crossing the diagonal or the window edge evaluate the mask.
+// Design (bf16): one workgroup = NW waves x 32 queries of one (batch, head), two workgroups per CU.
+// Each wave keeps its queries' Q in registers as MFMA B fragments and computes S^T = K Q^T per
+// 64-key tile, so a lane owns one query column: the row max / row sum of the online softmax are
+// lane-local plus one v_permlane32_swap.  O^T = V^T P^T reuses the S^T accumulators directly as the
+// B operand (P split into bf16 hi + lo, two MFMAs on one V fragment); the V^T fragments come from
+// the row-major V tile through ds_read_b64_tr_b16.  K/V tiles stream global -> LDS with
+// global_load_lds into a two-stage ring, one tile ahead of the compute (one barrier per tile).  Tiles outside
+// [q0 - w + 1, q_end] are never loaded; per wave, tiles wholly outside the window are skipped and
+// only tiles crossing the diagonal or the window edge evaluate the mask.  O is rescaled lazily,
+// only when a row maximum grows by more than 2^8.
 #include "common.h"
 #include "launch.h"
 
@@ -21,19 +23,129 @@ namespace swattn {
 
 constexpr int kFwdBC = 64;  // keys per tile
 
+// Streams one 64-key tile of K and of V into LDS (row-major, swizzled) with global_load_lds.
+// Rows past the valid length are clamped to the last valid row: their scores are masked, so any
+// finite data will do, and no load leaves the tensor.
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs p) {
+__device__ __forceinline__ void fwd_issue_tile(const uint16_t* kb, const uint16_t* vb, int rs,
+                                               int kt, int L, uint16_t* sK, uint16_t* sV,
+                                               int wave, int lane) {
+  constexpr int CPR = D / 8;         // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;      // rows per load instruction (one 1 KB instruction per wave)
+  constexpr int INSTS = kFwdBC / RPI;
+  const int cp = lane % CPR;
+#pragma unroll
+  for (int i = wave; i < INSTS; i += NW) {
+    const int r = i * RPI + lane / CPR;
+    const int j = min(kt * kFwdBC + r, L - 1);
+    g2lds16(kb + (int64_t)j * rs + 8 * (cp ^ (r & (CPR - 1))), sK + i * 512);
+    g2lds16(vb + (int64_t)j * rs + 8 * swz_trread<D>(r, cp), sV + i * 512);
+  }
+}
+
+// Per-wave state of the forward that lives across key tiles.
+template <int D>
+struct FwdState {
+  f32x16 oacc[D / 32];
+  float m_use, l_run;
+};
+
+// One key tile: issue the DMA of the next tile into `nxt`, then consume `cur`.  Within one call the
+// two stages are distinct buffers, which the __restrict__ qualifiers state; that lets the compiler
+// see that the LDS reads of `cur` do not depend on the DMA writes to `nxt` still in flight.
+template <int D, int NW>
+__device__ __forceinline__ void fwd_step(const uint16_t* __restrict__ cur,
+                                         uint16_t* __restrict__ nxt, bool issue_next, int kt_next,
+                                         const uint16_t* kb, const uint16_t* vb, int rs, int L,
+                                         int kt, int qa, int qi, int w, float sl2,
+                                         const uint4 (&qf)[D / 16], FwdState<D>& S, int wave,
+                                         int lane) {
+  constexpr int BC = kFwdBC, DK = D / 16, MB = D / 32, NB = BC / 32, TILE = BC * D;
+  constexpr float kRescale = 8.f;  // lazy rescaling threshold (log2 units)
+  const int half = lane >> 5, l32 = lane & 31;
+  if (issue_next) fwd_issue_tile<D, NW>(kb, vb, rs, kt_next, L, nxt, nxt + TILE, wave, lane);
+
+  const uint16_t* sK = cur;
+  const uint16_t* sV = cur + TILE;
+  const int k_lo = kt * BC, k_hi = k_lo + BC - 1;
+  const int qz = qa + 31;
+  if ((qa >= L) || (k_lo > qz) || (qa - k_hi >= w)) return;
+  const bool need_mask = !(k_hi <= qa && qz - k_lo < w);
+  // S^T (keys x queries) for the tile
+  f32x16 s[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) s[nb] = zero16();
+#pragma unroll
+  for (int t = 0; t < DK; ++t)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int row = nb * 32 + l32;
+      const uint4 a =
+          *reinterpret_cast<const uint4*>(sK + row * D + 8 * swz_rowread<D>(row, 2 * t + half));
+      s[nb] = mfma32(a, qf[t], s[nb]);
+    }
+  // online softmax in the log2 domain; this lane owns query qi
+  float mraw = -INFINITY;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (need_mask) {
+        const int key = k_lo + nb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (key > qi || qi - key >= w) s[nb][r] = -INFINITY;
+      }
+      mraw = fmaxf(mraw, s[nb][r]);
+    }
+  const float m_tile = max_with_partner(mraw) * sl2;
+  // rescale O only when some row max has grown past the threshold (exact either way)
+  if (__builtin_amdgcn_ballot_w64(m_tile > S.m_use + kRescale) != 0) {
+    const float m_new = fmaxf(S.m_use, m_tile);
+    // a row with no visible key yet keeps m = -inf (and O = 0, l = 0): avoid exp2(-inf + inf)
+    const float alpha = (m_new == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(S.m_use - m_new);
+    S.l_run *= alpha;
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S.oacc[m][r] *= alpha;
+    S.m_use = m_new;
+  }
+  const float m_eff = (S.m_use == -INFINITY) ? 0.f : S.m_use;
+  float lsum = 0.f;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e = __builtin_amdgcn_exp2f(fmaf(s[nb][r], sl2, -m_eff));
+      s[nb][r] = e;
+      lsum += e;
+    }
+  S.l_run += lsum;
+  // O^T += V^T P^T with P carried as bf16 hi + lo (the output is stored in bf16, whose rounding
+  // alone costs up to half an ulp, so P must not add 2^-9 relative on top)
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      uint4 ph, pl;
+      pack_frag_split(s[nb], u, ph, pl);
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        const uint4 a = tr_frag<D>(sV, nb * 32 + 16 * u, m, lane);
+        S.oacc[m] = mfma32(a, ph, S.oacc[m]);
+        S.oacc[m] = mfma32(a, pl, S.oacc[m]);
+      }
+    }
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs p) {
   constexpr int BR = 32 * NW;
   constexpr int BC = kFwdBC;
-  constexpr int NT = 64 * NW;
-  constexpr int DK = D / 16;             // MFMA k-steps over D
-  constexpr int MB = D / 32;             // 32-row blocks of O^T
-  constexpr int NB = BC / 32;            // 32-key blocks per tile
-  constexpr int GROUPS = (BC / 4) * (D / 8);  // (4 keys x 8 features) load items per tile
-  constexpr int ITEMS = (GROUPS + NT - 1) / NT;
+  constexpr int DK = D / 16;  // MFMA k-steps over D
+  constexpr int MB = D / 32;  // 32-row blocks of O^T
+  constexpr int TILE = BC * D;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BC * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * BC];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * TILE];  // [stage][K|V]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -67,130 +179,24 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs p) {
   for (int t = 0; t < DK; ++t)
     qf[t] = qvalid ? ldg16(qb + (int64_t)qi * rs + 16 * t + 8 * half) : make_uint4(0, 0, 0, 0);
 
-  f32x16 oacc[MB];
+  FwdState<D> S;
 #pragma unroll
-  for (int m = 0; m < MB; ++m) oacc[m] = zero16();
-  float m_run = -INFINITY, l_run = 0.f;
-  const float sl2 = p.scale_log2;
+  for (int m = 0; m < MB; ++m) S.oacc[m] = zero16();
+  S.m_use = -INFINITY;
+  S.l_run = 0.f;
 
-  uint4 kr[ITEMS][4], vr[ITEMS][4];
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-      const int idx = tid + it * NT;
-      if (idx < GROUPS) {
-        const int g = idx / (D / 8), c = idx % (D / 8);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = kt * BC + 4 * g + i;
-          if (j < L) {
-            kr[it][i] = ldg16(kb + (int64_t)j * rs + 8 * c);
-            vr[it][i] = ldg16(vb + (int64_t)j * rs + 8 * c);
-          } else {
-            kr[it][i] = make_uint4(0, 0, 0, 0);
-            vr[it][i] = make_uint4(0, 0, 0, 0);
-          }
-        }
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-      const int idx = tid + it * NT;
-      if (idx < GROUPS) {
-        const int g = idx / (D / 8), c = idx % (D / 8);
-        store_group<D, BC, true, false>(sK, nullptr, g, c, kr[it]);
-        store_group<D, BC, false, true>(nullptr, sVt, g, c, vr[it]);
-      }
-    }
-  };
-
-  load_tile(kt_begin);
+  fwd_issue_tile<D, NW>(kb, vb, rs, kt_begin, L, smem, smem + TILE, wave, lane);
+  uint16_t* stage0 = smem;
+  uint16_t* stage1 = smem + 2 * TILE;
   for (int kt = kt_begin; kt <= kt_end; ++kt) {
-    if (kt != kt_begin) __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (kt < kt_end) load_tile(kt + 1);
-
-    const int k_lo = kt * BC, k_hi = k_lo + BC - 1;
-    const int qz = qa + 31;
-    const bool skip = (qa >= L) || (k_lo > qz) || (qa - k_hi >= w);
-    if (skip) continue;
-    const bool need_mask = !(k_hi <= qa && qz - k_lo < w);
-
-    // S^T (keys x queries) for the tile.
-    f32x16 s[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      s[nb] = zero16();
-      const int row = nb * 32 + l32;
-#pragma unroll
-      for (int t = 0; t < DK; ++t) {
-        const uint4 a = *reinterpret_cast<const uint4*>(sK + normal_off<D>(row, 2 * t + half));
-        s[nb] = mfma32(a, qf[t], s[nb]);
-      }
-    }
-
-    // Online softmax in the log2 domain; this lane owns query qi.
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[nb][r] * sl2;
-        if (need_mask) {
-          const int key = k_lo + nb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key > qi || qi - key >= w) x = -INFINITY;
-        }
-        s[nb][r] = x;
-        mloc = fmaxf(mloc, x);
-      }
-    }
-    const float m_new = fmaxf(m_run, max_with_partner(mloc));
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float lsum = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(s[nb][r] - m_use);
-        s[nb][r] = e;
-        lsum += e;
-      }
-    }
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-#pragma unroll
-    for (int m = 0; m < MB; ++m)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[m][r] *= alpha;
-
-    // O^T += V^T P^T, with P carried as bf16 hi + lo: the output is stored in bf16, whose rounding
-    // alone costs up to half an ulp, so P must not add another 2^-9 relative error on top.
-    uint4 ph[NB][2], pl[NB][2];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      pack_frag_split(s[nb], 0, ph[nb][0], pl[nb][0]);
-      pack_frag_split(s[nb], 1, ph[nb][1], pl[nb][1]);
-    }
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      const int d = m * 32 + l32;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const uint4 a =
-              *reinterpret_cast<const uint4*>(sVt + trans_off<BC>(d, 2 * (2 * nb + u) + half));
-          oacc[m] = mfma32(a, ph[nb][u], oacc[m]);
-          oacc[m] = mfma32(a, pl[nb][u], oacc[m]);
-        }
-    }
+    wait_vmcnt<0>();  // this tile's DMA (the only one in flight) has landed
+    __syncthreads();  // ... for every wave, and every wave is done with the other stage
+    const bool even = ((kt - kt_begin) & 1) == 0;
+    fwd_step<D, NW>(even ? stage0 : stage1, even ? stage1 : stage0, kt < kt_end, kt + 1, kb, vb,
+                    rs, L, kt, qa, qi, w, p.scale_log2, qf, S, wave, lane);
   }
 
-  const float l_tot = sum_with_partner(l_run);
+  const float l_tot = sum_with_partner(S.l_run);
   if (!qvalid) return;
   const float inv = 1.f / l_tot;
   uint16_t* ob = p.o + (int64_t)b * p.q_bstride + h * D + (int64_t)qi * rs;
@@ -199,12 +205,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint2 st;
-      st.x = pack_bf16x2(oacc[m][4 * j + 0] * inv, oacc[m][4 * j + 1] * inv);
-      st.y = pack_bf16x2(oacc[m][4 * j + 2] * inv, oacc[m][4 * j + 3] * inv);
+      st.x = pack_bf16x2(S.oacc[m][4 * j + 0] * inv, S.oacc[m][4 * j + 1] * inv);
+      st.y = pack_bf16x2(S.oacc[m][4 * j + 2] * inv, S.oacc[m][4 * j + 3] * inv);
       *reinterpret_cast<uint2*>(ob + m * 32 + 8 * j + 4 * half) = st;
     }
   if (p.lse && half == 0)
-    p.lse[(int64_t)bh * p.lse_T + qi] = (m_run + __log2f(l_tot)) * kLn2;
+    p.lse[(int64_t)bh * p.lse_T + qi] = (S.m_use + __log2f(l_tot)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------------------------
