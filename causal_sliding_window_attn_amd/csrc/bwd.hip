@@ -10,11 +10,12 @@
 //
 // dQ pass: a workgroup owns NW x 32 queries (Q, dO in registers as B fragments, lane = query as in
 // the forward), computes Delta for them first and writes it to the workspace, then walks the
-// in-window key tiles: S^T = K Q^T, dP^T = V dO^T, dS^T, and dQ^T += K^T dS^T with K^T stored
-// transposed in LDS.
+// in-window key tiles: S^T = K Q^T, dP^T = V dO^T, dS^T, and dQ^T += K^T dS^T.
 // dK/dV pass: a workgroup owns NW x 32 keys (K, V in registers, lane = key) and walks the query
-// tiles that can see them: S = Q K^T, dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS with
-// dO^T and Q^T stored transposed in LDS.
+// tiles that can see them: S = Q K^T, dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS.
+// Both passes stream their tiles global -> LDS with global_load_lds into a two-stage ring (one
+// tile ahead, one barrier per tile) and take every transposed operand (K^T, Q^T, dO^T) straight
+// from the row-major tile with ds_read_b64_tr_b16.
 #include "common.h"
 #include "launch.h"
 
@@ -23,16 +24,60 @@ namespace swattn {
 constexpr int kBwdBC = 64;  // keys per tile in the dQ pass
 constexpr int kBwdBQ = 64;  // queries per tile in the dK/dV pass
 
+// ------------------------------------------------------------------------------------------ dQ
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs p) {
-  constexpr int BR = 32 * NW, BC = kBwdBC, NT = 64 * NW;
-  constexpr int DK = D / 16, MB = D / 32, NB = BC / 32;
-  constexpr int GROUPS = (BC / 4) * (D / 8);
-  constexpr int ITEMS = (GROUPS + NT - 1) / NT;
+__device__ __forceinline__ void dq_step(const uint16_t* __restrict__ cur,
+                                        uint16_t* __restrict__ nxt, bool issue_next,
+                                        const uint16_t* kb, const uint16_t* vb, int rs, int T,
+                                        int kt, int qa, int qi, int w, float sl2, float lse2,
+                                        float delta, const uint4 (&qf)[D / 16],
+                                        const uint4 (&df)[D / 16], f32x16 (&dqacc)[D / 32],
+                                        int wave, int lane) {
+  constexpr int BC = kBwdBC, DK = D / 16, MB = D / 32, NB = BC / 32, TILE = BC * D;
+  const int half = lane >> 5, l32 = lane & 31;
+  if (issue_next) {
+    issue_rows<D, NW, BC>(kb, rs, (kt + 1) * BC, T - 1, nxt, wave, lane);
+    issue_rows<D, NW, BC>(vb, rs, (kt + 1) * BC, T - 1, nxt + TILE, wave, lane);
+  }
+  const uint16_t* sK = cur;
+  const uint16_t* sV = cur + TILE;
+  const int k_lo = kt * BC, k_hi = k_lo + BC - 1, qz = qa + 31;
+  if ((qa >= T) || (k_lo > qz) || (qa - k_hi >= w)) return;
+  const bool need_mask = !(k_hi <= qa && qz - k_lo < w);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    f32x16 s = zero16(), dp = zero16();
+    const int row = nb * 32 + l32;
+#pragma unroll
+    for (int t = 0; t < DK; ++t) {
+      s = mfma32(row_chunk<D>(sK, row, 2 * t + half), qf[t], s);
+      dp = mfma32(row_chunk<D>(sV, row, 2 * t + half), df[t], dp);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse2));
+      if (need_mask) {
+        const int key = k_lo + nb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (key > qi || qi - key >= w) pr = 0.f;
+      }
+      s[r] = pr * (dp[r] - delta);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint4 dsf = pack_frag(s, u);
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+        dqacc[m] = mfma32(tr_frag<D>(sK, nb * 32 + 16 * u, m, lane), dsf, dqacc[m]);
+    }
+  }
+}
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BC * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sKt[D * BC];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[BC * D];
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs p) {
+  constexpr int BR = 32 * NW, BC = kBwdBC;
+  constexpr int DK = D / 16, MB = D / 32, TILE = BC * D;
+
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * TILE];  // [stage][K|V]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -50,9 +95,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs p) {
 
   const int64_t base = (int64_t)b * p.bstride + h * D;
   const int rs = p.row_stride;
-  const uint16_t* qb = p.q + base;
   const uint16_t* kb = p.k + base;
   const uint16_t* vb = p.v + base;
+
+  issue_rows<D, NW, BC>(kb, rs, kt_begin * BC, T - 1, smem, wave, lane);
+  issue_rows<D, NW, BC>(vb, rs, kt_begin * BC, T - 1, smem + TILE, wave, lane);
 
   const int qa = q0 + 32 * wave;
   const int qi = qa + l32;
@@ -80,93 +127,19 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs p) {
   const float delta = sum_with_partner(dsum);
   if (qvalid && half == 0) p.delta[(int64_t)bh * T + qi] = delta;
   const float lse2 = qvalid ? p.lse[(int64_t)bh * T + qi] * kLog2e : 0.f;
-  const float sl2 = p.scale_log2;
 
   f32x16 dqacc[MB];
 #pragma unroll
   for (int m = 0; m < MB; ++m) dqacc[m] = zero16();
 
-  uint4 kr[ITEMS][4], vr[ITEMS][4];
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-      const int idx = tid + it * NT;
-      if (idx < GROUPS) {
-        const int g = idx / (D / 8), c = idx % (D / 8);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = kt * BC + 4 * g + i;
-          if (j < T) {
-            kr[it][i] = ldg16(kb + (int64_t)j * rs + 8 * c);
-            vr[it][i] = ldg16(vb + (int64_t)j * rs + 8 * c);
-          } else {
-            kr[it][i] = make_uint4(0, 0, 0, 0);
-            vr[it][i] = make_uint4(0, 0, 0, 0);
-          }
-        }
-      }
-    }
-  };
-
-  load_tile(kt_begin);
+  uint16_t* stage0 = smem;
+  uint16_t* stage1 = smem + 2 * TILE;
   for (int kt = kt_begin; kt <= kt_end; ++kt) {
-    if (kt != kt_begin) __syncthreads();
-#pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-      const int idx = tid + it * NT;
-      if (idx < GROUPS) {
-        const int g = idx / (D / 8), c = idx % (D / 8);
-        store_group<D, BC, true, true>(sK, sKt, g, c, kr[it]);
-        store_group<D, BC, true, false>(sV, nullptr, g, c, vr[it]);
-      }
-    }
+    wait_vmcnt<0>();
     __syncthreads();
-    if (kt < kt_end) load_tile(kt + 1);
-
-    const int k_lo = kt * BC, k_hi = k_lo + BC - 1, qz = qa + 31;
-    if ((qa >= T) || (k_lo > qz) || (qa - k_hi >= w)) continue;
-    const bool need_mask = !(k_hi <= qa && qz - k_lo < w);
-
-    f32x16 s[NB], dp[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      s[nb] = zero16();
-      dp[nb] = zero16();
-      const int row = nb * 32 + l32;
-#pragma unroll
-      for (int t = 0; t < DK; ++t) {
-        const int off = normal_off<D>(row, 2 * t + half);
-        s[nb] = mfma32(*reinterpret_cast<const uint4*>(sK + off), qf[t], s[nb]);
-        dp[nb] = mfma32(*reinterpret_cast<const uint4*>(sV + off), df[t], dp[nb]);
-      }
-    }
-    uint4 dsf[NB][2];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(s[nb][r] * sl2 - lse2);
-        if (need_mask) {
-          const int key = k_lo + nb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key > qi || qi - key >= w) pr = 0.f;
-        }
-        s[nb][r] = pr * (dp[nb][r] - delta);
-      }
-      dsf[nb][0] = pack_frag(s[nb], 0);
-      dsf[nb][1] = pack_frag(s[nb], 1);
-    }
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      const int d = m * 32 + l32;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const uint4 a =
-              *reinterpret_cast<const uint4*>(sKt + trans_off<BC>(d, 2 * (2 * nb + u) + half));
-          dqacc[m] = mfma32(a, dsf[nb][u], dqacc[m]);
-        }
-    }
+    const bool even = ((kt - kt_begin) & 1) == 0;
+    dq_step<D, NW>(even ? stage0 : stage1, even ? stage1 : stage0, kt < kt_end, kb, vb, rs, T, kt,
+                   qa, qi, w, p.scale_log2, lse2, delta, qf, df, dqacc, wave, lane);
   }
 
   if (!qvalid) return;
@@ -183,19 +156,96 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs p) {
     }
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs p) {
-  constexpr int BK = 32 * NW, BQ = kBwdBQ, NT = 64 * NW;
-  constexpr int DK = D / 16, MB = D / 32, QB = BQ / 32;
-  constexpr int GROUPS = (BQ / 4) * (D / 8);
-  constexpr int ITEMS = (GROUPS + NT - 1) / NT;
+// ---------------------------------------------------------------------------------------- dK/dV
+// One query tile's stage: Q rows, dO rows (row-major, swizzled), then LSE and Delta of the rows.
+template <int D>
+struct DkdvStage {
+  static constexpr int TILE = kBwdBQ * D;
+  static constexpr int ELEMS = 2 * TILE + 2 * kBwdBQ * 2;  // in uint16 units
+};
 
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[BQ * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sQt[D * BQ];
-  __shared__ __attribute__((aligned(16))) uint16_t sO[BQ * D];   // dO, row-major
-  __shared__ __attribute__((aligned(16))) uint16_t sOt[D * BQ];  // dO, transposed
-  __shared__ float sL[BQ];
-  __shared__ float sDl[BQ];
+template <int D, int NW>
+__device__ __forceinline__ void dkdv_issue(const uint16_t* qb, const uint16_t* db,
+                                           const float* lseb, const float* delb, int rs, int qt,
+                                           int T, uint16_t* stage, int wave, int lane) {
+  constexpr int BQ = kBwdBQ, TILE = DkdvStage<D>::TILE;
+  issue_rows<D, NW, BQ>(qb, rs, qt * BQ, T - 1, stage, wave, lane);
+  issue_rows<D, NW, BQ>(db, rs, qt * BQ, T - 1, stage + TILE, wave, lane);
+  static_assert(BQ == 64, "one 4-byte DMA per lane covers the 64 rows' LSE / Delta");
+  if (wave == NW - 1) {
+    const int j = min(qt * BQ + lane, T - 1);
+    float* sl = reinterpret_cast<float*>(stage + 2 * TILE);
+    g2lds4(lseb + j, sl);
+    g2lds4(delb + j, sl + BQ);
+  }
+}
+
+template <int D, int NW>
+__device__ __forceinline__ void dkdv_step(const uint16_t* __restrict__ cur,
+                                          uint16_t* __restrict__ nxt, bool issue_next,
+                                          const uint16_t* qb, const uint16_t* db,
+                                          const float* lseb, const float* delb, int rs, int T,
+                                          int qt, int ka, int kj, int w, float sl2,
+                                          const uint4 (&kf)[D / 16], const uint4 (&vf)[D / 16],
+                                          f32x16 (&dkacc)[D / 32], f32x16 (&dvacc)[D / 32],
+                                          int wave, int lane) {
+  constexpr int BQ = kBwdBQ, DK = D / 16, MB = D / 32, QB = BQ / 32, TILE = DkdvStage<D>::TILE;
+  const int half = lane >> 5, l32 = lane & 31;
+  if (issue_next) dkdv_issue<D, NW>(qb, db, lseb, delb, rs, qt + 1, T, nxt, wave, lane);
+  const uint16_t* sQ = cur;
+  const uint16_t* sO = cur + TILE;
+  const float* sL = reinterpret_cast<const float*>(cur + 2 * TILE);
+  const float* sDl = sL + BQ;
+#pragma unroll
+  for (int qb2 = 0; qb2 < QB; ++qb2) {
+    const int qs = qt * BQ + 32 * qb2, qz = qs + 31, kz = ka + 31;
+    if (ka >= T || qz < ka || qs - kz >= w || qs >= T) continue;
+    const bool need_mask = !(qs >= kz && qz - ka < w && qz < T);
+    f32x16 s = zero16(), dp = zero16();
+    const int row = 32 * qb2 + l32;
+#pragma unroll
+    for (int t = 0; t < DK; ++t) {
+      s = mfma32(row_chunk<D>(sQ, row, 2 * t + half), kf[t], s);
+      dp = mfma32(row_chunk<D>(sO, row, 2 * t + half), vf[t], dp);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ql0 = 32 * qb2 + 8 * j + 4 * half;
+      const float4 l4 = *reinterpret_cast<const float4*>(sL + ql0);
+      const float4 d4 = *reinterpret_cast<const float4*>(sDl + ql0);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * j + i;
+        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lv[i] * kLog2e));
+        if (need_mask) {
+          const int qg = qt * BQ + ql0 + i;
+          if (kj > qg || qg - kj >= w || qg >= T) pr = 0.f;
+        }
+        s[r] = pr;
+        dp[r] = pr * (dp[r] - dv[i]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint4 pf = pack_frag(s, u);
+      const uint4 dsf = pack_frag(dp, u);
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        dvacc[m] = mfma32(tr_frag<D>(sO, 32 * qb2 + 16 * u, m, lane), pf, dvacc[m]);
+        dkacc[m] = mfma32(tr_frag<D>(sQ, 32 * qb2 + 16 * u, m, lane), dsf, dkacc[m]);
+      }
+    }
+  }
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs p) {
+  constexpr int BK = 32 * NW, BQ = kBwdBQ;
+  constexpr int DK = D / 16, MB = D / 32, SE = DkdvStage<D>::ELEMS;
+
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * SE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -217,10 +267,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs p) {
   const float* lseb = p.lse + (int64_t)bh * T;
   const float* delb = p.delta + (int64_t)bh * T;
 
+  dkdv_issue<D, NW>(qb, db, lseb, delb, rs, qt_begin, T, smem, wave, lane);
+
   const int ka = k0 + 32 * wave;
   const int kj = ka + l32;
   const bool kvalid = kj < T;
-
   uint4 kf[DK], vf[DK];
 #pragma unroll
   for (int t = 0; t < DK; ++t) {
@@ -234,95 +285,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs p) {
     dkacc[m] = zero16();
     dvacc[m] = zero16();
   }
-  const float sl2 = p.scale_log2;
 
-  uint4 qr[ITEMS][4], dr[ITEMS][4];
-  float lr = 0.f, dl = 0.f;
-  auto load_tile = [&](int qt) {
-#pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-      const int idx = tid + it * NT;
-      if (idx < GROUPS) {
-        const int g = idx / (D / 8), c = idx % (D / 8);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = qt * BQ + 4 * g + i;
-          if (j < T) {
-            qr[it][i] = ldg16(qb + (int64_t)j * rs + 8 * c);
-            dr[it][i] = ldg16(db + (int64_t)j * rs + 8 * c);
-          } else {
-            qr[it][i] = make_uint4(0, 0, 0, 0);
-            dr[it][i] = make_uint4(0, 0, 0, 0);
-          }
-        }
-      }
-    }
-    if (tid < BQ) {
-      const int j = qt * BQ + tid;
-      lr = j < T ? lseb[j] * kLog2e : INFINITY;  // +inf makes P = 0 for rows past T
-      dl = j < T ? delb[j] : 0.f;
-    }
-  };
-
-  load_tile(qt_begin);
+  uint16_t* stage0 = smem;
+  uint16_t* stage1 = smem + SE;
   for (int qt = qt_begin; qt <= qt_end; ++qt) {
-    if (qt != qt_begin) __syncthreads();
-#pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-      const int idx = tid + it * NT;
-      if (idx < GROUPS) {
-        const int g = idx / (D / 8), c = idx % (D / 8);
-        store_group<D, BQ, true, true>(sQ, sQt, g, c, qr[it]);
-        store_group<D, BQ, true, true>(sO, sOt, g, c, dr[it]);
-      }
-    }
-    if (tid < BQ) {
-      sL[tid] = lr;
-      sDl[tid] = dl;
-    }
+    wait_vmcnt<0>();
     __syncthreads();
-    if (qt < qt_end) load_tile(qt + 1);
-
-#pragma unroll
-    for (int qb2 = 0; qb2 < QB; ++qb2) {
-      const int qs = qt * BQ + 32 * qb2, qz = qs + 31, kz = ka + 31;
-      if (ka >= T || qz < ka || qs - kz >= w) continue;
-      const bool need_mask = !(qs >= kz && qz - ka < w && qz < T);
-      f32x16 s = zero16(), dp = zero16();
-      const int row = 32 * qb2 + l32;
-#pragma unroll
-      for (int t = 0; t < DK; ++t) {
-        const int off = normal_off<D>(row, 2 * t + half);
-        s = mfma32(*reinterpret_cast<const uint4*>(sQ + off), kf[t], s);
-        dp = mfma32(*reinterpret_cast<const uint4*>(sO + off), vf[t], dp);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ql = 32 * qb2 + 8 * (r >> 2) + 4 * half + (r & 3);
-        float pr = __builtin_amdgcn_exp2f(s[r] * sl2 - sL[ql]);
-        if (need_mask) {
-          const int qg = qt * BQ + ql;
-          if (kj > qg || qg - kj >= w) pr = 0.f;
-        }
-        s[r] = pr;
-        dp[r] = pr * (dp[r] - sDl[ql]);
-      }
-      uint4 pf[2], dsf[2];
-      pf[0] = pack_frag(s, 0);
-      pf[1] = pack_frag(s, 1);
-      dsf[0] = pack_frag(dp, 0);
-      dsf[1] = pack_frag(dp, 1);
-#pragma unroll
-      for (int m = 0; m < MB; ++m) {
-        const int d = m * 32 + l32;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int off = trans_off<BQ>(d, 2 * (2 * qb2 + u) + half);
-          dvacc[m] = mfma32(*reinterpret_cast<const uint4*>(sOt + off), pf[u], dvacc[m]);
-          dkacc[m] = mfma32(*reinterpret_cast<const uint4*>(sQt + off), dsf[u], dkacc[m]);
-        }
-      }
-    }
+    const bool even = ((qt - qt_begin) & 1) == 0;
+    dkdv_step<D, NW>(even ? stage0 : stage1, even ? stage1 : stage0, qt < qt_end, qb, db, lseb,
+                     delb, rs, T, qt, ka, kj, w, p.scale_log2, kf, vf, dkacc, dvacc, wave, lane);
   }
 
   if (!kvalid) return;
@@ -343,6 +314,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs p) {
     }
 }
 
+// ------------------------------------------------------------------------------------- launchers
 template <int D>
 static hipError_t launch_dq_d(const BwdArgs& a, hipStream_t s) {
   constexpr int NW = 4;

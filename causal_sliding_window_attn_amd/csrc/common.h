@@ -161,6 +161,11 @@ __device__ __forceinline__ void g2lds16(const uint16_t* gsrc, uint16_t* lds_base
                                    0);
 }
 
+__device__ __forceinline__ void g2lds4(const float* gsrc, float* lds_base) {
+  __builtin_amdgcn_global_load_lds((const SWATTN_AS1 void*)gsrc, (SWATTN_AS3 void*)lds_base, 4, 0,
+                                   0);
+}
+
 __device__ __forceinline__ uint2 lds_tr16(const uint16_t* p) {
   v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SWATTN_AS3 v4i16*)p);
   return __builtin_bit_cast(uint2, r);
@@ -173,21 +178,44 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Physical 16-byte chunk of logical chunk c in row r of a row-major [rows][D] bf16 tile.
-// K-like tiles (read one 16-byte chunk per lane, 32 consecutive rows): XOR with the row.
+// Physical 16-byte chunk of logical chunk c in row r of a row-major [rows][D] bf16 tile.  One
+// swizzle serves both ways a tile is read:
+//   row reads (ds_read_b128, 32 consecutive rows, one chunk each): the XOR term is a bijection over
+//   every 16 rows (D = 128) or over the 8 rows of one 256-byte bank parity (D = 64);
+//   transposed reads (ds_read_b64_tr_b16, 4 consecutive rows x 64 bytes per 32 lanes): the 4 rows
+//   land in 4 different 64-byte bank segments.
 template <int D>
-__device__ __forceinline__ int swz_rowread(int r, int c) {
-  return c ^ (r & (D / 8 - 1));
+__device__ __forceinline__ int swz(int r, int c) {
+  return D == 128 ? (c ^ (4 * (r & 3) + ((r >> 2) & 3)))
+                  : (c ^ (4 * ((r >> 1) & 1) + ((r >> 2) & 3)));
 }
-// V-like tiles (read with ds_read_tr16_b64: 4 consecutive rows x 64 bytes per 32 lanes): move
-// each of 4 consecutive rows to a different 64-byte bank segment.
+
+// Streams `rows` consecutive rows (row0 .. row0 + rows - 1 of a [*, rs]-strided bf16 tensor, clamped
+// to row `last`) into a row-major swizzled LDS tile with global_load_lds, NW waves sharing the work.
+// Clamped rows hold a copy of a valid row: callers mask them, and no load leaves the tensor.
+template <int D, int NW, int ROWS>
+__device__ __forceinline__ void issue_rows(const uint16_t* base, int rs, int row0, int last,
+                                           uint16_t* tile, int wave, int lane) {
+  constexpr int CPR = D / 8;     // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;  // rows per load instruction (1 KB per wave)
+  constexpr int INSTS = ROWS / RPI;
+  const int cp = lane % CPR;
+#pragma unroll
+  for (int i = wave; i < INSTS; i += NW) {
+    const int r = i * RPI + lane / CPR;
+    const int j = min(row0 + r, last);
+    g2lds16(base + (int64_t)j * rs + 8 * swz<D>(r, cp), tile + i * 512);
+  }
+}
+
+// The 16-byte row chunk c (features 8c .. 8c+7) of row r of a swizzled tile.
 template <int D>
-__device__ __forceinline__ int swz_trread(int r, int c) {
-  return D == 128 ? (c ^ (4 * (r & 3))) : (c ^ (4 * ((r >> 1) & 1)));
+__device__ __forceinline__ uint4 row_chunk(const uint16_t* tile, int r, int c) {
+  return *reinterpret_cast<const uint4*>(tile + r * D + 8 * swz<D>(r, c));
 }
 
 // One MFMA A fragment of V^T for d-rows 32 * mb .. +32 and the 16 sequence rows starting at
-// `row0`, read from a row-major tile swizzled with swz_trread: slot s of lane (d, half) holds
+// `row0`, read from a row-major tile swizzled with swz: slot s of lane (d, half) holds
 // row row0 + 8 * (s / 4) + 4 * half + (s % 4).
 template <int D>
 __device__ __forceinline__ uint4 tr_frag(const uint16_t* tile, int row0, int mb, int lane) {
@@ -195,8 +223,8 @@ __device__ __forceinline__ uint4 tr_frag(const uint16_t* tile, int row0, int mb,
   const int d = 32 * mb + 16 * (g & 1) + 4 * c;  // first of the 4 features this lane addresses
   const int r1 = row0 + 4 * h + j, r2 = r1 + 8;
   const int ch = d >> 3, sub = d & 7;
-  const uint2 lo = lds_tr16(tile + r1 * D + 8 * swz_trread<D>(r1, ch) + sub);
-  const uint2 hi = lds_tr16(tile + r2 * D + 8 * swz_trread<D>(r2, ch) + sub);
+  const uint2 lo = lds_tr16(tile + r1 * D + 8 * swz<D>(r1, ch) + sub);
+  const uint2 hi = lds_tr16(tile + r2 * D + 8 * swz<D>(r2, ch) + sub);
   return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 

@@ -24,23 +24,12 @@ namespace swattn {
 constexpr int kFwdBC = 64;  // keys per tile
 
 // Streams one 64-key tile of K and of V into LDS (row-major, swizzled) with global_load_lds.
-// Rows past the valid length are clamped to the last valid row: their scores are masked, so any
-// finite data will do, and no load leaves the tensor.
 template <int D, int NW>
 __device__ __forceinline__ void fwd_issue_tile(const uint16_t* kb, const uint16_t* vb, int rs,
                                                int kt, int L, uint16_t* sK, uint16_t* sV,
                                                int wave, int lane) {
-  constexpr int CPR = D / 8;         // 16-byte chunks per row
-  constexpr int RPI = 64 / CPR;      // rows per load instruction (one 1 KB instruction per wave)
-  constexpr int INSTS = kFwdBC / RPI;
-  const int cp = lane % CPR;
-#pragma unroll
-  for (int i = wave; i < INSTS; i += NW) {
-    const int r = i * RPI + lane / CPR;
-    const int j = min(kt * kFwdBC + r, L - 1);
-    g2lds16(kb + (int64_t)j * rs + 8 * (cp ^ (r & (CPR - 1))), sK + i * 512);
-    g2lds16(vb + (int64_t)j * rs + 8 * swz_trread<D>(r, cp), sV + i * 512);
-  }
+  issue_rows<D, NW, kFwdBC>(kb, rs, kt * kFwdBC, L - 1, sK, wave, lane);
+  issue_rows<D, NW, kFwdBC>(vb, rs, kt * kFwdBC, L - 1, sV, wave, lane);
 }
 
 // Per-wave state of the forward that lives across key tiles.
@@ -80,9 +69,7 @@ __device__ __forceinline__ void fwd_step(const uint16_t* __restrict__ cur,
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int row = nb * 32 + l32;
-      const uint4 a =
-          *reinterpret_cast<const uint4*>(sK + row * D + 8 * swz_rowread<D>(row, 2 * t + half));
-      s[nb] = mfma32(a, qf[t], s[nb]);
+      s[nb] = mfma32(row_chunk<D>(sK, row, 2 * t + half), qf[t], s[nb]);
     }
   // online softmax in the log2 domain; this lane owns query qi
   float mraw = -INFINITY;
