@@ -11,8 +11,9 @@
 // dQ pass: a workgroup owns NW x 32 queries (Q, dO in registers as B fragments, lane = query as in
 // the forward), computes Delta for them first and writes it to the workspace, then walks the
 // in-window key tiles: S^T = K Q^T, dP^T = V dO^T, dS^T, and dQ^T += K^T dS^T.
-// dK/dV pass: a workgroup owns NW x 32 keys (K, V in registers, lane = key) and walks the query
-// tiles that can see them: S = Q K^T, dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS.
+// dK/dV pass: a workgroup owns 128 keys and walks the query tiles that can see them; half of its
+// waves compute S = Q K^T, P and dV^T += dO^T P, the other half dP = dO V^T, dS and dK^T += Q^T dS,
+// exchanging P through LDS (lane = key in both).
 // Both passes stream their tiles global -> LDS with global_load_lds into a two-stage ring (one
 // tile ahead, one barrier per tile) and take every transposed operand (K^T, Q^T, dO^T) straight
 // from the row-major tile with ds_read_b64_tr_b16.
@@ -105,28 +106,37 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs p) {
   const int qi = qa + l32;
   const bool qvalid = qi < T;
 
-  uint4 qf[DK], df[DK];
+  // rows past T load row T - 1 (in bounds) and are zeroed below
+  uint4 qf[DK], df[DK], of[DK];
+  const int qc = min(qi, T - 1);
+  const int64_t roff = base + (int64_t)qc * rs + 8 * half;
+#pragma unroll
+  for (int t = 0; t < DK; ++t) {
+    qf[t] = ldg16(p.q + roff + 16 * t);
+    df[t] = ldg16(p.dout + roff + 16 * t);
+    of[t] = ldg16(p.o + roff + 16 * t);
+  }
+  const float lse_raw = p.lse[(int64_t)bh * T + qc];
   float dsum = 0.f;
 #pragma unroll
   for (int t = 0; t < DK; ++t) {
-    const int64_t off = base + (int64_t)qi * rs + 16 * t + 8 * half;
-    if (qvalid) {
-      qf[t] = ldg16(p.q + off);
-      df[t] = ldg16(p.dout + off);
-      const uint4 ov = ldg16(p.o + off);
-      const uint32_t* dw = reinterpret_cast<const uint32_t*>(&df[t]);
-      const uint32_t* ow = reinterpret_cast<const uint32_t*>(&ov);
+    const uint32_t* dw = reinterpret_cast<const uint32_t*>(&df[t]);
+    const uint32_t* ow = reinterpret_cast<const uint32_t*>(&of[t]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        dsum += bf16_lo(dw[e]) * bf16_lo(ow[e]) + bf16_hi(dw[e]) * bf16_hi(ow[e]);
-    } else {
+    for (int e = 0; e < 4; ++e)
+      dsum += bf16_lo(dw[e]) * bf16_lo(ow[e]) + bf16_hi(dw[e]) * bf16_hi(ow[e]);
+  }
+  if (!qvalid) {
+#pragma unroll
+    for (int t = 0; t < DK; ++t) {
       qf[t] = make_uint4(0, 0, 0, 0);
       df[t] = make_uint4(0, 0, 0, 0);
     }
+    dsum = 0.f;
   }
   const float delta = sum_with_partner(dsum);
   if (qvalid && half == 0) p.delta[(int64_t)bh * T + qi] = delta;
-  const float lse2 = qvalid ? p.lse[(int64_t)bh * T + qi] * kLog2e : 0.f;
+  const float lse2 = qvalid ? lse_raw * kLog2e : 0.f;
 
   f32x16 dqacc[MB];
 #pragma unroll
@@ -157,11 +167,17 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs p) {
 }
 
 // ---------------------------------------------------------------------------------------- dK/dV
-// One query tile's stage: Q rows, dO rows (row-major, swizzled), then LSE and Delta of the rows.
+// Eight waves own 128 keys: waves 0-3 ("P waves") compute S = Q K^T and P for key block w and
+// accumulate dV^T += dO^T P; waves 4-7 ("dS waves") compute dP = dO V^T for the same key block and
+// accumulate dK^T += Q^T dS.  P passes from one to the other through LDS in register order (fp32),
+// so each wave carries one operand fragment set and one accumulator set -- two waves per SIMD --
+// and the MFMA work per phase is balanced: {S | dP}, barrier, {dV | dS, dK}.
+constexpr int kDkdvWaves = 8;
+
 template <int D>
 struct DkdvStage {
   static constexpr int TILE = kBwdBQ * D;
-  static constexpr int ELEMS = 2 * TILE + 2 * kBwdBQ * 2;  // in uint16 units
+  static constexpr int ELEMS = 2 * TILE + 2 * kBwdBQ * 2;  // Q | dO | LSE | Delta, uint16 units
 };
 
 template <int D, int NW>
@@ -180,76 +196,132 @@ __device__ __forceinline__ void dkdv_issue(const uint16_t* qb, const uint16_t* d
   }
 }
 
-template <int D, int NW>
-__device__ __forceinline__ void dkdv_step(const uint16_t* __restrict__ cur,
-                                          uint16_t* __restrict__ nxt, bool issue_next,
-                                          const uint16_t* qb, const uint16_t* db,
-                                          const float* lseb, const float* delb, int rs, int T,
-                                          int qt, int ka, int kj, int w, float sl2,
-                                          const uint4 (&kf)[D / 16], const uint4 (&vf)[D / 16],
-                                          f32x16 (&dkacc)[D / 32], f32x16 (&dvacc)[D / 32],
-                                          int wave, int lane) {
-  constexpr int BQ = kBwdBQ, DK = D / 16, MB = D / 32, QB = BQ / 32, TILE = DkdvStage<D>::TILE;
+// Phase 1 of one query tile.  P waves: S, P (written to sP); dS waves: dP (kept in registers).
+template <int D>
+__device__ __forceinline__ void dkdv_phase1(const uint16_t* __restrict__ cur,
+                                            float* __restrict__ sP, bool pwave, int qt, int ka,
+                                            int kj, int T, int w, float sl2,
+                                            const uint4 (&frag)[D / 16], f32x16 (&dp)[2],
+                                            int lane) {
+  constexpr int BQ = kBwdBQ, DK = D / 16, TILE = DkdvStage<D>::TILE;
   const int half = lane >> 5, l32 = lane & 31;
-  if (issue_next) dkdv_issue<D, NW>(qb, db, lseb, delb, rs, qt + 1, T, nxt, wave, lane);
-  const uint16_t* sQ = cur;
-  const uint16_t* sO = cur + TILE;
+  const uint16_t* src = pwave ? cur : cur + TILE;  // Q rows for S, dO rows for dP
   const float* sL = reinterpret_cast<const float*>(cur + 2 * TILE);
-  const float* sDl = sL + BQ;
 #pragma unroll
-  for (int qb2 = 0; qb2 < QB; ++qb2) {
+  for (int qb2 = 0; qb2 < BQ / 32; ++qb2) {
     const int qs = qt * BQ + 32 * qb2, qz = qs + 31, kz = ka + 31;
     if (ka >= T || qz < ka || qs - kz >= w || qs >= T) continue;
-    const bool need_mask = !(qs >= kz && qz - ka < w && qz < T);
-    f32x16 s = zero16(), dp = zero16();
+    f32x16 acc = zero16();
     const int row = 32 * qb2 + l32;
 #pragma unroll
-    for (int t = 0; t < DK; ++t) {
-      s = mfma32(row_chunk<D>(sQ, row, 2 * t + half), kf[t], s);
-      dp = mfma32(row_chunk<D>(sO, row, 2 * t + half), vf[t], dp);
+    for (int t = 0; t < DK; ++t) acc = mfma32(row_chunk<D>(src, row, 2 * t + half), frag[t], acc);
+    if (!pwave) {
+      dp[qb2] = acc;
+      continue;
     }
+    const bool need_mask = !(qs >= kz && qz - ka < w && qz < T);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int ql0 = 32 * qb2 + 8 * j + 4 * half;
       const float4 l4 = *reinterpret_cast<const float4*>(sL + ql0);
-      const float4 d4 = *reinterpret_cast<const float4*>(sDl + ql0);
       const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * j + i;
-        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lv[i] * kLog2e));
+        float pr = __builtin_amdgcn_exp2f(fmaf(acc[r], sl2, -lv[i] * kLog2e));
         if (need_mask) {
           const int qg = qt * BQ + ql0 + i;
           if (kj > qg || qg - kj >= w || qg >= T) pr = 0.f;
         }
-        s[r] = pr;
-        dp[r] = pr * (dp[r] - dv[i]);
+        acc[r] = pr;
       }
     }
+    float4* dst = reinterpret_cast<float4*>(sP) + qb2 * 4 * 64;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dst[j * 64 + lane] = make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]);
+  }
+}
+
+// Phase 2.  P waves: dV^T += dO^T P; dS waves: dS = P (dP - Delta), dK^T += Q^T dS.
+template <int D>
+__device__ __forceinline__ void dkdv_phase2(const uint16_t* __restrict__ cur,
+                                            const float* __restrict__ sP, bool pwave, int qt,
+                                            int ka, int T, int w, const f32x16 (&dp)[2],
+                                            f32x16 (&acc)[D / 32], int lane) {
+  constexpr int BQ = kBwdBQ, MB = D / 32, TILE = DkdvStage<D>::TILE;
+  const int half = lane >> 5;
+  const uint16_t* sQ = cur;
+  const uint16_t* sO = cur + TILE;
+  const float* sDl = reinterpret_cast<const float*>(cur + 2 * TILE) + BQ;
+#pragma unroll
+  for (int qb2 = 0; qb2 < BQ / 32; ++qb2) {
+    const int qs = qt * BQ + 32 * qb2, qz = qs + 31, kz = ka + 31;
+    if (ka >= T || qz < ka || qs - kz >= w || qs >= T) continue;
+    const float4* src = reinterpret_cast<const float4*>(sP) + qb2 * 4 * 64;
+    f32x16 x;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 v4 = src[j * 64 + lane];
+      x[4 * j] = v4.x;
+      x[4 * j + 1] = v4.y;
+      x[4 * j + 2] = v4.z;
+      x[4 * j + 3] = v4.w;
+    }
+    if (!pwave) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 d4 = *reinterpret_cast<const float4*>(sDl + 32 * qb2 + 8 * j + 4 * half);
+        x[4 * j] *= dp[qb2][4 * j] - d4.x;
+        x[4 * j + 1] *= dp[qb2][4 * j + 1] - d4.y;
+        x[4 * j + 2] *= dp[qb2][4 * j + 2] - d4.z;
+        x[4 * j + 3] *= dp[qb2][4 * j + 3] - d4.w;
+      }
+    }
+    const uint16_t* tsrc = pwave ? sO : sQ;  // dO^T for dV, Q^T for dK
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const uint4 pf = pack_frag(s, u);
-      const uint4 dsf = pack_frag(dp, u);
+      const uint4 f = pack_frag(x, u);
 #pragma unroll
-      for (int m = 0; m < MB; ++m) {
-        dvacc[m] = mfma32(tr_frag<D>(sO, 32 * qb2 + 16 * u, m, lane), pf, dvacc[m]);
-        dkacc[m] = mfma32(tr_frag<D>(sQ, 32 * qb2 + 16 * u, m, lane), dsf, dkacc[m]);
-      }
+      for (int m = 0; m < MB; ++m)
+        acc[m] = mfma32(tr_frag<D>(tsrc, 32 * qb2 + 16 * u, m, lane), f, acc[m]);
     }
   }
 }
 
+// One query tile: issue the next tile's DMA into `nxt`, phase 1, LDS hand-off of P, phase 2.  The
+// __restrict__ qualifiers state that, within one tile, the stage being read, the stage being
+// filled and the P exchange buffer are distinct, so the LDS reads need not wait for the DMA.
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs p) {
-  constexpr int BK = 32 * NW, BQ = kBwdBQ;
+__device__ __forceinline__ void dkdv_step(const uint16_t* __restrict__ cur,
+                                          uint16_t* __restrict__ nxt, float* __restrict__ sP,
+                                          bool issue_next, const uint16_t* qb, const uint16_t* db,
+                                          const float* lseb, const float* delb, int rs, int qt,
+                                          int ka, int kj, int T, int w, float sl2, bool pwave,
+                                          const uint4 (&frag)[D / 16], f32x16 (&dp)[2],
+                                          f32x16 (&acc)[D / 32], int wave, int lane) {
+  if (issue_next) dkdv_issue<D, NW>(qb, db, lseb, delb, rs, qt + 1, T, nxt, wave, lane);
+  dkdv_phase1<D>(cur, sP, pwave, qt, ka, kj, T, w, sl2, frag, dp, lane);
+  lds_barrier();  // P of this tile is in LDS
+  dkdv_phase2<D>(cur, sP, pwave, qt, ka, T, w, dp, acc, lane);
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs p) {
+  constexpr int NW = kDkdvWaves, BK = 128, BQ = kBwdBQ;
   constexpr int DK = D / 16, MB = D / 32, SE = DkdvStage<D>::ELEMS;
+  constexpr int PELEMS = 4 * BQ * 32;  // fp32 P of 4 key blocks x 64 queries
 
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * SE];
+  __shared__ __attribute__((aligned(16))) float sPall[PELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
+  const bool pwave = wave < 4;
+  const int kblk = wave & 3;
+  float* sP = sPall + kblk * BQ * 32;
+
   const int bid = blockIdx.x;
   const int kt = bid / p.BH;  // key tiles nearest the start see the most queries: first
   const int bh = bid % p.BH;
@@ -269,48 +341,45 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs p) {
 
   dkdv_issue<D, NW>(qb, db, lseb, delb, rs, qt_begin, T, smem, wave, lane);
 
-  const int ka = k0 + 32 * wave;
+  const int ka = k0 + 32 * kblk;
   const int kj = ka + l32;
   const bool kvalid = kj < T;
-  uint4 kf[DK], vf[DK];
+  // P waves hold K (B operand of S = Q K^T), dS waves hold V (B operand of dP = dO V^T)
+  const uint16_t* fsrc = pwave ? p.k : p.v;
+  uint4 frag[DK];
+  const int64_t foff = base + (int64_t)min(kj, T - 1) * rs + 8 * half;
 #pragma unroll
-  for (int t = 0; t < DK; ++t) {
-    const int64_t off = base + (int64_t)kj * rs + 16 * t + 8 * half;
-    kf[t] = kvalid ? ldg16(p.k + off) : make_uint4(0, 0, 0, 0);
-    vf[t] = kvalid ? ldg16(p.v + off) : make_uint4(0, 0, 0, 0);
-  }
-  f32x16 dkacc[MB], dvacc[MB];
+  for (int t = 0; t < DK; ++t) frag[t] = ldg16(fsrc + foff + 16 * t);
+  if (!kvalid)
 #pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    dkacc[m] = zero16();
-    dvacc[m] = zero16();
-  }
+    for (int t = 0; t < DK; ++t) frag[t] = make_uint4(0, 0, 0, 0);
+  f32x16 acc[MB];  // dV^T (P waves) or dK^T (dS waves)
+#pragma unroll
+  for (int m = 0; m < MB; ++m) acc[m] = zero16();
+  f32x16 dp[2];
 
   uint16_t* stage0 = smem;
   uint16_t* stage1 = smem + SE;
   for (int qt = qt_begin; qt <= qt_end; ++qt) {
     wait_vmcnt<0>();
-    __syncthreads();
+    __syncthreads();  // stage qt landed for all waves; previous tile's phase 2 is finished
     const bool even = ((qt - qt_begin) & 1) == 0;
-    dkdv_step<D, NW>(even ? stage0 : stage1, even ? stage1 : stage0, qt < qt_end, qb, db, lseb,
-                     delb, rs, T, qt, ka, kj, w, p.scale_log2, kf, vf, dkacc, dvacc, wave, lane);
+    dkdv_step<D, NW>(even ? stage0 : stage1, even ? stage1 : stage0, sP, qt < qt_end, qb, db,
+                     lseb, delb, rs, qt, ka, kj, T, w, p.scale_log2, pwave, frag, dp, acc, wave,
+                     lane);
   }
 
   if (!kvalid) return;
-  const float sc = p.scale;
-  uint16_t* dko = p.dk + base + (int64_t)kj * rs;
-  uint16_t* dvo = p.dv + base + (int64_t)kj * rs;
+  const float sc = pwave ? 1.f : p.scale;
+  uint16_t* out = (pwave ? p.dv : p.dk) + base + (int64_t)kj * rs;
 #pragma unroll
   for (int m = 0; m < MB; ++m)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint2 a, c;
-      a.x = pack_bf16x2(dkacc[m][4 * j + 0] * sc, dkacc[m][4 * j + 1] * sc);
-      a.y = pack_bf16x2(dkacc[m][4 * j + 2] * sc, dkacc[m][4 * j + 3] * sc);
-      c.x = pack_bf16x2(dvacc[m][4 * j + 0], dvacc[m][4 * j + 1]);
-      c.y = pack_bf16x2(dvacc[m][4 * j + 2], dvacc[m][4 * j + 3]);
-      *reinterpret_cast<uint2*>(dko + m * 32 + 8 * j + 4 * half) = a;
-      *reinterpret_cast<uint2*>(dvo + m * 32 + 8 * j + 4 * half) = c;
+      uint2 a;
+      a.x = pack_bf16x2(acc[m][4 * j + 0] * sc, acc[m][4 * j + 1] * sc);
+      a.y = pack_bf16x2(acc[m][4 * j + 2] * sc, acc[m][4 * j + 3] * sc);
+      *reinterpret_cast<uint2*>(out + m * 32 + 8 * j + 4 * half) = a;
     }
 }
 
@@ -327,11 +396,10 @@ static hipError_t launch_dq_d(const BwdArgs& a, hipStream_t s) {
 
 template <int D>
 static hipError_t launch_dkdv_d(const BwdArgs& a, hipStream_t s) {
-  constexpr int NW = 4;
   BwdArgs p = a;
-  p.n_tiles = (p.T + 32 * NW - 1) / (32 * NW);
+  p.n_tiles = (p.T + 127) / 128;  // 128 keys per workgroup
   const unsigned grid = (unsigned)p.n_tiles * (unsigned)p.BH;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW>), dim3(grid), dim3(64 * NW), 0, s, p);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(grid), dim3(64 * kDkdvWaves), 0, s, p);
   return hipGetLastError();
 }
 

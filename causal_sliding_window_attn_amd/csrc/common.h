@@ -178,6 +178,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Workgroup barrier for LDS-only hand-off between waves: waits for this wave's LDS accesses, then
+// s_barrier.  Unlike __syncthreads it carries no release fence, so it does not drain global_load_lds
+// DMA still in flight to another stage.  The "memory" clobber keeps the compiler from moving memory
+// operations across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Physical 16-byte chunk of logical chunk c in row r of a row-major [rows][D] bf16 tile.  One
 // swizzle serves both ways a tile is read:
 //   row reads (ds_read_b128, 32 consecutive rows, one chunk each): the XOR term is a bijection over

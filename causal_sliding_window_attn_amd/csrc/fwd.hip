@@ -161,10 +161,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs p) {
   const int qi = qa + l32;        // this lane's query
   const bool qvalid = qi < L;
 
-  uint4 qf[DK];
+  uint4 qf[DK];  // rows past L load row L - 1 (in bounds) and are zeroed
+  const int64_t qoff = (int64_t)min(qi, L - 1) * rs + 8 * half;
 #pragma unroll
-  for (int t = 0; t < DK; ++t)
-    qf[t] = qvalid ? ldg16(qb + (int64_t)qi * rs + 16 * t + 8 * half) : make_uint4(0, 0, 0, 0);
+  for (int t = 0; t < DK; ++t) qf[t] = ldg16(qb + qoff + 16 * t);
+  if (!qvalid)
+#pragma unroll
+    for (int t = 0; t < DK; ++t) qf[t] = make_uint4(0, 0, 0, 0);
 
   FwdState<D> S;
 #pragma unroll
