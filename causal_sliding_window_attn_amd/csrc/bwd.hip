@@ -59,7 +59,8 @@ __device__ __forceinline__ void dq_step(const uint16_t* __restrict__ cur,
       float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse2));
       if (need_mask) {
         const int key = k_lo + nb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (key > qi || qi - key >= w) pr = 0.f;
+        const bool ok = (key <= qi) & (qi - key < w);
+        pr = ok ? pr : 0.f;
       }
       s[r] = pr * (dp[r] - delta);
     }
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs p) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * TILE];  // [stage][K|V]
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int bid = blockIdx.x;
   const int qt = p.n_tiles - 1 - bid / p.BH;
@@ -231,7 +232,8 @@ __device__ __forceinline__ void dkdv_phase1(const uint16_t* __restrict__ cur,
         float pr = __builtin_amdgcn_exp2f(fmaf(acc[r], sl2, -lv[i] * kLog2e));
         if (need_mask) {
           const int qg = qt * BQ + ql0 + i;
-          if (kj > qg || qg - kj >= w || qg >= T) pr = 0.f;
+          const bool ok = (kj <= qg) & (qg - kj < w) & (qg < T);
+          pr = ok ? pr : 0.f;
         }
         acc[r] = pr;
       }
@@ -316,7 +318,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs p)
   __shared__ __attribute__((aligned(16))) float sPall[PELEMS];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const bool pwave = wave < 4;
   const int kblk = wave & 3;

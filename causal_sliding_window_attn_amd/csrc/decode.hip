@@ -7,10 +7,13 @@
 //
 // Design: decode is a matrix-vector product per (sequence, head) -- about one flop per byte of
 // cache -- so it is HBM-bound and uses VALU dot products, not MFMA.  The visible key range is
-// split into 64-key chunks; one wave per (chunk, head, sequence) issues all of its chunk's K and V
-// loads (16-byte, D/8 lanes per key row) before using any of them, reduces q.k over the row's
-// lanes with DPP, and writes the chunk's (max, sum, unnormalised output) in fp32.  A second
-// kernel merges the chunks with the log-sum-exp rule and writes O (bf16) and LSE.
+// split into 64-key chunks; a wave issues all of one chunk's K and V loads (16-byte, D/8 lanes per
+// key row) before using any of them and reduces q.k over the row's lanes with DPP.  Two schedules:
+//   many (sequence, head) pairs: one workgroup per pair, chunks dealt to its 4 waves, partial
+//   results merged in LDS (decode_fused_kernel, one launch, no workspace);
+//   few pairs (long contexts, small batch): one wave per (head, chunk, sequence) writes its chunk's
+//   (max, sum, unnormalised output) to the workspace and a second kernel merges the chunks.
+// Both merge with the log-sum-exp rule and write O (bf16) and LSE.
 #include "common.h"
 #include "launch.h"
 
@@ -44,7 +47,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecArgs p) {
   constexpr int C = kDecodeChunk;
   constexpr int NL = C / KPI;     // loads per lane per tensor
 
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;  // heads fastest: adjacent bytes
   const int L = min(max(p.lens[b], 0), p.Lcap);
   if (L == 0) return;
   const int nvis = min(p.window, L);
@@ -182,6 +185,135 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecArgs p) {
   if (p.lse && lane == 0) p.lse[bh] = (M + __log2f(Ls)) * kLn2;
 }
 
+// One workgroup of NW waves per (sequence, head): the visible key range is split into 64-key chunks
+// dealt round-robin to the waves (split-K inside the workgroup); each wave keeps a running online
+// softmax over its chunks, and the NW partial results are merged in LDS with the log-sum-exp rule.
+// Used when there are enough (sequence, head) pairs to fill the GPU; no workspace is touched.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_fused_kernel(DecArgs p) {
+  constexpr int LPK = D / 8, KPI = 64 / LPK, C = kDecodeChunk, NL = C / KPI;
+  __shared__ float s_o[NW][D];
+  __shared__ float s_ml[NW][2];
+
+  const int bh = blockIdx.x;  // consecutive workgroups: consecutive heads, adjacent bytes
+  const int b = bh / p.H, h = bh % p.H;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int L = min(max(p.lens[b], 0), p.Lcap);
+  uint16_t* ob = p.o + (int64_t)bh * D;
+  if (L == 0) {
+    for (int d = threadIdx.x; d < D; d += 64 * NW) ob[d] = 0;
+    if (p.lse && threadIdx.x == 0) p.lse[bh] = -INFINITY;
+    return;
+  }
+  const int nvis = min(p.window, L);
+  const int j0 = L - nvis;
+  const int nc = (nvis + C - 1) / C;
+
+  const int kq = lane / LPK, dc = lane % LPK;
+  const int64_t rowstride = (int64_t)p.H * D;
+  const uint16_t* kb = p.kc + ((int64_t)b * p.Lcap) * rowstride + h * D + 8 * dc;
+  const uint16_t* vb = p.vc + ((int64_t)b * p.Lcap) * rowstride + h * D + 8 * dc;
+  float qv[8];
+  {
+    const uint4 qq = ldg16(p.q + (int64_t)bh * D + 8 * dc);
+    const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qq);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qv[2 * e] = bf16_lo(qw[e]) * p.scale_log2;
+      qv[2 * e + 1] = bf16_hi(qw[e]) * p.scale_log2;
+    }
+  }
+  float m_run = -INFINITY, l_run = 0.f;  // l_run: this lane's key rows only
+  float ov[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ov[e] = 0.f;
+
+  for (int c = wave; c < nc; c += NW) {
+    const int cs = j0 + c * C;
+    const int ce = min(cs + C, L);
+    uint4 kr[NL], vr[NL];
+#pragma unroll
+    for (int r = 0; r < NL; ++r) {
+      const int j = min(cs + r * KPI + kq, ce - 1);  // rows past the chunk re-read a valid row
+      kr[r] = ldg16(kb + j * rowstride);
+      vr[r] = ldg16(vb + j * rowstride);
+    }
+    float sc[NL];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < NL; ++r) {
+      const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kr[r]);
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = fmaf(qv[2 * e], bf16_lo(kw[e]), acc);
+        acc = fmaf(qv[2 * e + 1], bf16_hi(kw[e]), acc);
+      }
+      acc = group_sum<LPK>(acc);
+      sc[r] = (cs + r * KPI + kq < ce) ? acc : -INFINITY;
+      mx = fmaxf(mx, sc[r]);
+    }
+#pragma unroll
+    for (int off = LPK; off < 32; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    mx = max_with_partner(mx);
+    const float m_new = fmaxf(m_run, mx);  // finite: every chunk holds a visible key
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ov[e] *= alpha;
+    m_run = m_new;
+#pragma unroll
+    for (int r = 0; r < NL; ++r) {
+      const float pr = __builtin_amdgcn_exp2f(sc[r] - m_new);
+      l_run += pr;
+      const uint32_t* vw = reinterpret_cast<const uint32_t*>(&vr[r]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ov[2 * e] = fmaf(pr, bf16_lo(vw[e]), ov[2 * e]);
+        ov[2 * e + 1] = fmaf(pr, bf16_hi(vw[e]), ov[2 * e + 1]);
+      }
+    }
+  }
+  // this wave's partial: sum over the key-row groups (lanes with equal dc)
+#pragma unroll
+  for (int off = LPK; off < 32; off <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ov[e] += __shfl_xor(ov[e], off);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ov[e] = sum_with_partner(ov[e]);
+  float lsum = (dc == 0) ? l_run : 0.f;
+  for (int off = 1; off < 32; off <<= 1) lsum += __shfl_xor(lsum, off);
+  lsum = sum_with_partner(lsum);
+  if (kq == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_o[wave][8 * dc + e] = ov[e];
+  }
+  if (lane == 0) {
+    s_ml[wave][0] = m_run;  // -inf for a wave that got no chunk
+    s_ml[wave][1] = lsum;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, s_ml[w][0]);
+  float wt[NW], Ls = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    wt[w] = (s_ml[w][0] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s_ml[w][0] - M);
+    Ls = fmaf(s_ml[w][1], wt[w], Ls);
+  }
+  const float inv = 1.f / Ls;
+  for (int d = lane; d < D; d += 64) {
+    float a = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) a = fmaf(s_o[w][d], wt[w], a);
+    ob[d] = __builtin_bit_cast(uint16_t, (__bf16)(a * inv));
+  }
+  if (p.lse && lane == 0) p.lse[bh] = (M + __log2f(Ls)) * kLn2;
+}
+
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs p) {
   const int chunks = p.D / 8;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -199,9 +331,13 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs p) {
 
 template <int D>
 static hipError_t launch_decode_d(const DecArgs& a, hipStream_t s) {
+  if (decode_uses_fused(a.B, a.H)) {
+    hipLaunchKernelGGL((decode_fused_kernel<D, 4>), dim3(a.B * a.H), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const int vis_max = a.window < a.Lcap ? a.window : a.Lcap;
   const int nc = (vis_max + kDecodeChunk - 1) / kDecodeChunk;
-  hipLaunchKernelGGL((decode_split_kernel<D>), dim3(nc, a.H, a.B), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((decode_split_kernel<D>), dim3(a.H, nc, a.B), dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.H), dim3(64), 0, s, a);

@@ -79,7 +79,8 @@ __device__ __forceinline__ void fwd_step(const uint16_t* __restrict__ cur,
     for (int r = 0; r < 16; ++r) {
       if (need_mask) {
         const int key = k_lo + nb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (key > qi || qi - key >= w) s[nb][r] = -INFINITY;
+        const bool ok = (key <= qi) & (qi - key < w);
+        s[nb][r] = ok ? s[nb][r] : -INFINITY;
       }
       mraw = fmaxf(mraw, s[nb][r]);
     }
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs p) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * TILE];  // [stage][K|V]
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
 
   const int bid = blockIdx.x;
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs p) {
   float* og = reinterpret_cast<float*>(p.o);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int bid = blockIdx.x;
   const int qt = p.n_qtiles - 1 - bid / p.BH;

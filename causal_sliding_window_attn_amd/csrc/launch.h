@@ -68,6 +68,10 @@ struct AppendArgs {
 
 constexpr int kDecodeChunk = 64;  // keys per split of the decode
 
+// Decode schedule: one workgroup per (sequence, head) when the pairs alone fill the GPU's CUs
+// several times over, else split each pair's keys across workgroups and merge in a second kernel.
+inline bool decode_uses_fused(int B, int H) { return (long long)B * H >= 512; }
+
 hipError_t launch_fwd(const FwdArgs& a, bool f32, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t s);
