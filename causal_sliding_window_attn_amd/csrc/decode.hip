@@ -332,7 +332,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs p) {
 template <int D>
 static hipError_t launch_decode_d(const DecArgs& a, hipStream_t s) {
   if (decode_uses_fused(a.B, a.H)) {
-    hipLaunchKernelGGL((decode_fused_kernel<D, 4>), dim3(a.B * a.H), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_fused_kernel<D, 8>), dim3(a.B * a.H), dim3(512), 0, s, a);
     return hipGetLastError();
   }
   const int vis_max = a.window < a.Lcap ? a.window : a.Lcap;
