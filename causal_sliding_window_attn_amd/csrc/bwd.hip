@@ -32,8 +32,8 @@ __device__ __forceinline__ void dq_step(const uint16_t* __restrict__ cur,
                                         const uint16_t* kb, const uint16_t* vb, int rs, int T,
                                         int kt, int qa, int qi, int w, float sl2, float lse2,
                                         float delta, const uint4 (&qf)[D / 16],
-                                        const uint4 (&df)[D / 16], f32x16 (&dqacc)[D / 32],
-                                        int wave, int lane) {
+                                        const uint4 (&df)[D / 16], const LdsOffsets<D>& lo,
+                                        f32x16 (&dqacc)[D / 32], int wave, int lane) {
   constexpr int BC = kBwdBC, DK = D / 16, MB = D / 32, NB = BC / 32, TILE = BC * D;
   const int half = lane >> 5, l32 = lane & 31;
   if (issue_next) {
@@ -48,11 +48,10 @@ __device__ __forceinline__ void dq_step(const uint16_t* __restrict__ cur,
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     f32x16 s = zero16(), dp = zero16();
-    const int row = nb * 32 + l32;
 #pragma unroll
     for (int t = 0; t < DK; ++t) {
-      s = mfma32(row_chunk<D>(sK, row, 2 * t + half), qf[t], s);
-      dp = mfma32(row_chunk<D>(sV, row, 2 * t + half), df[t], dp);
+      s = mfma32(rc_frag<D>(sK, lo, nb, t), qf[t], s);
+      dp = mfma32(rc_frag<D>(sV, lo, nb, t), df[t], dp);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -69,7 +68,7 @@ __device__ __forceinline__ void dq_step(const uint16_t* __restrict__ cur,
       const uint4 dsf = pack_frag(s, u);
 #pragma unroll
       for (int m = 0; m < MB; ++m)
-        dqacc[m] = mfma32(tr_frag<D>(sK, nb * 32 + 16 * u, m, lane), dsf, dqacc[m]);
+        dqacc[m] = mfma32(tr_frag_o<D>(sK, lo, nb * 32 + 16 * u, m), dsf, dqacc[m]);
     }
   }
 }
@@ -143,6 +142,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs p) {
 #pragma unroll
   for (int m = 0; m < MB; ++m) dqacc[m] = zero16();
 
+  const LdsOffsets<D> lo(lane);
   uint16_t* stage0 = smem;
   uint16_t* stage1 = smem + 2 * TILE;
   for (int kt = kt_begin; kt <= kt_end; ++kt) {
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs p) {
     __syncthreads();
     const bool even = ((kt - kt_begin) & 1) == 0;
     dq_step<D, NW>(even ? stage0 : stage1, even ? stage1 : stage0, kt < kt_end, kb, vb, rs, T, kt,
-                   qa, qi, w, p.scale_log2, lse2, delta, qf, df, dqacc, wave, lane);
+                   qa, qi, w, p.scale_log2, lse2, delta, qf, df, lo, dqacc, wave, lane);
   }
 
   if (!qvalid) return;
@@ -203,7 +203,7 @@ __device__ __forceinline__ void dkdv_phase1(const uint16_t* __restrict__ cur,
                                             float* __restrict__ sP, bool pwave, int qt, int ka,
                                             int kj, int T, int w, float sl2,
                                             const uint4 (&frag)[D / 16], f32x16 (&dp)[2],
-                                            int lane) {
+                                            const LdsOffsets<D>& lo, int lane) {
   constexpr int BQ = kBwdBQ, DK = D / 16, TILE = DkdvStage<D>::TILE;
   const int half = lane >> 5, l32 = lane & 31;
   const uint16_t* src = pwave ? cur : cur + TILE;  // Q rows for S, dO rows for dP
@@ -213,9 +213,8 @@ __device__ __forceinline__ void dkdv_phase1(const uint16_t* __restrict__ cur,
     const int qs = qt * BQ + 32 * qb2, qz = qs + 31, kz = ka + 31;
     if (ka >= T || qz < ka || qs - kz >= w || qs >= T) continue;
     f32x16 acc = zero16();
-    const int row = 32 * qb2 + l32;
 #pragma unroll
-    for (int t = 0; t < DK; ++t) acc = mfma32(row_chunk<D>(src, row, 2 * t + half), frag[t], acc);
+    for (int t = 0; t < DK; ++t) acc = mfma32(rc_frag<D>(src, lo, qb2, t), frag[t], acc);
     if (!pwave) {
       dp[qb2] = acc;
       continue;
@@ -250,7 +249,8 @@ template <int D>
 __device__ __forceinline__ void dkdv_phase2(const uint16_t* __restrict__ cur,
                                             const float* __restrict__ sP, bool pwave, int qt,
                                             int ka, int T, int w, const f32x16 (&dp)[2],
-                                            f32x16 (&acc)[D / 32], int lane) {
+                                            f32x16 (&acc)[D / 32], const LdsOffsets<D>& lo,
+                                            int lane) {
   constexpr int BQ = kBwdBQ, MB = D / 32, TILE = DkdvStage<D>::TILE;
   const int half = lane >> 5;
   const uint16_t* sQ = cur;
@@ -286,7 +286,7 @@ __device__ __forceinline__ void dkdv_phase2(const uint16_t* __restrict__ cur,
       const uint4 f = pack_frag(x, u);
 #pragma unroll
       for (int m = 0; m < MB; ++m)
-        acc[m] = mfma32(tr_frag<D>(tsrc, 32 * qb2 + 16 * u, m, lane), f, acc[m]);
+        acc[m] = mfma32(tr_frag_o<D>(tsrc, lo, 32 * qb2 + 16 * u, m), f, acc[m]);
     }
   }
 }
@@ -301,11 +301,12 @@ __device__ __forceinline__ void dkdv_step(const uint16_t* __restrict__ cur,
                                           const float* lseb, const float* delb, int rs, int qt,
                                           int ka, int kj, int T, int w, float sl2, bool pwave,
                                           const uint4 (&frag)[D / 16], f32x16 (&dp)[2],
-                                          f32x16 (&acc)[D / 32], int wave, int lane) {
+                                          f32x16 (&acc)[D / 32], const LdsOffsets<D>& lo,
+                                          int wave, int lane) {
   if (issue_next) dkdv_issue<D, NW>(qb, db, lseb, delb, rs, qt + 1, T, nxt, wave, lane);
-  dkdv_phase1<D>(cur, sP, pwave, qt, ka, kj, T, w, sl2, frag, dp, lane);
+  dkdv_phase1<D>(cur, sP, pwave, qt, ka, kj, T, w, sl2, frag, dp, lo, lane);
   lds_barrier();  // P of this tile is in LDS
-  dkdv_phase2<D>(cur, sP, pwave, qt, ka, T, w, dp, acc, lane);
+  dkdv_phase2<D>(cur, sP, pwave, qt, ka, T, w, dp, acc, lo, lane);
 }
 
 template <int D>
@@ -360,6 +361,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs p)
   for (int m = 0; m < MB; ++m) acc[m] = zero16();
   f32x16 dp[2];
 
+  const LdsOffsets<D> lo(lane);
   uint16_t* stage0 = smem;
   uint16_t* stage1 = smem + SE;
   for (int qt = qt_begin; qt <= qt_end; ++qt) {
@@ -367,8 +369,8 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs p)
     __syncthreads();  // stage qt landed for all waves; previous tile's phase 2 is finished
     const bool even = ((qt - qt_begin) & 1) == 0;
     dkdv_step<D, NW>(even ? stage0 : stage1, even ? stage1 : stage0, sP, qt < qt_end, qb, db,
-                     lseb, delb, rs, qt, ka, kj, T, w, p.scale_log2, pwave, frag, dp, acc, wave,
-                     lane);
+                     lseb, delb, rs, qt, ka, kj, T, w, p.scale_log2, pwave, frag, dp, acc, lo,
+                     wave, lane);
   }
 
   if (!kvalid) return;

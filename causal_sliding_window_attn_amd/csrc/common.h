@@ -236,4 +236,46 @@ __device__ __forceinline__ uint4 tr_frag(const uint16_t* tile, int row0, int mb,
   return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
+
+// Per-lane LDS element offsets for the two fragment reads, precomputed once per kernel.  With the
+// swizzle above, a fragment's address is (tile base) + (per-lane term that depends only on the
+// k-step t or the 32-row block mb) + (a compile-time row offset), so every read in the loop is one
+// VGPR plus an immediate:
+//   rc[t]:    row_chunk of row (l % 32) and chunk (2t + half), for a block whose first row is a
+//             multiple of 32 -- add 32 * D * (block) as a constant;
+//   tr[mb][e]: the two 8-byte transposed reads of tr_frag for row0 = 0 -- add row0 * D (row0 a
+//             multiple of 16) as a constant.
+template <int D>
+struct LdsOffsets {
+  int rc[D / 16];
+  int tr[D / 32][2];
+  __device__ __forceinline__ explicit LdsOffsets(int lane) {
+    const int l32 = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) rc[t] = l32 * D + 8 * swz<D>(l32, 2 * t + half);
+    const int g = lane >> 4, j = (lane >> 2) & 3, c = lane & 3, h = g >> 1;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) {
+      const int d = 32 * mb + 16 * (g & 1) + 4 * c;
+      const int r1 = 4 * h + j, r2 = r1 + 8;
+      tr[mb][0] = r1 * D + 8 * swz<D>(r1, d >> 3) + (d & 7);
+      tr[mb][1] = r2 * D + 8 * swz<D>(r2, d >> 3) + (d & 7);
+    }
+  }
+};
+
+template <int D>
+__device__ __forceinline__ uint4 rc_frag(const uint16_t* tile, const LdsOffsets<D>& o, int blk32,
+                                         int t) {
+  return *reinterpret_cast<const uint4*>(tile + blk32 * 32 * D + o.rc[t]);
+}
+
+template <int D>
+__device__ __forceinline__ uint4 tr_frag_o(const uint16_t* tile, const LdsOffsets<D>& o, int row0,
+                                           int mb) {
+  const uint2 lo = lds_tr16(tile + row0 * D + o.tr[mb][0]);
+  const uint2 hi = lds_tr16(tile + row0 * D + o.tr[mb][1]);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
 }  // namespace swattn

@@ -47,8 +47,8 @@ __device__ __forceinline__ void fwd_step(const uint16_t* __restrict__ cur,
                                          uint16_t* __restrict__ nxt, bool issue_next, int kt_next,
                                          const uint16_t* kb, const uint16_t* vb, int rs, int L,
                                          int kt, int qa, int qi, int w, float sl2,
-                                         const uint4 (&qf)[D / 16], FwdState<D>& S, int wave,
-                                         int lane) {
+                                         const uint4 (&qf)[D / 16], const LdsOffsets<D>& lo,
+                                         FwdState<D>& S, int wave, int lane) {
   constexpr int BC = kFwdBC, DK = D / 16, MB = D / 32, NB = BC / 32, TILE = BC * D;
   constexpr float kRescale = 8.f;  // lazy rescaling threshold (log2 units)
   const int half = lane >> 5, l32 = lane & 31;
@@ -67,10 +67,7 @@ __device__ __forceinline__ void fwd_step(const uint16_t* __restrict__ cur,
 #pragma unroll
   for (int t = 0; t < DK; ++t)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int row = nb * 32 + l32;
-      s[nb] = mfma32(row_chunk<D>(sK, row, 2 * t + half), qf[t], s[nb]);
-    }
+    for (int nb = 0; nb < NB; ++nb) s[nb] = mfma32(rc_frag<D>(sK, lo, nb, t), qf[t], s[nb]);
   // online softmax in the log2 domain; this lane owns query qi
   float mraw = -INFINITY;
 #pragma unroll
@@ -118,7 +115,7 @@ __device__ __forceinline__ void fwd_step(const uint16_t* __restrict__ cur,
       pack_frag_split(s[nb], u, ph, pl);
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
-        const uint4 a = tr_frag<D>(sV, nb * 32 + 16 * u, m, lane);
+        const uint4 a = tr_frag_o<D>(sV, lo, nb * 32 + 16 * u, m);
         S.oacc[m] = mfma32(a, ph, S.oacc[m]);
         S.oacc[m] = mfma32(a, pl, S.oacc[m]);
       }
@@ -176,6 +173,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs p) {
   S.m_use = -INFINITY;
   S.l_run = 0.f;
 
+  const LdsOffsets<D> lo(lane);
   fwd_issue_tile<D, NW>(kb, vb, rs, kt_begin, L, smem, smem + TILE, wave, lane);
   uint16_t* stage0 = smem;
   uint16_t* stage1 = smem + 2 * TILE;
@@ -184,7 +182,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs p) {
     __syncthreads();  // ... for every wave, and every wave is done with the other stage
     const bool even = ((kt - kt_begin) & 1) == 0;
     fwd_step<D, NW>(even ? stage0 : stage1, even ? stage1 : stage0, kt < kt_end, kt + 1, kb, vb,
-                    rs, L, kt, qa, qi, w, p.scale_log2, qf, S, wave, lane);
+                    rs, L, kt, qa, qi, w, p.scale_log2, qf, lo, S, wave, lane);
   }
 
   const float l_tot = sum_with_partner(S.l_run);
