@@ -26,26 +26,16 @@ constexpr int kBwdBC = 64;  // keys per tile in the dQ pass
 constexpr int kBwdBQ = 64;  // queries per tile in the dK/dV pass
 
 // ------------------------------------------------------------------------------------------ dQ
-template <int D, int NW>
-__device__ __forceinline__ void dq_step(const uint16_t* __restrict__ cur,
-                                        uint16_t* __restrict__ nxt, bool issue_next,
-                                        const uint16_t* kb, const uint16_t* vb, int rs, int T,
-                                        int kt, int qa, int qi, int w, float sl2, float lse2,
-                                        float delta, const uint4 (&qf)[D / 16],
-                                        const uint4 (&df)[D / 16], const LdsOffsets<D>& lo,
-                                        f32x16 (&dqacc)[D / 32], int wave, int lane) {
-  constexpr int BC = kBwdBC, DK = D / 16, MB = D / 32, NB = BC / 32, TILE = BC * D;
-  const int half = lane >> 5, l32 = lane & 31;
-  if (issue_next) {
-    issue_rows<D, NW, BC>(kb, rs, (kt + 1) * BC, T - 1, nxt, wave, lane);
-    issue_rows<D, NW, BC>(vb, rs, (kt + 1) * BC, T - 1, nxt + TILE, wave, lane);
-  }
-  const uint16_t* sK = cur;
-  const uint16_t* sV = cur + TILE;
-  const int k_lo = kt * BC, k_hi = k_lo + BC - 1, qz = qa + 31;
-  if ((qa >= T) || (k_lo > qz) || (qa - k_hi >= w)) return;
-  const bool need_mask = !(k_hi <= qa && qz - k_lo < w);
-#pragma unroll
+template <int D, bool MASK>
+__device__ __forceinline__ void dq_tile(const uint16_t* __restrict__ sK,
+                                        const uint16_t* __restrict__ sV, int k_lo, int qi, int w,
+                                        float sl2, float lse2, float delta,
+                                        const uint4 (&qf)[D / 16], const uint4 (&df)[D / 16],
+                                        const LdsOffsets<D>& lo, f32x16 (&dqacc)[D / 32],
+                                        int lane) {
+  constexpr int BC = kBwdBC, DK = D / 16, MB = D / 32, NB = BC / 32;
+  const int half = lane >> 5;
+#pragma unroll 1
   for (int nb = 0; nb < NB; ++nb) {
     f32x16 s = zero16(), dp = zero16();
 #pragma unroll
@@ -53,13 +43,14 @@ __device__ __forceinline__ void dq_step(const uint16_t* __restrict__ cur,
       s = mfma32(rc_frag<D>(sK, lo, nb, t), qf[t], s);
       dp = mfma32(rc_frag<D>(sV, lo, nb, t), df[t], dp);
     }
+    // key j is visible to query i iff (unsigned)(i - j) < w
+    const int d0 = qi - (k_lo + nb * 32) - 4 * half;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse2));
-      if (need_mask) {
-        const int key = k_lo + nb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const bool ok = (key <= qi) & (qi - key < w);
-        pr = ok ? pr : 0.f;
+      if (MASK) {
+        const unsigned dist = (unsigned)(d0 - (8 * (r >> 2) + (r & 3)));
+        pr = dist < (unsigned)w ? pr : 0.f;
       }
       s[r] = pr * (dp[r] - delta);
     }
@@ -71,6 +62,27 @@ __device__ __forceinline__ void dq_step(const uint16_t* __restrict__ cur,
         dqacc[m] = mfma32(tr_frag_o<D>(sK, lo, nb * 32 + 16 * u, m), dsf, dqacc[m]);
     }
   }
+}
+
+template <int D, int NW>
+__device__ __forceinline__ void dq_step(const uint16_t* __restrict__ cur,
+                                        uint16_t* __restrict__ nxt, bool issue_next,
+                                        const uint16_t* kb, const uint16_t* vb, int rs, int T,
+                                        int kt, int qa, int qi, int w, float sl2, float lse2,
+                                        float delta, const uint4 (&qf)[D / 16],
+                                        const uint4 (&df)[D / 16], const LdsOffsets<D>& lo,
+                                        f32x16 (&dqacc)[D / 32], int wave, int lane) {
+  constexpr int BC = kBwdBC, TILE = BC * D;
+  if (issue_next) {
+    issue_rows<D, NW, BC>(kb, rs, (kt + 1) * BC, T - 1, nxt, wave, lane);
+    issue_rows<D, NW, BC>(vb, rs, (kt + 1) * BC, T - 1, nxt + TILE, wave, lane);
+  }
+  const int k_lo = kt * BC, k_hi = k_lo + BC - 1, qz = qa + 31;
+  if ((qa >= T) || (k_lo > qz) || (qa - k_hi >= w)) return;
+  if (k_hi <= qa && qz - k_lo < w)
+    dq_tile<D, false>(cur, cur + TILE, k_lo, qi, w, sl2, lse2, delta, qf, df, lo, dqacc, lane);
+  else
+    dq_tile<D, true>(cur, cur + TILE, k_lo, qi, w, sl2, lse2, delta, qf, df, lo, dqacc, lane);
 }
 
 template <int D, int NW>
@@ -197,6 +209,30 @@ __device__ __forceinline__ void dkdv_issue(const uint16_t* qb, const uint16_t* d
   }
 }
 
+// P = exp2(S * scale - LSE) for one 32-query block (lane = key kj, accumulator r = query row).
+template <bool MASK>
+__device__ __forceinline__ void dkdv_probs(f32x16& acc, const float* sL, int qb2, int qt, int kj,
+                                           int T, int w, float sl2, int half) {
+  constexpr int BQ = kBwdBQ;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ql0 = 32 * qb2 + 8 * j + 4 * half;
+    const float4 l4 = *reinterpret_cast<const float4*>(sL + ql0);
+    const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * j + i;
+      float pr = __builtin_amdgcn_exp2f(fmaf(acc[r], sl2, -lv[i] * kLog2e));
+      if (MASK) {
+        // query i sees key j iff (unsigned)(i - j) < w; rows past T hold a clamped copy: drop them
+        const int qg = qt * BQ + ql0 + i;
+        pr = ((unsigned)(qg - kj) < (unsigned)w) & (qg < T) ? pr : 0.f;
+      }
+      acc[r] = pr;
+    }
+  }
+}
+
 // Phase 1 of one query tile.  P waves: S, P (written to sP); dS waves: dP (kept in registers).
 template <int D>
 __device__ __forceinline__ void dkdv_phase1(const uint16_t* __restrict__ cur,
@@ -219,24 +255,10 @@ __device__ __forceinline__ void dkdv_phase1(const uint16_t* __restrict__ cur,
       dp[qb2] = acc;
       continue;
     }
-    const bool need_mask = !(qs >= kz && qz - ka < w && qz < T);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ql0 = 32 * qb2 + 8 * j + 4 * half;
-      const float4 l4 = *reinterpret_cast<const float4*>(sL + ql0);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * j + i;
-        float pr = __builtin_amdgcn_exp2f(fmaf(acc[r], sl2, -lv[i] * kLog2e));
-        if (need_mask) {
-          const int qg = qt * BQ + ql0 + i;
-          const bool ok = (kj <= qg) & (qg - kj < w) & (qg < T);
-          pr = ok ? pr : 0.f;
-        }
-        acc[r] = pr;
-      }
-    }
+    if (qs >= kz && qz - ka < w && qz < T)
+      dkdv_probs<false>(acc, sL, qb2, qt, kj, T, w, sl2, half);
+    else
+      dkdv_probs<true>(acc, sL, qb2, qt, kj, T, w, sl2, half);
     float4* dst = reinterpret_cast<float4*>(sP) + qb2 * 4 * 64;
 #pragma unroll
     for (int j = 0; j < 4; ++j)

@@ -22,6 +22,12 @@
 namespace swattn {
 
 constexpr int kFwdBC = 64;  // keys per tile
+#ifndef FWD_NW
+#define FWD_NW 4  // waves (x 32 queries) per workgroup
+#endif
+#ifndef FWD_NS
+#define FWD_NS 2  // K/V ring stages
+#endif
 
 // Streams one 64-key tile of K and of V into LDS (row-major, swizzled) with global_load_lds.
 template <int D, int NW>
@@ -39,48 +45,26 @@ struct FwdState {
   float m_use, l_run;
 };
 
-// One key tile: issue the DMA of the next tile into `nxt`, then consume `cur`.  Within one call the
-// two stages are distinct buffers, which the __restrict__ qualifiers state; that lets the compiler
-// see that the LDS reads of `cur` do not depend on the DMA writes to `nxt` still in flight.
-template <int D, int NW>
-__device__ __forceinline__ void fwd_step(const uint16_t* __restrict__ cur,
-                                         uint16_t* __restrict__ nxt, bool issue_next, int kt_next,
-                                         const uint16_t* kb, const uint16_t* vb, int rs, int L,
-                                         int kt, int qa, int qi, int w, float sl2,
-                                         const uint4 (&qf)[D / 16], const LdsOffsets<D>& lo,
-                                         FwdState<D>& S, int wave, int lane) {
-  constexpr int BC = kFwdBC, DK = D / 16, MB = D / 32, NB = BC / 32, TILE = BC * D;
+// Softmax bookkeeping of one key tile held in two 32-key S^T accumulator blocks: mask (boundary
+// tiles only), row max over the whole tile, and the lazy rescale of O -- all before any of the
+// tile's probabilities reach O.
+template <int D, bool MASK>
+__device__ __forceinline__ void fwd_tile_max(f32x16& s0, f32x16& s1, int k_lo, int qi, int w,
+                                             int half, float sl2, FwdState<D>& S) {
+  constexpr int MB = D / 32;
   constexpr float kRescale = 8.f;  // lazy rescaling threshold (log2 units)
-  const int half = lane >> 5, l32 = lane & 31;
-  if (issue_next) fwd_issue_tile<D, NW>(kb, vb, rs, kt_next, L, nxt, nxt + TILE, wave, lane);
-
-  const uint16_t* sK = cur;
-  const uint16_t* sV = cur + TILE;
-  const int k_lo = kt * BC, k_hi = k_lo + BC - 1;
-  const int qz = qa + 31;
-  if ((qa >= L) || (k_lo > qz) || (qa - k_hi >= w)) return;
-  const bool need_mask = !(k_hi <= qa && qz - k_lo < w);
-  // S^T (keys x queries) for the tile
-  f32x16 s[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) s[nb] = zero16();
-#pragma unroll
-  for (int t = 0; t < DK; ++t)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) s[nb] = mfma32(rc_frag<D>(sK, lo, nb, t), qf[t], s[nb]);
-  // online softmax in the log2 domain; this lane owns query qi
   float mraw = -INFINITY;
+  // key j is visible to query i iff 0 <= i - j < w, i.e. (unsigned)(i - j) < w
+  const int d0 = qi - k_lo - 4 * half;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (need_mask) {
-        const int key = k_lo + nb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const bool ok = (key <= qi) & (qi - key < w);
-        s[nb][r] = ok ? s[nb][r] : -INFINITY;
-      }
-      mraw = fmaxf(mraw, s[nb][r]);
+  for (int r = 0; r < 16; ++r) {
+    if (MASK) {
+      const int off = 8 * (r >> 2) + (r & 3);
+      s0[r] = (unsigned)(d0 - off) < (unsigned)w ? s0[r] : -INFINITY;
+      s1[r] = (unsigned)(d0 - 32 - off) < (unsigned)w ? s1[r] : -INFINITY;
     }
+    mraw = fmaxf(mraw, fmaxf(s0[r], s1[r]));
+  }
   const float m_tile = max_with_partner(mraw) * sl2;
   // rescale O only when some row max has grown past the threshold (exact either way)
   if (__builtin_amdgcn_ballot_w64(m_tile > S.m_use + kRescale) != 0) {
@@ -94,43 +78,107 @@ __device__ __forceinline__ void fwd_step(const uint16_t* __restrict__ cur,
       for (int r = 0; r < 16; ++r) S.oacc[m][r] *= alpha;
     S.m_use = m_new;
   }
+}
+
+template <int D>
+__device__ __forceinline__ void fwd_block_exp(f32x16& s, float sl2, FwdState<D>& S, uint4 (&ph)[2],
+                                              uint4 (&pl)[2]) {
   const float m_eff = (S.m_use == -INFINITY) ? 0.f : S.m_use;
   float lsum = 0.f;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float e = __builtin_amdgcn_exp2f(fmaf(s[nb][r], sl2, -m_eff));
-      s[nb][r] = e;
-      lsum += e;
-    }
+  for (int r = 0; r < 16; ++r) {
+    const float e = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -m_eff));
+    s[r] = e;
+    lsum += e;
+  }
   S.l_run += lsum;
-  // O^T += V^T P^T with P carried as bf16 hi + lo (the output is stored in bf16, whose rounding
-  // alone costs up to half an ulp, so P must not add 2^-9 relative on top)
+  // P as bf16 hi + lo: the output is stored in bf16, whose rounding alone costs up to half an
+  // ulp, so P must not add 2^-9 relative on top
+  pack_frag_split(s, 0, ph[0], pl[0]);
+  pack_frag_split(s, 1, ph[1], pl[1]);
+}
+
+// O^T += V^T P^T for one 32-key block.
+template <int D>
+__device__ __forceinline__ void fwd_block_pv(const uint16_t* sV, const LdsOffsets<D>& lo, int nb,
+                                             const uint4 (&ph)[2], const uint4 (&pl)[2],
+                                             FwdState<D>& S) {
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      uint4 ph, pl;
-      pack_frag_split(s[nb], u, ph, pl);
-#pragma unroll
-      for (int m = 0; m < MB; ++m) {
-        const uint4 a = tr_frag_o<D>(sV, lo, nb * 32 + 16 * u, m);
-        S.oacc[m] = mfma32(a, ph, S.oacc[m]);
-        S.oacc[m] = mfma32(a, pl, S.oacc[m]);
-      }
+    for (int m = 0; m < D / 32; ++m) {
+      const uint4 a = tr_frag_o<D>(sV, lo, nb * 32 + 16 * u, m);
+      S.oacc[m] = mfma32(a, ph[u], S.oacc[m]);
+      S.oacc[m] = mfma32(a, pl[u], S.oacc[m]);
     }
 }
 
+// The compute of one key tile: S^T for both 32-key blocks, the tile's softmax bookkeeping, then
+// block 0's PV MFMAs run under block 1's exponentials (interleave pinned with
+// sched_group_barrier) before block 1's PV.
+template <int D, bool MASK>
+__device__ __forceinline__ void fwd_tile(const uint16_t* __restrict__ sK,
+                                         const uint16_t* __restrict__ sV, int k_lo, int qi, int w,
+                                         float sl2, const uint4 (&qf)[D / 16],
+                                         const LdsOffsets<D>& lo, FwdState<D>& S, int lane) {
+  constexpr int DK = D / 16;
+  const int half = lane >> 5;
+  f32x16 s0 = zero16(), s1 = zero16();
+#pragma unroll
+  for (int t = 0; t < DK; ++t) {
+    s0 = mfma32(rc_frag<D>(sK, lo, 0, t), qf[t], s0);
+    s1 = mfma32(rc_frag<D>(sK, lo, 1, t), qf[t], s1);
+  }
+  fwd_tile_max<D, MASK>(s0, s1, k_lo, qi, w, half, sl2, S);
+  uint4 ph0[2], pl0[2], ph1[2], pl1[2];
+  fwd_block_exp<D>(s0, sl2, S, ph0, pl0);
+  // { PV of block 0 } || { exponentials and packing of block 1 }
+  fwd_block_pv<D>(sV, lo, 0, ph0, pl0, S);
+  fwd_block_exp<D>(s1, sl2, S, ph1, pl1);
+#pragma unroll
+  for (int t = 0; t < 2 * D / 32; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read (transposed pair)
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA hi, lo
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+  }
+  fwd_block_pv<D>(sV, lo, 1, ph1, pl1, S);
+}
+
+// One key tile: issue the DMA of the next tile into `nxt`, then consume `cur`.  Within one call the
+// two stages are distinct buffers, which the __restrict__ qualifiers state; that lets the compiler
+// see that the LDS reads of `cur` do not depend on the DMA writes to `nxt` still in flight.  Tiles
+// crossing the diagonal or the window edge take the masked instantiation (a wave-uniform branch).
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs p) {
+__device__ __forceinline__ void fwd_step(const uint16_t* __restrict__ cur,
+                                         uint16_t* __restrict__ nxt, bool issue_next, int kt_next,
+                                         const uint16_t* kb, const uint16_t* vb, int rs, int L,
+                                         int kt, int qa, int qi, int w, float sl2,
+                                         const uint4 (&qf)[D / 16], const LdsOffsets<D>& lo,
+                                         FwdState<D>& S, int wave, int lane) {
+  constexpr int BC = kFwdBC, TILE = BC * D;
+  static_assert(BC == 64, "two 32-key blocks per tile");
+  if (issue_next) fwd_issue_tile<D, NW>(kb, vb, rs, kt_next, L, nxt, nxt + TILE, wave, lane);
+  const int k_lo = kt * BC, k_hi = k_lo + BC - 1;
+  const int qz = qa + 31;
+  if ((qa >= L) || (k_lo > qz) || (qa - k_hi >= w)) return;
+  if (k_hi <= qa && qz - k_lo < w)
+    fwd_tile<D, false>(cur, cur + TILE, k_lo, qi, w, sl2, qf, lo, S, lane);
+  else
+    fwd_tile<D, true>(cur, cur + TILE, k_lo, qi, w, sl2, qf, lo, S, lane);
+}
+
+// NW waves x 32 queries per workgroup, NS-stage K/V ring (prefetch NS - 1 tiles ahead).
+template <int D, int NW, int NS>
+__global__ __launch_bounds__(64 * NW, (NW >= 8 ? 1 : 2)) void fwd_bf16_kernel(FwdArgs p) {
   constexpr int BR = 32 * NW;
   constexpr int BC = kFwdBC;
   constexpr int DK = D / 16;  // MFMA k-steps over D
   constexpr int MB = D / 32;  // 32-row blocks of O^T
   constexpr int TILE = BC * D;
+  constexpr int LOADS = 2 * (BC * D / 512) / NW;  // global_load_lds per wave per tile
+  static_assert((BC * D / 512) % NW == 0, "every wave issues the same number of DMA loads");
 
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * TILE];  // [stage][K|V]
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * 2 * TILE];  // [stage][K|V]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -174,15 +222,21 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs p) {
   S.l_run = 0.f;
 
   const LdsOffsets<D> lo(lane);
-  fwd_issue_tile<D, NW>(kb, vb, rs, kt_begin, L, smem, smem + TILE, wave, lane);
-  uint16_t* stage0 = smem;
-  uint16_t* stage1 = smem + 2 * TILE;
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (kt_begin + i <= kt_end)
+      fwd_issue_tile<D, NW>(kb, vb, rs, kt_begin + i, L, smem + i * 2 * TILE,
+                            smem + i * 2 * TILE + TILE, wave, lane);
+  int st = 0;  // stage of tile kt
   for (int kt = kt_begin; kt <= kt_end; ++kt) {
-    wait_vmcnt<0>();  // this tile's DMA (the only one in flight) has landed
-    __syncthreads();  // ... for every wave, and every wave is done with the other stage
-    const bool even = ((kt - kt_begin) & 1) == 0;
-    fwd_step<D, NW>(even ? stage0 : stage1, even ? stage1 : stage0, kt < kt_end, kt + 1, kb, vb,
-                    rs, L, kt, qa, qi, w, p.scale_log2, qf, lo, S, wave, lane);
+    // tile kt has landed once at most the (NS - 2) younger tiles' DMA is still in flight
+    if (NS == 3 && kt < kt_end) wait_vmcnt<LOADS>(); else wait_vmcnt<0>();
+    __syncthreads();  // ... for every wave; and every wave is done with the stage refilled next
+    const int nx = (st + NS - 1) % NS;
+    fwd_step<D, NW>(smem + st * 2 * TILE, smem + nx * 2 * TILE, kt + NS - 1 <= kt_end,
+                    kt + NS - 1, kb, vb, rs, L, kt, qa, qi, w, p.scale_log2, qf, lo, S, wave,
+                    lane);
+    st = (st + 1) % NS;
   }
 
   const float l_tot = sum_with_partner(S.l_run);
@@ -313,12 +367,12 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-template <int D, int NW>
+template <int D, int NW, int NS>
 static hipError_t launch_bf16(const FwdArgs& a, hipStream_t s) {
   FwdArgs p = a;
   p.n_qtiles = (p.T + 32 * NW - 1) / (32 * NW);
   const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.BH;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW>), dim3(grid), dim3(64 * NW), 0, s, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS>), dim3(grid), dim3(64 * NW), 0, s, p);
   return hipGetLastError();
 }
 
@@ -333,7 +387,7 @@ static hipError_t launch_f32(const FwdArgs& a, hipStream_t s) {
 
 hipError_t launch_fwd(const FwdArgs& a, bool f32, hipStream_t s) {
   if (f32) return a.D == 64 ? launch_f32<64>(a, s) : launch_f32<128>(a, s);
-  return a.D == 64 ? launch_bf16<64, 4>(a, s) : launch_bf16<128, 4>(a, s);
+  return a.D == 64 ? launch_bf16<64, FWD_NW, FWD_NS>(a, s) : launch_bf16<128, FWD_NW, FWD_NS>(a, s);
 }
 
 }  // namespace swattn
