@@ -58,7 +58,11 @@ def cpu_baseline(case, q, k, v, do, n_heads: int):
     from oracle import attention as ref
 
     B, H = case.B, case.H
-    heads = [(i % B, (i * 7 + i // B) % H) for i in range(n_heads)]
+    n_heads = min(n_heads, B * H)
+    if n_heads == B * H:  # the whole layer
+        heads = [(b, h) for b in range(B) for h in range(H)]
+    else:  # a spread of distinct heads
+        heads = sorted({((i * 13) % B, (i * 7) % H) for i in range(4 * n_heads)})[:n_heads]
     pick = lambda t: torch.stack([t[b, :, h] for b, h in heads])[:, :, None, :].double().numpy()  # noqa: E731
     Q, K, V, DO = pick(q), pick(k), pick(v), pick(do)
     threads = min(16, len(os.sched_getaffinity(0)))
@@ -66,14 +70,15 @@ def cpu_baseline(case, q, k, v, do, n_heads: int):
     ref.forward(Q, K, V, case.window, threads=threads)
     ref.backward(Q, K, V, DO, case.window, threads=threads)
     dt = time.perf_counter() - t0
-    flops = 14 * case.D * pairs(case.T, case.window) * n_heads
+    flops = 14 * case.D * pairs(case.T, case.window) * len(heads)
     return {
         "value": round(flops / dt / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"fp64 oracle fwd+bwd on {n_heads} of the {B * H} (b,h) heads of the d20 layer "
-                  f"(T={case.T}, D={case.D}, full causal), same seeded inputs; {dt:.2f} s wall",
+        "sample": f"fp64 oracle fwd+bwd on {len(heads)} of the {B * H} (b,h) heads of the d20 "
+                  f"layer (T={case.T}, D={case.D}, full causal), same seeded inputs; {dt:.2f} s "
+                  f"wall on {threads} threads",
     }
 
 

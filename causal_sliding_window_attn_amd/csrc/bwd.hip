@@ -95,10 +95,9 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
-  // head-major work items (all query tiles of one head on one XCD), longest tiles first
-  const int item = xcd_remap(blockIdx.x, p.n_tiles * p.BH);
-  const int bh = item / p.n_tiles;
-  const int qt = p.n_tiles - 1 - item % p.n_tiles;
+  const int bid = blockIdx.x;
+  const int qt = p.n_tiles - 1 - bid / p.BH;
+  const int bh = bid % p.BH;
   const int b = bh / p.H, h = bh % p.H;
   const int T = p.T;
   const int q0 = qt * BR;
@@ -348,11 +347,9 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs p)
   const int kblk = wave & 3;
   float* sP = sPall + kblk * BQ * 32;
 
-  // head-major work items (all key tiles of one head on one XCD); key tiles nearest the start
-  // see the most queries: first
-  const int item = xcd_remap(blockIdx.x, p.n_tiles * p.BH);
-  const int bh = item / p.n_tiles;
-  const int kt = item % p.n_tiles;
+  const int bid = blockIdx.x;
+  const int kt = bid / p.BH;  // key tiles nearest the start see the most queries: first
+  const int bh = bid % p.BH;
   const int b = bh / p.H, h = bh % p.H;
   const int T = p.T;
   const int k0 = kt * BK;

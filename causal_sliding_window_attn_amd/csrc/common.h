@@ -90,18 +90,6 @@ __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
-// Workgroup -> work item mapping aware of the 8 XCDs of an MI355X.  Workgroup ids are dealt to
-// the XCDs round-robin (id % 8), and each XCD has its own L2.  This bijection gives XCD x a
-// contiguous slice of the G work items, in order, so when work items are numbered head-major all
-// tiles of one (batch, head) -- which re-read the same K/V (or Q/dO) -- run on one XCD at about
-// the same time and share its L2.
-__device__ __forceinline__ int xcd_remap(int bid, int G) {
-  constexpr int X = 8;
-  const int x = bid % X, slot = bid / X;
-  const int q = G / X, r = G % X;
-  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + slot;
-}
-
 // ---------------------------------------------------------------------------------------------
 // LDS tile layouts for a tile of R sequence rows x D features (bf16).
 //

@@ -184,10 +184,9 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 1 : 2)) void fwd_bf16_kernel(Fw
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
 
-  // head-major work items (all query tiles of one head on one XCD), longest tiles first
-  const int item = xcd_remap(blockIdx.x, p.n_qtiles * p.BH);
-  const int bh = item / p.n_qtiles;
-  const int qt = p.n_qtiles - 1 - item % p.n_qtiles;
+  const int bid = blockIdx.x;
+  const int qt = p.n_qtiles - 1 - bid / p.BH;  // longest query tiles first
+  const int bh = bid % p.BH;
   const int b = bh / p.H, h = bh % p.H;
 
   int L = p.kv_len;
