@@ -12,8 +12,8 @@
 // the forward), computes Delta for them first and writes it to the workspace, then walks the
 // in-window key tiles: S^T = K Q^T, dP^T = V dO^T, dS^T, and dQ^T += K^T dS^T.
 // dK/dV pass: a workgroup owns 128 keys and walks the query tiles that can see them; half of its
-// waves compute S = Q K^T, P and dV^T += dO^T P, the other half dP = dO V^T, dS and dK^T += Q^T dS,
-// exchanging P through LDS (lane = key in both).
+// waves compute S = Q K^T, P and dV^T += dO^T P, the other half, one tile behind, dP = dO V^T, dS
+// and dK^T += Q^T dS, taking P through LDS (lane = key in both).
 // Both passes stream their tiles global -> LDS with global_load_lds into a two-stage ring (one
 // tile ahead, one barrier per tile) and take every transposed operand (K^T, Q^T, dO^T) straight
 // from the row-major tile with ds_read_b64_tr_b16.
@@ -182,15 +182,19 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs p) {
 // ---------------------------------------------------------------------------------------- dK/dV
 // Eight waves own 128 keys: waves 0-3 ("P waves") compute S = Q K^T and P for key block w and
 // accumulate dV^T += dO^T P; waves 4-7 ("dS waves") compute dP = dO V^T for the same key block and
-// accumulate dK^T += Q^T dS.  P passes from one to the other through LDS in register order (fp32),
-// so each wave carries one operand fragment set and one accumulator set -- two waves per SIMD --
-// and the MFMA work per phase is balanced: {S | dP}, barrier, {dV | dS, dK}.
+// accumulate dK^T += Q^T dS.  The dS waves run one query tile behind: in iteration i the P waves
+// handle tile i and leave its P (bf16, register order) in one of two LDS buffers, while the dS
+// waves handle tile i - 1 with the P left there in iteration i - 1.  A three-stage Q/dO ring keeps
+// tiles i + 1 (in flight), i and i - 1 resident, so one barrier per tile suffices and each wave
+// runs its own 32 MFMAs per tile without waiting for the other role.
 constexpr int kDkdvWaves = 8;
+constexpr int kDkdvStages = 3;
 
 template <int D>
 struct DkdvStage {
   static constexpr int TILE = kBwdBQ * D;
   static constexpr int ELEMS = 2 * TILE + 2 * kBwdBQ * 2;  // Q | dO | LSE | Delta, uint16 units
+  static constexpr int PELEMS = 4 * kBwdBQ * 32;           // bf16 P of 4 key blocks x 64 queries
 };
 
 template <int D, int NW>
@@ -233,119 +237,123 @@ __device__ __forceinline__ void dkdv_probs(f32x16& acc, const float* sL, int qb2
   }
 }
 
-// Phase 1 of one query tile.  P waves: S, P (written to sP); dS waves: dP (kept in registers).
+__device__ __forceinline__ bool dkdv_block_live(int qt, int qb2, int ka, int T, int w) {
+  const int qs = qt * kBwdBQ + 32 * qb2, qz = qs + 31, kz = ka + 31;
+  return !(ka >= T || qz < ka || qs - kz >= w || qs >= T);
+}
+
+// P waves, one query tile: S, P (to sP, bf16), dV^T += dO^T P.
 template <int D>
-__device__ __forceinline__ void dkdv_phase1(const uint16_t* __restrict__ cur,
-                                            float* __restrict__ sP, bool pwave, int qt, int ka,
-                                            int kj, int T, int w, float sl2,
-                                            const uint4 (&frag)[D / 16], f32x16 (&dp)[2],
-                                            const LdsOffsets<D>& lo, int lane) {
-  constexpr int BQ = kBwdBQ, DK = D / 16, TILE = DkdvStage<D>::TILE;
-  const int half = lane >> 5, l32 = lane & 31;
-  const uint16_t* src = pwave ? cur : cur + TILE;  // Q rows for S, dO rows for dP
+__device__ __forceinline__ void dkdv_pwave(const uint16_t* __restrict__ cur,
+                                           uint16_t* __restrict__ sP, int qt, int ka, int kj,
+                                           int T, int w, float sl2, const uint4 (&kf)[D / 16],
+                                           f32x16 (&dvacc)[D / 32], const LdsOffsets<D>& lo,
+                                           int lane) {
+  constexpr int BQ = kBwdBQ, DK = D / 16, MB = D / 32, TILE = DkdvStage<D>::TILE;
+  const int half = lane >> 5;
+  const uint16_t* sQ = cur;
+  const uint16_t* sO = cur + TILE;
   const float* sL = reinterpret_cast<const float*>(cur + 2 * TILE);
 #pragma unroll
   for (int qb2 = 0; qb2 < BQ / 32; ++qb2) {
-    const int qs = qt * BQ + 32 * qb2, qz = qs + 31, kz = ka + 31;
-    if (ka >= T || qz < ka || qs - kz >= w || qs >= T) continue;
+    if (!dkdv_block_live(qt, qb2, ka, T, w)) continue;
     f32x16 acc = zero16();
 #pragma unroll
-    for (int t = 0; t < DK; ++t) acc = mfma32(rc_frag<D>(src, lo, qb2, t), frag[t], acc);
-    if (!pwave) {
-      dp[qb2] = acc;
-      continue;
-    }
+    for (int t = 0; t < DK; ++t) acc = mfma32(rc_frag<D>(sQ, lo, qb2, t), kf[t], acc);
+    const int qs = qt * BQ + 32 * qb2, qz = qs + 31, kz = ka + 31;
     if (qs >= kz && qz - ka < w && qz < T)
       dkdv_probs<false>(acc, sL, qb2, qt, kj, T, w, sl2, half);
     else
       dkdv_probs<true>(acc, sL, qb2, qt, kj, T, w, sl2, half);
-    float4* dst = reinterpret_cast<float4*>(sP) + qb2 * 4 * 64;
+    const uint4 pf0 = pack_frag(acc, 0), pf1 = pack_frag(acc, 1);
+    uint4* dst = reinterpret_cast<uint4*>(sP) + qb2 * 2 * 64;
+    dst[lane] = pf0;
+    dst[64 + lane] = pf1;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      dst[j * 64 + lane] = make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]);
+    for (int m = 0; m < MB; ++m) {
+      dvacc[m] = mfma32(tr_frag_o<D>(sO, lo, 32 * qb2, m), pf0, dvacc[m]);
+      dvacc[m] = mfma32(tr_frag_o<D>(sO, lo, 32 * qb2 + 16, m), pf1, dvacc[m]);
+    }
   }
 }
 
-// Phase 2.  P waves: dV^T += dO^T P; dS waves: dS = P (dP - Delta), dK^T += Q^T dS.
+// dS waves, one query tile: dP, dS = P (dP - Delta) with P from sP, dK^T += Q^T dS.
 template <int D>
-__device__ __forceinline__ void dkdv_phase2(const uint16_t* __restrict__ cur,
-                                            const float* __restrict__ sP, bool pwave, int qt,
-                                            int ka, int T, int w, const f32x16 (&dp)[2],
-                                            f32x16 (&acc)[D / 32], const LdsOffsets<D>& lo,
-                                            int lane) {
-  constexpr int BQ = kBwdBQ, MB = D / 32, TILE = DkdvStage<D>::TILE;
+__device__ __forceinline__ void dkdv_swave(const uint16_t* __restrict__ cur,
+                                           const uint16_t* __restrict__ sP, int qt, int ka, int T,
+                                           int w, const uint4 (&vf)[D / 16],
+                                           f32x16 (&dkacc)[D / 32], const LdsOffsets<D>& lo,
+                                           int lane) {
+  constexpr int BQ = kBwdBQ, DK = D / 16, MB = D / 32, TILE = DkdvStage<D>::TILE;
   const int half = lane >> 5;
   const uint16_t* sQ = cur;
   const uint16_t* sO = cur + TILE;
   const float* sDl = reinterpret_cast<const float*>(cur + 2 * TILE) + BQ;
 #pragma unroll
   for (int qb2 = 0; qb2 < BQ / 32; ++qb2) {
-    const int qs = qt * BQ + 32 * qb2, qz = qs + 31, kz = ka + 31;
-    if (ka >= T || qz < ka || qs - kz >= w || qs >= T) continue;
-    const float4* src = reinterpret_cast<const float4*>(sP) + qb2 * 4 * 64;
-    f32x16 x;
+    if (!dkdv_block_live(qt, qb2, ka, T, w)) continue;
+    f32x16 dp = zero16();
+#pragma unroll
+    for (int t = 0; t < DK; ++t) dp = mfma32(rc_frag<D>(sO, lo, qb2, t), vf[t], dp);
+    const uint4* src = reinterpret_cast<const uint4*>(sP) + qb2 * 2 * 64;
+    const uint4 pw[2] = {src[lane], src[64 + lane]};
+    const uint32_t* pu = reinterpret_cast<const uint32_t*>(pw);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float4 v4 = src[j * 64 + lane];
-      x[4 * j] = v4.x;
-      x[4 * j + 1] = v4.y;
-      x[4 * j + 2] = v4.z;
-      x[4 * j + 3] = v4.w;
-    }
-    if (!pwave) {
+      const float4 d4 = *reinterpret_cast<const float4*>(sDl + 32 * qb2 + 8 * j + 4 * half);
+      const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 d4 = *reinterpret_cast<const float4*>(sDl + 32 * qb2 + 8 * j + 4 * half);
-        x[4 * j] *= dp[qb2][4 * j] - d4.x;
-        x[4 * j + 1] *= dp[qb2][4 * j + 1] - d4.y;
-        x[4 * j + 2] *= dp[qb2][4 * j + 2] - d4.z;
-        x[4 * j + 3] *= dp[qb2][4 * j + 3] - d4.w;
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * j + i;  // P slot r is bf16 element r of the packed pair (u = r / 8)
+        const uint32_t word = pu[r >> 1];
+        const float pr = (r & 1) ? bf16_hi(word) : bf16_lo(word);
+        dp[r] = pr * (dp[r] - dv[i]);
       }
     }
-    const uint16_t* tsrc = pwave ? sO : sQ;  // dO^T for dV, Q^T for dK
+    const uint4 df0 = pack_frag(dp, 0), df1 = pack_frag(dp, 1);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint4 f = pack_frag(x, u);
-#pragma unroll
-      for (int m = 0; m < MB; ++m)
-        acc[m] = mfma32(tr_frag_o<D>(tsrc, lo, 32 * qb2 + 16 * u, m), f, acc[m]);
+    for (int m = 0; m < MB; ++m) {
+      dkacc[m] = mfma32(tr_frag_o<D>(sQ, lo, 32 * qb2, m), df0, dkacc[m]);
+      dkacc[m] = mfma32(tr_frag_o<D>(sQ, lo, 32 * qb2 + 16, m), df1, dkacc[m]);
     }
   }
 }
 
-// One query tile: issue the next tile's DMA into `nxt`, phase 1, LDS hand-off of P, phase 2.  The
-// __restrict__ qualifiers state that, within one tile, the stage being read, the stage being
-// filled and the P exchange buffer are distinct, so the LDS reads need not wait for the DMA.
+// One iteration: DMA of the next tile into `nxt`, then the P waves on `curp` (tile qt) and the dS
+// waves on `curs` (tile qt - 1).  The __restrict__ qualifiers state that, within one iteration,
+// the three stages and the two P buffers are distinct, so LDS reads need not wait for the DMA.
 template <int D, int NW>
-__device__ __forceinline__ void dkdv_step(const uint16_t* __restrict__ cur,
-                                          uint16_t* __restrict__ nxt, float* __restrict__ sP,
-                                          bool issue_next, const uint16_t* qb, const uint16_t* db,
-                                          const float* lseb, const float* delb, int rs, int qt,
-                                          int ka, int kj, int T, int w, float sl2, bool pwave,
-                                          const uint4 (&frag)[D / 16], f32x16 (&dp)[2],
+__device__ __forceinline__ void dkdv_step(const uint16_t* __restrict__ curp,
+                                          const uint16_t* __restrict__ curs,
+                                          uint16_t* __restrict__ nxt, uint16_t* __restrict__ pw,
+                                          const uint16_t* __restrict__ pr, bool issue_next,
+                                          bool p_on, bool s_on, const uint16_t* qb,
+                                          const uint16_t* db, const float* lseb, const float* delb,
+                                          int rs, int qt, int ka, int kj, int T, int w, float sl2,
+                                          bool pwave, const uint4 (&frag)[D / 16],
                                           f32x16 (&acc)[D / 32], const LdsOffsets<D>& lo,
                                           int wave, int lane) {
   if (issue_next) dkdv_issue<D, NW>(qb, db, lseb, delb, rs, qt + 1, T, nxt, wave, lane);
-  dkdv_phase1<D>(cur, sP, pwave, qt, ka, kj, T, w, sl2, frag, dp, lo, lane);
-  lds_barrier();  // P of this tile is in LDS
-  dkdv_phase2<D>(cur, sP, pwave, qt, ka, T, w, dp, acc, lo, lane);
+  if (pwave) {
+    if (p_on) dkdv_pwave<D>(curp, pw, qt, ka, kj, T, w, sl2, frag, acc, lo, lane);
+  } else {
+    if (s_on) dkdv_swave<D>(curs, pr, qt - 1, ka, T, w, frag, acc, lo, lane);
+  }
 }
 
 template <int D>
 __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs p) {
-  constexpr int NW = kDkdvWaves, BK = 128, BQ = kBwdBQ;
-  constexpr int DK = D / 16, MB = D / 32, SE = DkdvStage<D>::ELEMS;
-  constexpr int PELEMS = 4 * BQ * 32;  // fp32 P of 4 key blocks x 64 queries
+  constexpr int NW = kDkdvWaves, NS = kDkdvStages, BK = 128, BQ = kBwdBQ;
+  constexpr int DK = D / 16, MB = D / 32, SE = DkdvStage<D>::ELEMS, PE = DkdvStage<D>::PELEMS;
 
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * SE];
-  __shared__ __attribute__((aligned(16))) float sPall[PELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * SE];
+  __shared__ __attribute__((aligned(16))) uint16_t sPbuf[2 * PE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const bool pwave = wave < 4;
   const int kblk = wave & 3;
-  float* sP = sPall + kblk * BQ * 32;
 
   const int bid = blockIdx.x;
   const int kt = bid / p.BH;  // key tiles nearest the start see the most queries: first
@@ -381,18 +389,19 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs p)
   f32x16 acc[MB];  // dV^T (P waves) or dK^T (dS waves)
 #pragma unroll
   for (int m = 0; m < MB; ++m) acc[m] = zero16();
-  f32x16 dp[2];
 
   const LdsOffsets<D> lo(lane);
-  uint16_t* stage0 = smem;
-  uint16_t* stage1 = smem + SE;
-  for (int qt = qt_begin; qt <= qt_end; ++qt) {
-    wait_vmcnt<0>();
-    __syncthreads();  // stage qt landed for all waves; previous tile's phase 2 is finished
-    const bool even = ((qt - qt_begin) & 1) == 0;
-    dkdv_step<D, NW>(even ? stage0 : stage1, even ? stage1 : stage0, sP, qt < qt_end, qb, db,
-                     lseb, delb, rs, qt, ka, kj, T, w, p.scale_log2, pwave, frag, dp, acc, lo,
-                     wave, lane);
+  uint16_t* myP = sPbuf + kblk * (PE / 4);  // this key block's part of each P buffer
+  // iteration i: P waves on tile qt_begin + i (stage i % 3), dS waves on tile qt_begin + i - 1
+  const int n = qt_end - qt_begin + 1;
+  for (int i = 0; i <= n; ++i) {
+    wait_vmcnt<0>();  // tile i (the only DMA in flight) has landed
+    __syncthreads();  // ... for all waves; P of tile i - 1 is complete; stage (i + 1) % 3 is free
+    const int qt = qt_begin + i;
+    dkdv_step<D, NW>(smem + (i % NS) * SE, smem + ((i + NS - 1) % NS) * SE,
+                     smem + ((i + 1) % NS) * SE, myP + (i & 1) * PE, myP + ((i + 1) & 1) * PE,
+                     i + 1 < n, i < n, i >= 1, qb, db, lseb, delb, rs, qt, ka, kj, T, w,
+                     p.scale_log2, pwave, frag, acc, lo, wave, lane);
   }
 
   if (!kvalid) return;
