@@ -198,12 +198,14 @@ struct DkdvStage {
 };
 
 template <int D, int NW>
-__device__ __forceinline__ void dkdv_issue(const uint16_t* qb, const uint16_t* db,
-                                           const float* lseb, const float* delb, int rs, int qt,
-                                           int T, uint16_t* stage, int wave, int lane) {
+__device__ __forceinline__ void dkdv_issue(const RowDma<D, NW, kBwdBQ>& dma, const uint16_t* qb,
+                                           const uint16_t* db, const float* lseb,
+                                           const float* delb, int rs, int qt, int T,
+                                           uint16_t* stage, int wave, int lane) {
   constexpr int BQ = kBwdBQ, TILE = DkdvStage<D>::TILE;
-  issue_rows<D, NW, BQ>(qb, rs, qt * BQ, T - 1, stage, wave, lane);
-  issue_rows<D, NW, BQ>(db, rs, qt * BQ, T - 1, stage + TILE, wave, lane);
+  const int64_t row0 = (int64_t)qt * BQ * rs;
+  dma.issue(qb + row0, T - qt * BQ, stage, wave, lane);
+  dma.issue(db + row0, T - qt * BQ, stage + TILE, wave, lane);
   static_assert(BQ == 64, "one 4-byte DMA per lane covers the 64 rows' LSE / Delta");
   if (wave == NW - 1) {
     const int j = min(qt * BQ + lane, T - 1);
@@ -230,7 +232,7 @@ __device__ __forceinline__ void dkdv_probs(f32x16& acc, const float* sL, int qb2
       if (MASK) {
         // query i sees key j iff (unsigned)(i - j) < w; rows past T hold a clamped copy: drop them
         const int qg = qt * BQ + ql0 + i;
-        pr = ((unsigned)(qg - kj) < (unsigned)w) & (qg < T) ? pr : 0.f;
+        pr = (((unsigned)(qg - kj) < (unsigned)w) & (qg < T)) ? pr : 0.f;
       }
       acc[r] = pr;
     }
@@ -319,25 +321,48 @@ __device__ __forceinline__ void dkdv_swave(const uint16_t* __restrict__ cur,
   }
 }
 
-// One iteration: DMA of the next tile into `nxt`, then the P waves on `curp` (tile qt) and the dS
-// waves on `curs` (tile qt - 1).  The __restrict__ qualifiers state that, within one iteration,
-// the three stages and the two P buffers are distinct, so LDS reads need not wait for the DMA.
-template <int D, int NW>
+// One iteration: DMA of the next tile into `nxt`, then a P wave on `curp` (tile qt) or a dS wave
+// on `curs` (tile qt - 1).  The __restrict__ qualifiers state that, within one iteration, the three
+// stages and the two P buffers are distinct, so LDS reads need not wait for the DMA.
+template <int D, int NW, bool PW>
 __device__ __forceinline__ void dkdv_step(const uint16_t* __restrict__ curp,
                                           const uint16_t* __restrict__ curs,
                                           uint16_t* __restrict__ nxt, uint16_t* __restrict__ pw,
                                           const uint16_t* __restrict__ pr, bool issue_next,
-                                          bool p_on, bool s_on, const uint16_t* qb,
-                                          const uint16_t* db, const float* lseb, const float* delb,
-                                          int rs, int qt, int ka, int kj, int T, int w, float sl2,
-                                          bool pwave, const uint4 (&frag)[D / 16],
-                                          f32x16 (&acc)[D / 32], const LdsOffsets<D>& lo,
-                                          int wave, int lane) {
-  if (issue_next) dkdv_issue<D, NW>(qb, db, lseb, delb, rs, qt + 1, T, nxt, wave, lane);
-  if (pwave) {
-    if (p_on) dkdv_pwave<D>(curp, pw, qt, ka, kj, T, w, sl2, frag, acc, lo, lane);
-  } else {
-    if (s_on) dkdv_swave<D>(curs, pr, qt - 1, ka, T, w, frag, acc, lo, lane);
+                                          bool on, const uint16_t* qb, const uint16_t* db,
+                                          const float* lseb, const float* delb, int rs, int qt,
+                                          int ka, int kj, int T, int w, float sl2,
+                                          const uint4 (&frag)[D / 16], f32x16 (&acc)[D / 32],
+                                          const LdsOffsets<D>& lo,
+                                          const RowDma<D, NW, kBwdBQ>& dma, int wave, int lane) {
+  if (issue_next) dkdv_issue<D, NW>(dma, qb, db, lseb, delb, rs, qt + 1, T, nxt, wave, lane);
+  if (!on) return;
+  if (PW)
+    dkdv_pwave<D>(curp, pw, qt, ka, kj, T, w, sl2, frag, acc, lo, lane);
+  else
+    dkdv_swave<D>(curs, pr, qt - 1, ka, T, w, frag, acc, lo, lane);
+}
+
+// The tile loop of one role.  Both roles pass the same barriers in the same order; each role gets
+// its own copy of the loop so that its accumulators stay in one set of registers.
+// Iteration i: P waves on tile qt_begin + i (stage i % 3), dS waves on tile qt_begin + i - 1.
+template <int D, int NW, bool PW>
+__device__ __forceinline__ void dkdv_loop(uint16_t* smem, uint16_t* myP, int qt_begin, int n,
+                                          const uint16_t* qb, const uint16_t* db,
+                                          const float* lseb, const float* delb, int rs, int ka,
+                                          int kj, int T, int w, float sl2,
+                                          const uint4 (&frag)[D / 16], f32x16 (&acc)[D / 32],
+                                          const LdsOffsets<D>& lo,
+                                          const RowDma<D, NW, kBwdBQ>& dma, int wave, int lane) {
+  constexpr int NS = kDkdvStages, SE = DkdvStage<D>::ELEMS, PE = DkdvStage<D>::PELEMS;
+  for (int i = 0; i <= n; ++i) {
+    wait_vmcnt<0>();  // tile i (the only DMA in flight) has landed
+    __syncthreads();  // ... for all waves; P of tile i - 1 is complete; stage (i + 1) % 3 is free
+    dkdv_step<D, NW, PW>(smem + (i % NS) * SE, smem + ((i + NS - 1) % NS) * SE,
+                         smem + ((i + 1) % NS) * SE, myP + (i & 1) * PE,
+                         myP + ((i + 1) & 1) * PE, i + 1 < n, PW ? (i < n) : (i >= 1), qb, db,
+                         lseb, delb, rs, qt_begin + i, ka, kj, T, w, sl2, frag, acc, lo, dma,
+                         wave, lane);
   }
 }
 
@@ -372,7 +397,8 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs p)
   const float* lseb = p.lse + (int64_t)bh * T;
   const float* delb = p.delta + (int64_t)bh * T;
 
-  dkdv_issue<D, NW>(qb, db, lseb, delb, rs, qt_begin, T, smem, wave, lane);
+  const RowDma<D, NW, BQ> dma(rs, wave, lane);
+  dkdv_issue<D, NW>(dma, qb, db, lseb, delb, rs, qt_begin, T, smem, wave, lane);
 
   const int ka = k0 + 32 * kblk;
   const int kj = ka + l32;
@@ -392,17 +418,13 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs p)
 
   const LdsOffsets<D> lo(lane);
   uint16_t* myP = sPbuf + kblk * (PE / 4);  // this key block's part of each P buffer
-  // iteration i: P waves on tile qt_begin + i (stage i % 3), dS waves on tile qt_begin + i - 1
   const int n = qt_end - qt_begin + 1;
-  for (int i = 0; i <= n; ++i) {
-    wait_vmcnt<0>();  // tile i (the only DMA in flight) has landed
-    __syncthreads();  // ... for all waves; P of tile i - 1 is complete; stage (i + 1) % 3 is free
-    const int qt = qt_begin + i;
-    dkdv_step<D, NW>(smem + (i % NS) * SE, smem + ((i + NS - 1) % NS) * SE,
-                     smem + ((i + 1) % NS) * SE, myP + (i & 1) * PE, myP + ((i + 1) & 1) * PE,
-                     i + 1 < n, i < n, i >= 1, qb, db, lseb, delb, rs, qt, ka, kj, T, w,
-                     p.scale_log2, pwave, frag, acc, lo, wave, lane);
-  }
+  if (pwave)
+    dkdv_loop<D, NW, true>(smem, myP, qt_begin, n, qb, db, lseb, delb, rs, ka, kj, T, w,
+                           p.scale_log2, frag, acc, lo, dma, wave, lane);
+  else
+    dkdv_loop<D, NW, false>(smem, myP, qt_begin, n, qb, db, lseb, delb, rs, ka, kj, T, w,
+                            p.scale_log2, frag, acc, lo, dma, wave, lane);
 
   if (!kvalid) return;
   const float sc = pwave ? 1.f : p.scale;

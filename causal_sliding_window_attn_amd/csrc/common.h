@@ -216,6 +216,54 @@ __device__ __forceinline__ void issue_rows(const uint16_t* base, int rs, int row
   }
 }
 
+// Plan for streaming ROWS consecutive rows of a [*, rs]-strided bf16 tensor into a row-major
+// swizzled LDS tile with global_load_lds, NW waves sharing the work (one 1 KB instruction per
+// wave each).  Each lane's byte offset inside a tile is the same for every tile, so it is computed
+// once; a full tile then costs one scalar base plus one VGPR per load.  Rows past `nvalid` re-read
+// the last valid row: callers mask them, and no load leaves the tensor.
+template <int D, int NW, int ROWS>
+struct RowDma {
+  static constexpr int CPR = D / 8;     // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;  // rows per load instruction
+  static constexpr int INSTS = ROWS / RPI;
+  static constexpr int PER = INSTS / NW;  // instructions per wave
+  static_assert(INSTS % NW == 0, "every wave issues the same number of loads");
+  // a wave's successive loads are NW * RPI rows apart, a multiple of 16, so the swizzle term is
+  // the same for all of them: one per-lane offset plus a uniform stride
+  static_assert((NW * RPI) % 16 == 0, "swizzle period");
+  uint32_t off0;  // this lane's byte offset inside the tile for the wave's first load
+  int rs2;
+  __device__ __forceinline__ RowDma(int rs, int wave, int lane) : rs2(2 * rs) {
+    const int r = wave * RPI + lane / CPR;
+    off0 = (uint32_t)(r * rs2 + 16 * swz<D>(r, lane % CPR));
+  }
+  // Tile whose first row is `tile_row0` (pointer to that row's features of this head); rows
+  // past nvalid re-read row nvalid - 1.
+  __device__ __forceinline__ void issue(const uint16_t* tile_row0, int nvalid, uint16_t* lds,
+                                        int wave, int lane) const {
+    const char* b = reinterpret_cast<const char*>(tile_row0);
+    if (nvalid >= ROWS) {
+      // opaque copy: keeps the compiler from hoisting one 64-bit address per load out of the
+      // caller's loop, which costs more registers than the one add per load it saves
+      uint32_t o = off0;
+      asm volatile("" : "+v"(o));
+#pragma unroll
+      for (int k = 0; k < PER; ++k)
+        g2lds16(reinterpret_cast<const uint16_t*>(b + (int64_t)(k * NW * RPI) * rs2 + o),
+                lds + (wave + k * NW) * 512);
+    } else {
+      const int cp = lane % CPR;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int r = (wave + k * NW) * RPI + lane / CPR;
+        const int rc = min(r, nvalid - 1);
+        g2lds16(reinterpret_cast<const uint16_t*>(b + (int64_t)rc * rs2 + 16 * swz<D>(r, cp)),
+                lds + (wave + k * NW) * 512);
+      }
+    }
+  }
+};
+
 // The 16-byte row chunk c (features 8c .. 8c+7) of row r of a swizzled tile.
 template <int D>
 __device__ __forceinline__ uint4 row_chunk(const uint16_t* tile, int r, int c) {

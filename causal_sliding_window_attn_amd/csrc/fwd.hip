@@ -31,11 +31,14 @@ constexpr int kFwdBC = 64;  // keys per tile
 
 // Streams one 64-key tile of K and of V into LDS (row-major, swizzled) with global_load_lds.
 template <int D, int NW>
-__device__ __forceinline__ void fwd_issue_tile(const uint16_t* kb, const uint16_t* vb, int rs,
+__device__ __forceinline__ void fwd_issue_tile(const RowDma<D, NW, kFwdBC>& dma,
+                                               const uint16_t* kb, const uint16_t* vb, int rs,
                                                int kt, int L, uint16_t* sK, uint16_t* sV,
                                                int wave, int lane) {
-  issue_rows<D, NW, kFwdBC>(kb, rs, kt * kFwdBC, L - 1, sK, wave, lane);
-  issue_rows<D, NW, kFwdBC>(vb, rs, kt * kFwdBC, L - 1, sV, wave, lane);
+  const int64_t row0 = (int64_t)kt * kFwdBC * rs;
+  const int nvalid = L - kt * kFwdBC;
+  dma.issue(kb + row0, nvalid, sK, wave, lane);
+  dma.issue(vb + row0, nvalid, sV, wave, lane);
 }
 
 // Per-wave state of the forward that lives across key tiles.
@@ -63,7 +66,9 @@ __device__ __forceinline__ void fwd_tile_max(f32x16& s0, f32x16& s1, int k_lo, i
       s0[r] = (unsigned)(d0 - off) < (unsigned)w ? s0[r] : -INFINITY;
       s1[r] = (unsigned)(d0 - 32 - off) < (unsigned)w ? s1[r] : -INFINITY;
     }
-    mraw = fmaxf(mraw, fmaxf(s0[r], s1[r]));
+    // med3(a, b, largest float) = max(a, b) as one instruction whose result the compiler knows to be
+    // canonical, so the fmaxf chain below needs no canonicalising moves of the MFMA outputs
+    mraw = fmaxf(mraw, __builtin_amdgcn_fmed3f(s0[r], s1[r], 3.4028235e38f));
   }
   const float m_tile = max_with_partner(mraw) * sl2;
   // rescale O only when some row max has grown past the threshold (exact either way)
@@ -113,23 +118,31 @@ __device__ __forceinline__ void fwd_block_pv(const uint16_t* sV, const LdsOffset
     }
 }
 
-// The compute of one key tile: S^T for both 32-key blocks, the tile's softmax bookkeeping, then
-// block 0's PV MFMAs run under block 1's exponentials (interleave pinned with
-// sched_group_barrier) before block 1's PV.
+// S^T of one key tile (two 32-key blocks) and its softmax bookkeeping.  Only this part differs
+// between boundary and interior tiles.
 template <int D, bool MASK>
-__device__ __forceinline__ void fwd_tile(const uint16_t* __restrict__ sK,
-                                         const uint16_t* __restrict__ sV, int k_lo, int qi, int w,
-                                         float sl2, const uint4 (&qf)[D / 16],
-                                         const LdsOffsets<D>& lo, FwdState<D>& S, int lane) {
+__device__ __forceinline__ void fwd_tile_s(const uint16_t* __restrict__ sK, int k_lo, int qi,
+                                           int w, float sl2, const uint4 (&qf)[D / 16],
+                                           const LdsOffsets<D>& lo, FwdState<D>& S, f32x16& s0,
+                                           f32x16& s1, int lane) {
   constexpr int DK = D / 16;
-  const int half = lane >> 5;
-  f32x16 s0 = zero16(), s1 = zero16();
+  s0 = zero16();
+  s1 = zero16();
 #pragma unroll
   for (int t = 0; t < DK; ++t) {
     s0 = mfma32(rc_frag<D>(sK, lo, 0, t), qf[t], s0);
     s1 = mfma32(rc_frag<D>(sK, lo, 1, t), qf[t], s1);
   }
-  fwd_tile_max<D, MASK>(s0, s1, k_lo, qi, w, half, sl2, S);
+  fwd_tile_max<D, MASK>(s0, s1, k_lo, qi, w, lane >> 5, sl2, S);
+}
+
+// Probabilities and O update of one key tile, shared by boundary and interior tiles (one copy of
+// the code keeps O in the same registers on both paths): block 0's PV MFMAs run under block 1's
+// exponentials (interleave pinned with sched_group_barrier) before block 1's PV.
+template <int D>
+__device__ __forceinline__ void fwd_tile_pv(const uint16_t* __restrict__ sV, float sl2,
+                                            const LdsOffsets<D>& lo, FwdState<D>& S, f32x16& s0,
+                                            f32x16& s1) {
   uint4 ph0[2], pl0[2], ph1[2], pl1[2];
   fwd_block_exp<D>(s0, sl2, S, ph0, pl0);
   // { PV of block 0 } || { exponentials and packing of block 1 }
@@ -146,25 +159,52 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* __restrict__ sK,
 
 // One key tile: issue the DMA of the next tile into `nxt`, then consume `cur`.  Within one call the
 // two stages are distinct buffers, which the __restrict__ qualifiers state; that lets the compiler
-// see that the LDS reads of `cur` do not depend on the DMA writes to `nxt` still in flight.  Tiles
-// crossing the diagonal or the window edge take the masked instantiation (a wave-uniform branch).
-template <int D, int NW>
+// see that the LDS reads of `cur` do not depend on the DMA writes to `nxt` still in flight.  MASK
+// tiles may cross the diagonal or the window edge for some wave; a wave skips a tile it cannot see.
+template <int D, int NW, bool MASK>
 __device__ __forceinline__ void fwd_step(const uint16_t* __restrict__ cur,
                                          uint16_t* __restrict__ nxt, bool issue_next, int kt_next,
                                          const uint16_t* kb, const uint16_t* vb, int rs, int L,
                                          int kt, int qa, int qi, int w, float sl2,
                                          const uint4 (&qf)[D / 16], const LdsOffsets<D>& lo,
-                                         FwdState<D>& S, int wave, int lane) {
+                                         const RowDma<D, NW, kFwdBC>& dma, FwdState<D>& S,
+                                         int wave, int lane) {
   constexpr int BC = kFwdBC, TILE = BC * D;
   static_assert(BC == 64, "two 32-key blocks per tile");
-  if (issue_next) fwd_issue_tile<D, NW>(kb, vb, rs, kt_next, L, nxt, nxt + TILE, wave, lane);
-  const int k_lo = kt * BC, k_hi = k_lo + BC - 1;
-  const int qz = qa + 31;
-  if ((qa >= L) || (k_lo > qz) || (qa - k_hi >= w)) return;
-  if (k_hi <= qa && qz - k_lo < w)
-    fwd_tile<D, false>(cur, cur + TILE, k_lo, qi, w, sl2, qf, lo, S, lane);
-  else
-    fwd_tile<D, true>(cur, cur + TILE, k_lo, qi, w, sl2, qf, lo, S, lane);
+  if (issue_next)
+    fwd_issue_tile<D, NW>(dma, kb, vb, rs, kt_next, L, nxt, nxt + TILE, wave, lane);
+  const int k_lo = kt * BC;
+  if (MASK) {
+    const int k_hi = k_lo + BC - 1, qz = qa + 31;
+    if ((qa >= L) || (k_lo > qz) || (qa - k_hi >= w)) return;
+  } else {
+    if (qa >= L) return;
+  }
+  f32x16 s0, s1;
+  fwd_tile_s<D, MASK>(cur, k_lo, qi, w, sl2, qf, lo, S, s0, s1, lane);
+  fwd_tile_pv<D>(cur + TILE, sl2, lo, S, s0, s1);
+}
+
+// Key tiles kt0 .. kt1 - 1 through the NS-stage ring (stage `st` holds tile kt0 on entry).
+template <int D, int NW, int NS, bool MASK>
+__device__ __forceinline__ void fwd_run(int kt0, int kt1, int kt_end, int& st, uint16_t* smem,
+                                        const uint16_t* kb, const uint16_t* vb, int rs, int L,
+                                        int qa, int qi, int w, float sl2,
+                                        const uint4 (&qf)[D / 16], const LdsOffsets<D>& lo,
+                                        const RowDma<D, NW, kFwdBC>& dma, FwdState<D>& S,
+                                        int wave, int lane) {
+  constexpr int TILE = kFwdBC * D;
+  constexpr int LOADS = 2 * (kFwdBC * D / 512) / NW;  // global_load_lds per wave per tile
+  for (int kt = kt0; kt < kt1; ++kt) {
+    // tile kt has landed once at most the (NS - 2) younger tiles' DMA is still in flight
+    if (NS == 3 && kt < kt_end) wait_vmcnt<LOADS>(); else wait_vmcnt<0>();
+    __syncthreads();  // ... for every wave; and every wave is done with the stage refilled next
+    const int nx = (st + NS - 1) % NS;
+    fwd_step<D, NW, MASK>(smem + st * 2 * TILE, smem + nx * 2 * TILE, kt + NS - 1 <= kt_end,
+                          kt + NS - 1, kb, vb, rs, L, kt, qa, qi, w, sl2, qf, lo, dma, S, wave,
+                          lane);
+    st = (st + 1) % NS;
+  }
 }
 
 // NW waves x 32 queries per workgroup, NS-stage K/V ring (prefetch NS - 1 tiles ahead).
@@ -175,7 +215,6 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 1 : 2)) void fwd_bf16_kernel(Fw
   constexpr int DK = D / 16;  // MFMA k-steps over D
   constexpr int MB = D / 32;  // 32-row blocks of O^T
   constexpr int TILE = BC * D;
-  constexpr int LOADS = 2 * (BC * D / 512) / NW;  // global_load_lds per wave per tile
   static_assert((BC * D / 512) % NW == 0, "every wave issues the same number of DMA loads");
 
   __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * 2 * TILE];  // [stage][K|V]
@@ -222,21 +261,29 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 1 : 2)) void fwd_bf16_kernel(Fw
   S.l_run = 0.f;
 
   const LdsOffsets<D> lo(lane);
+  const RowDma<D, NW, BC> dma(rs, wave, lane);
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i)
     if (kt_begin + i <= kt_end)
-      fwd_issue_tile<D, NW>(kb, vb, rs, kt_begin + i, L, smem + i * 2 * TILE,
+      fwd_issue_tile<D, NW>(dma, kb, vb, rs, kt_begin + i, L, smem + i * 2 * TILE,
                             smem + i * 2 * TILE + TILE, wave, lane);
-  int st = 0;  // stage of tile kt
-  for (int kt = kt_begin; kt <= kt_end; ++kt) {
-    // tile kt has landed once at most the (NS - 2) younger tiles' DMA is still in flight
-    if (NS == 3 && kt < kt_end) wait_vmcnt<LOADS>(); else wait_vmcnt<0>();
-    __syncthreads();  // ... for every wave; and every wave is done with the stage refilled next
-    const int nx = (st + NS - 1) % NS;
-    fwd_step<D, NW>(smem + st * 2 * TILE, smem + nx * 2 * TILE, kt + NS - 1 <= kt_end,
-                    kt + NS - 1, kb, vb, rs, L, kt, qa, qi, w, p.scale_log2, qf, lo, S, wave,
-                    lane);
-    st = (st + 1) % NS;
+  // Tiles that every wave of the workgroup sees whole (k_hi <= q0 and q0 + BR - 1 - k_lo < w) run
+  // without the mask; the window-edge tiles before them and the diagonal tiles after them run with
+  // it.  Three loops rather than a per-tile branch keep O in one set of registers.
+  const int xw = q0 + BR - 1 - w;
+  const int in_lo = max(kt_begin, xw < 0 ? 0 : xw / BC + 1);
+  const int in_hi = min(kt_end + 1, (q0 + 1) / BC);  // exclusive
+  int st = 0;  // stage of the next tile
+  if (in_lo < in_hi) {
+    fwd_run<D, NW, NS, true>(kt_begin, in_lo, kt_end, st, smem, kb, vb, rs, L, qa, qi, w,
+                             p.scale_log2, qf, lo, dma, S, wave, lane);
+    fwd_run<D, NW, NS, false>(in_lo, in_hi, kt_end, st, smem, kb, vb, rs, L, qa, qi, w,
+                              p.scale_log2, qf, lo, dma, S, wave, lane);
+    fwd_run<D, NW, NS, true>(in_hi, kt_end + 1, kt_end, st, smem, kb, vb, rs, L, qa, qi, w,
+                             p.scale_log2, qf, lo, dma, S, wave, lane);
+  } else {
+    fwd_run<D, NW, NS, true>(kt_begin, kt_end + 1, kt_end, st, smem, kb, vb, rs, L, qa, qi, w,
+                             p.scale_log2, qf, lo, dma, S, wave, lane);
   }
 
   const float l_tot = sum_with_partner(S.l_run);
