@@ -26,10 +26,28 @@ constexpr int kBwdBC = 64;  // keys per tile in the dQ pass
 constexpr int kBwdBQ = 64;  // queries per tile in the dK/dV pass
 
 // ------------------------------------------------------------------------------------------ dQ
-template <int D, bool MASK>
+// dS^T = P^T (dP^T - Delta) for one 32-key block, in place in the S^T accumulator.
+template <bool MASK>
+__device__ __forceinline__ void dq_ds(f32x16& s, const f32x16& dp, int d0, int w, float sl2,
+                                      float lse2, float delta) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse2));
+    if (MASK) {
+      // key j is visible to query i iff (unsigned)(i - j) < w
+      const unsigned dist = (unsigned)(d0 - (8 * (r >> 2) + (r & 3)));
+      pr = dist < (unsigned)w ? pr : 0.f;
+    }
+    s[r] = pr * (dp[r] - delta);
+  }
+}
+
+// One key tile.  Only the probabilities depend on `mask` (a wave-uniform branch around them), so
+// the MFMA code and dQ's registers are the same for boundary and interior tiles.
+template <int D>
 __device__ __forceinline__ void dq_tile(const uint16_t* __restrict__ sK,
-                                        const uint16_t* __restrict__ sV, int k_lo, int qi, int w,
-                                        float sl2, float lse2, float delta,
+                                        const uint16_t* __restrict__ sV, bool mask, int k_lo,
+                                        int qi, int w, float sl2, float lse2, float delta,
                                         const uint4 (&qf)[D / 16], const uint4 (&df)[D / 16],
                                         const LdsOffsets<D>& lo, f32x16 (&dqacc)[D / 32],
                                         int lane) {
@@ -43,17 +61,11 @@ __device__ __forceinline__ void dq_tile(const uint16_t* __restrict__ sK,
       s = mfma32(rc_frag<D>(sK, lo, nb, t), qf[t], s);
       dp = mfma32(rc_frag<D>(sV, lo, nb, t), df[t], dp);
     }
-    // key j is visible to query i iff (unsigned)(i - j) < w
     const int d0 = qi - (k_lo + nb * 32) - 4 * half;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse2));
-      if (MASK) {
-        const unsigned dist = (unsigned)(d0 - (8 * (r >> 2) + (r & 3)));
-        pr = dist < (unsigned)w ? pr : 0.f;
-      }
-      s[r] = pr * (dp[r] - delta);
-    }
+    if (mask)
+      dq_ds<true>(s, dp, d0, w, sl2, lse2, delta);
+    else
+      dq_ds<false>(s, dp, d0, w, sl2, lse2, delta);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const uint4 dsf = pack_frag(s, u);
@@ -79,25 +91,18 @@ __device__ __forceinline__ void dq_step(const uint16_t* __restrict__ cur,
   }
   const int k_lo = kt * BC, k_hi = k_lo + BC - 1, qz = qa + 31;
   if ((qa >= T) || (k_lo > qz) || (qa - k_hi >= w)) return;
-  if (k_hi <= qa && qz - k_lo < w)
-    dq_tile<D, false>(cur, cur + TILE, k_lo, qi, w, sl2, lse2, delta, qf, df, lo, dqacc, lane);
-  else
-    dq_tile<D, true>(cur, cur + TILE, k_lo, qi, w, sl2, lse2, delta, qf, df, lo, dqacc, lane);
+  const bool mask = !(k_hi <= qa && qz - k_lo < w);
+  dq_tile<D>(cur, cur + TILE, mask, k_lo, qi, w, sl2, lse2, delta, qf, df, lo, dqacc, lane);
 }
 
+// One job: query tile qt (NW waves x 32 queries) of head bh.  Returns with every wave past its
+// last read of the two-stage ring.
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs p) {
+__device__ __forceinline__ void dq_job(const BwdArgs& p, int bh, int qt, uint16_t* smem, int wave,
+                                       int lane) {
   constexpr int BR = 32 * NW, BC = kBwdBC;
   constexpr int DK = D / 16, MB = D / 32, TILE = BC * D;
-
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * TILE];  // [stage][K|V]
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
-  const int bid = blockIdx.x;
-  const int qt = p.n_tiles - 1 - bid / p.BH;
-  const int bh = bid % p.BH;
   const int b = bh / p.H, h = bh % p.H;
   const int T = p.T;
   const int q0 = qt * BR;
@@ -177,6 +182,33 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs p) {
       st.y = pack_bf16x2(dqacc[m][4 * j + 2] * sc, dqacc[m][4 * j + 3] * sc);
       *reinterpret_cast<uint2*>(out + m * 32 + 8 * j + 4 * half) = st;
     }
+}
+
+// Full-causal training pass (p.paired): workgroup = head + query-tile pair (j, n - 1 - j), short
+// tile first (pair_job).  Otherwise: workgroup = one query tile, longest tiles first.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * kBwdBC * D];  // [stage][K|V]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bid = blockIdx.x;
+  int bh, qt0, qt1, njobs;
+  if (p.paired) {
+    const PairJob jb = pair_job(bid, p.BH, (p.n_tiles + 1) / 2);
+    bh = jb.bh;
+    qt0 = jb.j;
+    qt1 = p.n_tiles - 1 - jb.j;
+    njobs = qt1 != qt0 ? 2 : 1;
+  } else {
+    bh = bid % p.BH;
+    qt0 = qt1 = p.n_tiles - 1 - bid / p.BH;
+    njobs = 1;
+  }
+#pragma unroll 1
+  for (int jx = 0; jx < njobs; ++jx) {
+    if (jx) __syncthreads();  // every wave is done with the ring before the next job refills it
+    dq_job<D, NW>(p, bh, jx ? qt1 : qt0, smem, wave, lane);
+  }
 }
 
 // ---------------------------------------------------------------------------------------- dK/dV
@@ -321,74 +353,76 @@ __device__ __forceinline__ void dkdv_swave(const uint16_t* __restrict__ cur,
   }
 }
 
-// One iteration: DMA of the next tile into `nxt`, then a P wave on `curp` (tile qt) or a dS wave
-// on `curs` (tile qt - 1).  The __restrict__ qualifiers state that, within one iteration, the three
-// stages and the two P buffers are distinct, so LDS reads need not wait for the DMA.
+// One iteration: DMA of tile qt_next into `nxt`, then a P wave on `curp` (tile qt_p) or a dS wave
+// on `curs` (tile qt_s, the P waves' tile of the previous iteration).  The __restrict__ qualifiers
+// state that, within one iteration, the three stages and the two P buffers are distinct, so LDS
+// reads need not wait for the DMA.
 template <int D, int NW, bool PW>
 __device__ __forceinline__ void dkdv_step(const uint16_t* __restrict__ curp,
                                           const uint16_t* __restrict__ curs,
                                           uint16_t* __restrict__ nxt, uint16_t* __restrict__ pw,
                                           const uint16_t* __restrict__ pr, bool issue_next,
                                           bool on, const uint16_t* qb, const uint16_t* db,
-                                          const float* lseb, const float* delb, int rs, int qt,
-                                          int ka, int kj, int T, int w, float sl2,
-                                          const uint4 (&frag)[D / 16], f32x16 (&acc)[D / 32],
-                                          const LdsOffsets<D>& lo,
+                                          const float* lseb, const float* delb, int rs, int qt_p,
+                                          int qt_s, int qt_next, int ka, int kj, int T, int w,
+                                          float sl2, const uint4 (&frag)[D / 16],
+                                          f32x16 (&acc)[D / 32], const LdsOffsets<D>& lo,
                                           const RowDma<D, NW, kBwdBQ>& dma, int wave, int lane) {
-  if (issue_next) dkdv_issue<D, NW>(dma, qb, db, lseb, delb, rs, qt + 1, T, nxt, wave, lane);
+  if (issue_next) dkdv_issue<D, NW>(dma, qb, db, lseb, delb, rs, qt_next, T, nxt, wave, lane);
   if (!on) return;
   if (PW)
-    dkdv_pwave<D>(curp, pw, qt, ka, kj, T, w, sl2, frag, acc, lo, lane);
+    dkdv_pwave<D>(curp, pw, qt_p, ka, kj, T, w, sl2, frag, acc, lo, lane);
   else
-    dkdv_swave<D>(curs, pr, qt - 1, ka, T, w, frag, acc, lo, lane);
+    dkdv_swave<D>(curs, pr, qt_s, ka, T, w, frag, acc, lo, lane);
 }
 
-// The tile loop of one role.  Both roles pass the same barriers in the same order; each role gets
-// its own copy of the loop so that its accumulators stay in one set of registers.
-// Iteration i: P waves on tile qt_begin + i (stage i % 3), dS waves on tile qt_begin + i - 1.
+// The tile loop of one role over query tiles qt_hi down to qt_lo (stage 0 holds tile qt_hi on
+// entry).  Both roles pass the same barriers in the same order; each role gets its own copy of the
+// loop so that its accumulators stay in one set of registers.  Iteration i: P waves on tile
+// qt_hi - i (stage i % 3), dS waves on tile qt_hi - i + 1.
 template <int D, int NW, bool PW>
-__device__ __forceinline__ void dkdv_loop(uint16_t* smem, uint16_t* myP, int qt_begin, int n,
+__device__ __forceinline__ void dkdv_loop(uint16_t* smem, uint16_t* myP, int qt_lo, int qt_hi,
                                           const uint16_t* qb, const uint16_t* db,
                                           const float* lseb, const float* delb, int rs, int ka,
                                           int kj, int T, int w, float sl2,
                                           const uint4 (&frag)[D / 16], f32x16 (&acc)[D / 32],
                                           const LdsOffsets<D>& lo,
                                           const RowDma<D, NW, kBwdBQ>& dma, int wave, int lane) {
-  constexpr int NS = kDkdvStages, SE = DkdvStage<D>::ELEMS, PE = DkdvStage<D>::PELEMS;
+  constexpr int SE = DkdvStage<D>::ELEMS, PE = DkdvStage<D>::PELEMS;
+  const int n = qt_hi - qt_lo + 1;
+  int s0 = 0, s1 = 2 * SE, s2 = SE;  // element offsets of stages i % 3, (i - 1) % 3, (i + 1) % 3
   for (int i = 0; i <= n; ++i) {
     wait_vmcnt<0>();  // tile i (the only DMA in flight) has landed
     __syncthreads();  // ... for all waves; P of tile i - 1 is complete; stage (i + 1) % 3 is free
-    dkdv_step<D, NW, PW>(smem + (i % NS) * SE, smem + ((i + NS - 1) % NS) * SE,
-                         smem + ((i + 1) % NS) * SE, myP + (i & 1) * PE,
-                         myP + ((i + 1) & 1) * PE, i + 1 < n, PW ? (i < n) : (i >= 1), qb, db,
-                         lseb, delb, rs, qt_begin + i, ka, kj, T, w, sl2, frag, acc, lo, dma,
-                         wave, lane);
+    const int pb = (i & 1) * PE;
+    const int qt = qt_hi - i;
+    dkdv_step<D, NW, PW>(smem + s0, smem + s1, smem + s2, myP + pb, myP + (PE - pb), i + 1 < n,
+                         PW ? (i < n) : (i >= 1), qb, db, lseb, delb, rs, qt, qt + 1, qt - 1, ka,
+                         kj, T, w, sl2, frag, acc, lo, dma, wave, lane);
+    const int t = s1;  // rotate: the stage just read one behind becomes the next DMA target
+    s1 = s0;
+    s0 = s2;
+    s2 = t;
   }
 }
 
+// One job: key tile kt (128 keys) of head bh, walking the query tiles that see it from the last
+// one down.  Returns with every wave past its last read of the ring and the P buffers.
 template <int D>
-__global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs p) {
-  constexpr int NW = kDkdvWaves, NS = kDkdvStages, BK = 128, BQ = kBwdBQ;
-  constexpr int DK = D / 16, MB = D / 32, SE = DkdvStage<D>::ELEMS, PE = DkdvStage<D>::PELEMS;
-
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * SE];
-  __shared__ __attribute__((aligned(16))) uint16_t sPbuf[2 * PE];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+__device__ __forceinline__ void dkdv_job(const BwdArgs& p, int bh, int kt, uint16_t* smem,
+                                         uint16_t* sPbuf, int wave, int lane) {
+  constexpr int NW = kDkdvWaves, BK = 128, BQ = kBwdBQ;
+  constexpr int DK = D / 16, MB = D / 32, PE = DkdvStage<D>::PELEMS;
   const int half = lane >> 5, l32 = lane & 31;
   const bool pwave = wave < 4;
   const int kblk = wave & 3;
 
-  const int bid = blockIdx.x;
-  const int kt = bid / p.BH;  // key tiles nearest the start see the most queries: first
-  const int bh = bid % p.BH;
   const int b = bh / p.H, h = bh % p.H;
   const int T = p.T;
   const int k0 = kt * BK;
   const int w = min(p.window, T);
   const int q_last = min(T, k0 + BK - 1 + w) - 1;
-  const int qt_begin = k0 / BQ, qt_end = q_last / BQ;
+  const int qt_lo = k0 / BQ, qt_hi = q_last / BQ;
 
   const int64_t base = (int64_t)b * p.bstride + h * D;
   const int rs = p.row_stride;
@@ -398,7 +432,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs p)
   const float* delb = p.delta + (int64_t)bh * T;
 
   const RowDma<D, NW, BQ> dma(rs, wave, lane);
-  dkdv_issue<D, NW>(dma, qb, db, lseb, delb, rs, qt_begin, T, smem, wave, lane);
+  dkdv_issue<D, NW>(dma, qb, db, lseb, delb, rs, qt_hi, T, smem, wave, lane);
 
   const int ka = k0 + 32 * kblk;
   const int kj = ka + l32;
@@ -418,12 +452,11 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs p)
 
   const LdsOffsets<D> lo(lane);
   uint16_t* myP = sPbuf + kblk * (PE / 4);  // this key block's part of each P buffer
-  const int n = qt_end - qt_begin + 1;
   if (pwave)
-    dkdv_loop<D, NW, true>(smem, myP, qt_begin, n, qb, db, lseb, delb, rs, ka, kj, T, w,
+    dkdv_loop<D, NW, true>(smem, myP, qt_lo, qt_hi, qb, db, lseb, delb, rs, ka, kj, T, w,
                            p.scale_log2, frag, acc, lo, dma, wave, lane);
   else
-    dkdv_loop<D, NW, false>(smem, myP, qt_begin, n, qb, db, lseb, delb, rs, ka, kj, T, w,
+    dkdv_loop<D, NW, false>(smem, myP, qt_lo, qt_hi, qb, db, lseb, delb, rs, ka, kj, T, w,
                             p.scale_log2, frag, acc, lo, dma, wave, lane);
 
   if (!kvalid) return;
@@ -440,13 +473,45 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs p)
     }
 }
 
+// Full-causal training pass (p.paired): workgroup = head + key-tile pair (n - 1 - j, j), the short
+// tile (fewest queries) first, so that a head's workgroups start on the same query tiles together
+// (pair_job).  Otherwise: workgroup = one key tile, those seeing the most queries first.
+template <int D>
+__global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs p) {
+  constexpr int SE = DkdvStage<D>::ELEMS, PE = DkdvStage<D>::PELEMS;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[kDkdvStages * SE];
+  __shared__ __attribute__((aligned(16))) uint16_t sPbuf[2 * PE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bid = blockIdx.x;
+  int bh, kt0, kt1, njobs;
+  if (p.paired) {
+    const PairJob jb = pair_job(bid, p.BH, (p.n_tiles + 1) / 2);
+    bh = jb.bh;
+    kt0 = p.n_tiles - 1 - jb.j;
+    kt1 = jb.j;
+    njobs = kt1 != kt0 ? 2 : 1;
+  } else {
+    bh = bid % p.BH;
+    kt0 = kt1 = bid / p.BH;
+    njobs = 1;
+  }
+#pragma unroll 1
+  for (int jx = 0; jx < njobs; ++jx) {
+    if (jx) __syncthreads();  // every wave is done with the ring and P before the next job
+    dkdv_job<D>(p, bh, jx ? kt1 : kt0, smem, sPbuf, wave, lane);
+  }
+}
+
 // ------------------------------------------------------------------------------------- launchers
 template <int D>
 static hipError_t launch_dq_d(const BwdArgs& a, hipStream_t s) {
   constexpr int NW = 4;
   BwdArgs p = a;
   p.n_tiles = (p.T + 32 * NW - 1) / (32 * NW);
-  const unsigned grid = (unsigned)p.n_tiles * (unsigned)p.BH;
+  p.paired = p.window >= p.T ? 1 : 0;  // tile pairs carry equal work under the full causal mask
+  const unsigned per_head = p.paired ? (unsigned)(p.n_tiles + 1) / 2 : (unsigned)p.n_tiles;
+  const unsigned grid = per_head * (unsigned)p.BH;
   hipLaunchKernelGGL((bwd_dq_kernel<D, NW>), dim3(grid), dim3(64 * NW), 0, s, p);
   return hipGetLastError();
 }
@@ -454,8 +519,10 @@ static hipError_t launch_dq_d(const BwdArgs& a, hipStream_t s) {
 template <int D>
 static hipError_t launch_dkdv_d(const BwdArgs& a, hipStream_t s) {
   BwdArgs p = a;
-  p.n_tiles = (p.T + 127) / 128;  // 128 keys per workgroup
-  const unsigned grid = (unsigned)p.n_tiles * (unsigned)p.BH;
+  p.n_tiles = (p.T + 127) / 128;  // 128 keys per job
+  p.paired = p.window >= p.T ? 1 : 0;  // tile pairs carry equal work under the full causal mask
+  const unsigned per_head = p.paired ? (unsigned)(p.n_tiles + 1) / 2 : (unsigned)p.n_tiles;
+  const unsigned grid = per_head * (unsigned)p.BH;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(grid), dim3(64 * kDkdvWaves), 0, s, p);
   return hipGetLastError();
 }

@@ -295,35 +295,65 @@ __device__ __forceinline__ uint4 tr_frag(const uint16_t* tile, int row0, int mb,
 //             multiple of 16) as a constant.
 template <int D>
 struct LdsOffsets {
-  int rc[D / 16];
-  int tr[D / 32][2];
+  uint32_t rc[D / 16];     // byte offsets
+  uint32_t tr[D / 32][2];  // byte offsets
   __device__ __forceinline__ explicit LdsOffsets(int lane) {
     const int l32 = lane & 31, half = lane >> 5;
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) rc[t] = l32 * D + 8 * swz<D>(l32, 2 * t + half);
+    for (int t = 0; t < D / 16; ++t) rc[t] = 2 * (l32 * D + 8 * swz<D>(l32, 2 * t + half));
     const int g = lane >> 4, j = (lane >> 2) & 3, c = lane & 3, h = g >> 1;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
       const int d = 32 * mb + 16 * (g & 1) + 4 * c;
       const int r1 = 4 * h + j, r2 = r1 + 8;
-      tr[mb][0] = r1 * D + 8 * swz<D>(r1, d >> 3) + (d & 7);
-      tr[mb][1] = r2 * D + 8 * swz<D>(r2, d >> 3) + (d & 7);
+      tr[mb][0] = 2 * (r1 * D + 8 * swz<D>(r1, d >> 3) + (d & 7));
+      tr[mb][1] = 2 * (r2 * D + 8 * swz<D>(r2, d >> 3) + (d & 7));
     }
   }
 };
 
+// Byte address arithmetic on an LDS tile: the per-lane offset is one VGPR add onto the (scalar)
+// tile base, and block offsets that are compile-time constants fold into the instruction.
+__device__ __forceinline__ const char* lds_at(const uint16_t* tile, uint32_t lane_off,
+                                              int const_bytes) {
+  return reinterpret_cast<const char*>(tile) + lane_off + const_bytes;
+}
+
 template <int D>
 __device__ __forceinline__ uint4 rc_frag(const uint16_t* tile, const LdsOffsets<D>& o, int blk32,
                                          int t) {
-  return *reinterpret_cast<const uint4*>(tile + blk32 * 32 * D + o.rc[t]);
+  return *reinterpret_cast<const uint4*>(lds_at(tile, o.rc[t], blk32 * 32 * D * 2));
 }
 
 template <int D>
 __device__ __forceinline__ uint4 tr_frag_o(const uint16_t* tile, const LdsOffsets<D>& o, int row0,
                                            int mb) {
-  const uint2 lo = lds_tr16(tile + row0 * D + o.tr[mb][0]);
-  const uint2 hi = lds_tr16(tile + row0 * D + o.tr[mb][1]);
+  const uint2 lo = lds_tr16(reinterpret_cast<const uint16_t*>(lds_at(tile, o.tr[mb][0], row0 * D * 2)));
+  const uint2 hi = lds_tr16(reinterpret_cast<const uint16_t*>(lds_at(tile, o.tr[mb][1], row0 * D * 2)));
   return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+// Workgroup schedule for full-causal training passes, where the work of tile t of a head grows
+// (or shrinks) linearly with t: workgroup g owns the tile pair (j, n - 1 - j) of one head, so all
+// workgroups carry equal work and the launch ends without a tail.  Workgroups are handed to the
+// chip's 8 XCDs round-robin by index; the index -> (head, j) map gives each XCD a contiguous run of
+// heads with j fastest, so a head's workgroups run at the same time on one XCD and share its L2.
+constexpr int kXcds = 8;
+
+struct PairJob {
+  int bh;   // head (batch * H + h)
+  int j;    // pair index: tiles j and n - 1 - j
+};
+
+__device__ __forceinline__ PairJob pair_job(int bid, int BH, int npair) {
+  const int G = BH * npair;
+  const int x = bid % kXcds, n = bid / kXcds;
+  const int q = G / kXcds, r = G % kXcds;
+  const int lin = x * q + min(x, r) + n;  // XCD x owns [x q + min(x, r), +q + (x < r))
+  PairJob jb;
+  jb.bh = lin / npair;
+  jb.j = lin % npair;
+  return jb;
 }
 
 }  // namespace swattn

@@ -196,8 +196,12 @@ __device__ __forceinline__ void fwd_run(int kt0, int kt1, int kt_end, int& st, u
   constexpr int TILE = kFwdBC * D;
   constexpr int LOADS = 2 * (kFwdBC * D / 512) / NW;  // global_load_lds per wave per tile
   for (int kt = kt0; kt < kt1; ++kt) {
-    // tile kt has landed once at most the (NS - 2) younger tiles' DMA is still in flight
-    if (NS == 3 && kt < kt_end) wait_vmcnt<LOADS>(); else wait_vmcnt<0>();
+    // tile kt has landed once at most the younger tiles' DMA (up to NS - 2 of them) is in flight
+    static_assert(NS >= 2 && NS <= 4, "ring depth");
+    const int younger = min(NS - 2, kt_end - kt);
+    if (NS == 4 && younger >= 2) wait_vmcnt<2 * LOADS>();
+    else if (NS >= 3 && younger >= 1) wait_vmcnt<LOADS>();
+    else wait_vmcnt<0>();
     __syncthreads();  // ... for every wave; and every wave is done with the stage refilled next
     const int nx = (st + NS - 1) % NS;
     fwd_step<D, NW, MASK>(smem + st * 2 * TILE, smem + nx * 2 * TILE, kt + NS - 1 <= kt_end,
@@ -207,25 +211,17 @@ __device__ __forceinline__ void fwd_run(int kt0, int kt1, int kt_end, int& st, u
   }
 }
 
-// NW waves x 32 queries per workgroup, NS-stage K/V ring (prefetch NS - 1 tiles ahead).
+// One job: query tile qt (NW waves x 32 queries) of head bh, NS-stage K/V ring (prefetch NS - 1
+// tiles ahead).  Returns with every wave past its last read of the ring.
 template <int D, int NW, int NS>
-__global__ __launch_bounds__(64 * NW, (NW >= 8 ? 1 : 2)) void fwd_bf16_kernel(FwdArgs p) {
+__device__ __forceinline__ void fwd_job(const FwdArgs& p, int bh, int qt, uint16_t* smem,
+                                        int wave, int lane) {
   constexpr int BR = 32 * NW;
   constexpr int BC = kFwdBC;
   constexpr int DK = D / 16;  // MFMA k-steps over D
   constexpr int MB = D / 32;  // 32-row blocks of O^T
   constexpr int TILE = BC * D;
-  static_assert((BC * D / 512) % NW == 0, "every wave issues the same number of DMA loads");
-
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * 2 * TILE];  // [stage][K|V]
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
-
-  const int bid = blockIdx.x;
-  const int qt = p.n_qtiles - 1 - bid / p.BH;  // longest query tiles first
-  const int bh = bid % p.BH;
   const int b = bh / p.H, h = bh % p.H;
 
   int L = p.kv_len;
@@ -301,6 +297,30 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 1 : 2)) void fwd_bf16_kernel(Fw
     }
   if (p.lse && half == 0)
     p.lse[(int64_t)bh * p.lse_T + qi] = (S.m_use + __log2f(l_tot)) * kLn2;
+}
+
+// PAIRED (full-causal training forward): workgroup = head + query-tile pair (j, n - 1 - j), the
+// short tile first, so that a head's workgroups start on the same K/V tiles together (pair_job).
+// Otherwise (prefill, sliding window): workgroup = one query tile, longest tiles first.
+template <int D, int NW, int NS, bool PAIRED>
+__global__ __launch_bounds__(64 * NW, (NW >= 8 ? 1 : 2)) void fwd_bf16_kernel(FwdArgs p) {
+  static_assert((kFwdBC * D / 512) % NW == 0, "every wave issues the same number of DMA loads");
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * 2 * kFwdBC * D];  // [stage][K|V]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bid = blockIdx.x;
+  if (PAIRED) {
+    const PairJob jb = pair_job(bid, p.BH, (p.n_qtiles + 1) / 2);
+    const int qt1 = p.n_qtiles - 1 - jb.j;
+    fwd_job<D, NW, NS>(p, jb.bh, jb.j, smem, wave, lane);
+    if (qt1 != jb.j) {
+      __syncthreads();  // every wave is done with the ring before the next job refills it
+      fwd_job<D, NW, NS>(p, jb.bh, qt1, smem, wave, lane);
+    }
+  } else {
+    fwd_job<D, NW, NS>(p, bid % p.BH, p.n_qtiles - 1 - bid / p.BH, smem, wave, lane);
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -418,8 +438,14 @@ template <int D, int NW, int NS>
 static hipError_t launch_bf16(const FwdArgs& a, hipStream_t s) {
   FwdArgs p = a;
   p.n_qtiles = (p.T + 32 * NW - 1) / (32 * NW);
-  const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.BH;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS>), dim3(grid), dim3(64 * NW), 0, s, p);
+  // tile pairs carry equal work only when every query sees all earlier keys
+  if (p.lens == nullptr && p.window >= p.T && p.kv_len == p.T) {
+    const unsigned grid = (unsigned)(p.n_qtiles + 1) / 2 * (unsigned)p.BH;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, true>), dim3(grid), dim3(64 * NW), 0, s, p);
+  } else {
+    const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.BH;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, false>), dim3(grid), dim3(64 * NW), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -40,6 +40,7 @@ struct BwdArgs {
   int row_stride;    // H * D
   int H, BH, D, T, window;
   int n_tiles;       // filled by the launcher
+  int paired;        // filled by the launcher: full-causal training schedule (tile pairs)
   float scale;       // 1 / sqrt(D)
   float scale_log2;  // log2(e) / sqrt(D)
 };
