@@ -61,18 +61,20 @@ __device__ __forceinline__ void dq_tile(const uint16_t* __restrict__ sK,
       s = mfma32(rc_frag<D>(sK, lo, nb, t), qf[t], s);
       dp = mfma32(rc_frag<D>(sV, lo, nb, t), df[t], dp);
     }
+    sched_mfma_chain<2 * DK, 1, 8>();
     const int d0 = qi - (k_lo + nb * 32) - 4 * half;
     if (mask)
       dq_ds<true>(s, dp, d0, w, sl2, lse2, delta);
     else
       dq_ds<false>(s, dp, d0, w, sl2, lse2, delta);
+    const uint4 dsf[2] = {pack_frag(s, 0), pack_frag(s, 1)};
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint4 dsf = pack_frag(s, u);
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int m = 0; m < MB; ++m)
-        dqacc[m] = mfma32(tr_frag_o<D>(sK, lo, nb * 32 + 16 * u, m), dsf, dqacc[m]);
-    }
+        dqacc[m] = mfma32(tr_frag_o<D>(sK, lo, nb * 32 + 16 * u, m), dsf[u], dqacc[m]);
+    sched_mfma_chain<2 * MB, 2, 4>();
   }
 }
 
@@ -294,6 +296,7 @@ __device__ __forceinline__ void dkdv_pwave(const uint16_t* __restrict__ cur,
     f32x16 acc = zero16();
 #pragma unroll
     for (int t = 0; t < DK; ++t) acc = mfma32(rc_frag<D>(sQ, lo, qb2, t), kf[t], acc);
+    sched_mfma_chain<DK, 1, DK>();
     const int qs = qt * BQ + 32 * qb2, qz = qs + 31, kz = ka + 31;
     if (qs >= kz && qz - ka < w && qz < T)
       dkdv_probs<false>(acc, sL, qb2, qt, kj, T, w, sl2, half);
@@ -303,11 +306,13 @@ __device__ __forceinline__ void dkdv_pwave(const uint16_t* __restrict__ cur,
     uint4* dst = reinterpret_cast<uint4*>(sP) + qb2 * 2 * 64;
     dst[lane] = pf0;
     dst[64 + lane] = pf1;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
       dvacc[m] = mfma32(tr_frag_o<D>(sO, lo, 32 * qb2, m), pf0, dvacc[m]);
       dvacc[m] = mfma32(tr_frag_o<D>(sO, lo, 32 * qb2 + 16, m), pf1, dvacc[m]);
     }
+    sched_mfma_chain<2 * MB, 2, 4>();
   }
 }
 
@@ -329,6 +334,7 @@ __device__ __forceinline__ void dkdv_swave(const uint16_t* __restrict__ cur,
     f32x16 dp = zero16();
 #pragma unroll
     for (int t = 0; t < DK; ++t) dp = mfma32(rc_frag<D>(sO, lo, qb2, t), vf[t], dp);
+    sched_mfma_chain<DK, 1, DK>();
     const uint4* src = reinterpret_cast<const uint4*>(sP) + qb2 * 2 * 64;
     const uint4 pw[2] = {src[lane], src[64 + lane]};
     const uint32_t* pu = reinterpret_cast<const uint32_t*>(pw);
@@ -345,11 +351,13 @@ __device__ __forceinline__ void dkdv_swave(const uint16_t* __restrict__ cur,
       }
     }
     const uint4 df0 = pack_frag(dp, 0), df1 = pack_frag(dp, 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
       dkacc[m] = mfma32(tr_frag_o<D>(sQ, lo, 32 * qb2, m), df0, dkacc[m]);
       dkacc[m] = mfma32(tr_frag_o<D>(sQ, lo, 32 * qb2 + 16, m), df1, dkacc[m]);
     }
+    sched_mfma_chain<2 * MB, 2, 4>();
   }
 }
 

@@ -333,6 +333,22 @@ __device__ __forceinline__ uint4 tr_frag_o(const uint16_t* tile, const LdsOffset
   return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
+// Scheduling pin for a chain of N MFMAs that each take R LDS reads (written just above the call):
+// the reads of the first A MFMAs issue first, then each MFMA is followed by the reads of the MFMA
+// A places later, so LDS latency hides under A MFMAs instead of stalling each one.  The
+// sched_barrier stops later code from being mixed into the pattern.
+template <int N, int R, int A>
+__device__ __forceinline__ void sched_mfma_chain() {
+  static_assert(A >= 1 && A <= N, "lookahead");
+  __builtin_amdgcn_sched_group_barrier(0x100, R * A, 0);  // DS reads
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if (i + A < N) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Workgroup schedule for full-causal training passes, where the work of tile t of a head grows
 // (or shrinks) linearly with t: workgroup g owns the tile pair (j, n - 1 - j) of one head, so all
 // workgroups carry equal work and the launch ends without a tail.  Workgroups are handed to the

@@ -133,6 +133,7 @@ __device__ __forceinline__ void fwd_tile_s(const uint16_t* __restrict__ sK, int 
     s0 = mfma32(rc_frag<D>(sK, lo, 0, t), qf[t], s0);
     s1 = mfma32(rc_frag<D>(sK, lo, 1, t), qf[t], s1);
   }
+  sched_mfma_chain<2 * DK, 1, 8>();
   fwd_tile_max<D, MASK>(s0, s1, k_lo, qi, w, lane >> 5, sl2, S);
 }
 
@@ -202,7 +203,8 @@ __device__ __forceinline__ void fwd_run(int kt0, int kt1, int kt_end, int& st, u
     if (NS == 4 && younger >= 2) wait_vmcnt<2 * LOADS>();
     else if (NS >= 3 && younger >= 1) wait_vmcnt<LOADS>();
     else wait_vmcnt<0>();
-    __syncthreads();  // ... for every wave; and every wave is done with the stage refilled next
+    lds_barrier();  // ... for every wave (no drain of younger DMA); every wave is done with the
+                    // stage refilled next
     const int nx = (st + NS - 1) % NS;
     fwd_step<D, NW, MASK>(smem + st * 2 * TILE, smem + nx * 2 * TILE, kt + NS - 1 <= kt_end,
                           kt + NS - 1, kb, vb, rs, L, kt, qa, qi, w, sl2, qf, lo, dma, S, wave,
