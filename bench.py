@@ -11,7 +11,8 @@ Every part is bracketed by HIP events on the stream the kernels run on.
 
 The headline ``value`` is the d20 fwd+bwd rate in TFLOP/s counting unmasked FLOPs only (4D per
 visible (query, key) pair forward, 10D backward).  ``decode`` reports algorithmic HBM GB/s (every
-visible cache row read once, plus q and o), ``prefill`` TFLOP/s.  ``roofline`` describes the
+visible cache row read once, plus q and o), next to a plain streaming read of the same byte count
+(the rate this GPU sustains at that size); ``prefill`` TFLOP/s.  ``roofline`` describes the
 longest-running MFMA kernel; ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
 d20 workload on the host cores.  One JSON line goes to stdout; progress goes to stderr.
 """
@@ -49,6 +50,41 @@ def kernel_source_hash() -> str:
     for f in sorted(glob.glob(os.path.join(ROOT, "causal_sliding_window_attn_amd", "csrc", "*"))):
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
+
+
+def stream_read_gbs(bufs, nbytes: int, reps: int = 3) -> float:
+    """GB/s of a plain streaming read of nbytes per call (libswattn_probe.so), one call per
+    buffer in turn so that no call finds its bytes in the last-level cache."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "causal_sliding_window_attn_amd", "libswattn_probe.so"))
+    lib.swattn_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                       ctypes.c_int, ctypes.c_void_p]
+    lib.swattn_stream_read.restype = ctypes.c_int
+    blocks = 1024
+    out = torch.empty(blocks * 256, dtype=torch.int32, device=bufs[0].device)
+    st = torch.cuda.current_stream()
+    nbytes = nbytes // 16 * 16
+
+    def run():
+        for b in bufs:
+            assert b.numel() * b.element_size() >= nbytes
+            rc = lib.swattn_stream_read(b.data_ptr(), nbytes, out.data_ptr(), blocks,
+                                        ctypes.c_void_p(st.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"swattn_stream_read failed ({rc})")
+
+    run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / (reps * len(bufs))
+    return nbytes / t / 1e9
 
 
 def cpu_baseline(case, q, k, v, do, n_heads: int):
@@ -89,6 +125,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-heads", type=int, default=320)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stream-ref", action="store_true",
+                    help="skip the streaming-read reference of the decode roofline")
     ap.add_argument("--calib-copy-mib", type=int, default=1024,
                     help="after the timed region, one plain device copy of this size (the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -245,6 +283,12 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    # streaming-read reference: a plain read of the decode step's byte count, rotating over the
+    # 30 layers' key caches (each larger than the last-level cache), outside the timed region
+    stream_ref = None
+    if not args.no_stream_ref:
+        stream_ref = stream_read_gbs(kcache, int(dec_bytes / E.n_layer))
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_heads} heads ...")
@@ -276,7 +320,9 @@ def main() -> int:
                 "ms_dq": round(t_dq * 1e3, 4), "ms_dkdv": round(t_dkdv * 1e3, 4)},
         "decode": {"GB/s": round(dec_gbs, 1), "frac_of_hbm_peak": round(dec_gbs / PEAK_HBM, 4),
                    "us_per_layer_step": round(t_dec / E.n_layer * 1e6, 2),
-                   "bytes_per_layer_step": round(dec_bytes / E.n_layer)},
+                   "bytes_per_layer_step": round(dec_bytes / E.n_layer),
+                   "stream_read_ref_GB/s": stream_ref and round(stream_ref, 1),
+                   "frac_of_stream_read_ref": stream_ref and round(dec_gbs / stream_ref, 4)},
         "prefill": {"TFLOP/s": round(pre_flops / t_pre / 1e12, 2), "ms_per_layer": round(t_pre * 1e3, 4)},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -13,6 +13,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libswattn.so")
 SOURCES = ["api.cpp", "fwd.hip", "bwd.hip", "decode.hip"]
+# measurement helper used by bench.py only (streaming-read reference for the decode roofline)
+PROBE_LIB = os.path.join(PKG, "libswattn_probe.so")
+PROBE_SOURCES = ["stream_probe.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are switched off for all device code; hipcc's host pass warns that it
@@ -48,18 +51,25 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(extra: list[str] | None = None) -> str:
-    """Compile every source for gfx950 and link libswattn.so next to this file.  Returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    extra = list(extra or [])
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list[str], lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(extra: list[str] | None = None) -> str:
+    """Compile every source for gfx950 and link libswattn.so (and the bench's streaming-read probe
+    library) next to this file.  Returns the path of libswattn.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    extra = list(extra or [])
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, extra), srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     return LIB
 
 
