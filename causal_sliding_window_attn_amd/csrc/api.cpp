@@ -109,7 +109,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 
 size_t attn_bwd_workspace_bytes(int B, int H, int T, int D) {
   if (B < 1 || H < 1 || T < 1 || (D != 64 && D != 128)) return 0;
-  return align256((size_t)B * H * T * sizeof(float));
+  return 2 * align256((size_t)B * H * T * sizeof(float));  // Delta, then LSE in base 2
 }
 
 }  // extern "C"
@@ -152,6 +152,7 @@ int bwd_common(const char* what, BwdPass pass, const void* q, const void* k, con
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
   a.delta = static_cast<float*>(ws);
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + need / 2);
   a.bstride = (int64_t)T * H * D;
   a.row_stride = H * D;
   a.H = H;

@@ -154,7 +154,10 @@ __device__ __forceinline__ void dq_job(const BwdArgs& p, int bh, int qt, uint16_
     dsum = 0.f;
   }
   const float delta = sum_with_partner(dsum);
-  if (qvalid && half == 0) p.delta[(int64_t)bh * T + qi] = delta;
+  if (qvalid && half == 0) {
+    p.delta[(int64_t)bh * T + qi] = delta;
+    p.lse2[(int64_t)bh * T + qi] = lse_raw * kLog2e;  // the dK/dV pass reads LSE in base 2
+  }
   const float lse2 = qvalid ? lse_raw * kLog2e : 0.f;
 
   f32x16 dqacc[MB];
@@ -249,7 +252,8 @@ __device__ __forceinline__ void dkdv_issue(const RowDma<D, NW, kBwdBQ>& dma, con
   }
 }
 
-// P = exp2(S * scale - LSE) for one 32-query block (lane = key kj, accumulator r = query row).
+// P = exp2(S * scale * log2(e) - LSE * log2(e)) for one 32-query block (lane = key kj,
+// accumulator r = query row); sL holds the rows' LSE already in base 2.
 template <bool MASK>
 __device__ __forceinline__ void dkdv_probs(f32x16& acc, const float* sL, int qb2, int qt, int kj,
                                            int T, int w, float sl2, int half) {
@@ -262,7 +266,7 @@ __device__ __forceinline__ void dkdv_probs(f32x16& acc, const float* sL, int qb2
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * j + i;
-      float pr = __builtin_amdgcn_exp2f(fmaf(acc[r], sl2, -lv[i] * kLog2e));
+      float pr = __builtin_amdgcn_exp2f(fmaf(acc[r], sl2, -lv[i]));
       if (MASK) {
         // query i sees key j iff (unsigned)(i - j) < w; rows past T hold a clamped copy: drop them
         const int qg = qt * BQ + ql0 + i;
@@ -436,7 +440,7 @@ __device__ __forceinline__ void dkdv_job(const BwdArgs& p, int bh, int kt, uint1
   const int rs = p.row_stride;
   const uint16_t* qb = p.q + base;
   const uint16_t* db = p.dout + base;
-  const float* lseb = p.lse + (int64_t)bh * T;
+  const float* lseb = p.lse2 + (int64_t)bh * T;  // LSE * log2(e), from the dQ pass
   const float* delb = p.delta + (int64_t)bh * T;
 
   const RowDma<D, NW, BQ> dma(rs, wave, lane);

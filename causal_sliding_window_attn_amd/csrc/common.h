@@ -60,17 +60,18 @@ __device__ __forceinline__ uint4 pack_frag(const f32x16& acc, int u) {
   return r;
 }
 
-// Eight fp32 values -> two bf16x8 fragments hi + lo with hi = bf16(x) and lo = bf16(x - hi), so
-// hi + lo carries x to about 2^-17 relative (one bf16 alone keeps only 2^-9).
+// Eight fp32 values -> two bf16x8 fragments hi + lo with hi = x truncated to bf16 (one v_perm per
+// pair) and lo = bf16(x - hi): x - hi is exact in fp32, so hi + lo carries x to about 2^-16
+// relative (one bf16 alone keeps only 2^-9).
 __device__ __forceinline__ void pack_frag_split(const f32x16& acc, int u, uint4& hi, uint4& lo) {
   uint32_t* h = reinterpret_cast<uint32_t*>(&hi);
   uint32_t* l = reinterpret_cast<uint32_t*>(&lo);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const float a = acc[8 * u + 2 * e], b = acc[8 * u + 2 * e + 1];
-    const uint32_t w = pack_bf16x2(a, b);
-    h[e] = w;
-    l[e] = pack_bf16x2(a - __uint_as_float(w << 16), b - __uint_as_float(w & 0xffff0000u));
+    const uint32_t ab = __float_as_uint(a), bb = __float_as_uint(b);
+    h[e] = __builtin_amdgcn_perm(bb, ab, 0x07060302u);  // upper halves of a (low) and b (high)
+    l[e] = pack_bf16x2(a - __uint_as_float(ab & 0xffff0000u), b - __uint_as_float(bb & 0xffff0000u));
   }
 }
 

@@ -35,7 +35,8 @@ struct BwdArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* delta;      // [BH, T] workspace
+  float* delta;      // [BH, T] workspace: Delta_i = dO_i . O_i (written by the dQ pass)
+  float* lse2;       // [BH, T] workspace: LSE_i * log2(e) (written by the dQ pass)
   int64_t bstride;   // T * H * D
   int row_stride;    // H * D
   int H, BH, D, T, window;

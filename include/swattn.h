@@ -72,7 +72,8 @@ const char* attn_last_error(void);
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int T,
              int D, int window, int dtype, void* stream);
 
-/* Bytes of device workspace attn_bwd needs (the per-row Delta_i = dO_i . O_i, float32). */
+/* Bytes of device workspace attn_bwd needs: per row, Delta_i = dO_i . O_i and LSE_i * log2(e)
+ * (float32 each), written by the dQ pass and read by the dK/dV pass. */
 size_t attn_bwd_workspace_bytes(int B, int H, int T, int D);
 
 /*
@@ -89,8 +90,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
 /*
  * The two passes of attn_bwd, for callers that schedule or time them separately.  attn_bwd is
  * exactly attn_bwd_dq followed by attn_bwd_dkdv on the same stream with the same arguments.
- *   attn_bwd_dq:   writes Delta_i = dO_i . O_i into ws and dq.
- *   attn_bwd_dkdv: reads Delta from ws as left there by attn_bwd_dq for the same (q, k, v, o, lse,
+ *   attn_bwd_dq:   writes Delta_i = dO_i . O_i and LSE_i * log2(e) into ws, and dq.
+ *   attn_bwd_dkdv: reads both from ws as left there by attn_bwd_dq for the same (q, k, v, o, lse,
  *                  dout, shapes, window) and writes dk, dv.  Called without that, results are
  *                  undefined (but every access stays inside the buffers).
  * Arguments, layouts, validation and status codes are those of attn_bwd.
