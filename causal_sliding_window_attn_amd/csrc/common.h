@@ -253,12 +253,16 @@ struct RowDma {
         g2lds16(reinterpret_cast<const uint16_t*>(b + (int64_t)(k * NW * RPI) * rs2 + o),
                 lds + (wave + k * NW) * 512);
     } else {
+      // the partial tile (at most one per sequence): an opaque copy of the row count keeps its
+      // clamped addresses from being computed speculatively on every full tile as well
+      int last = nvalid - 1;
+      asm volatile("" : "+s"(last));
       const int cp = lane % CPR;
 #pragma unroll
       for (int k = 0; k < PER; ++k) {
         const int r = (wave + k * NW) * RPI + lane / CPR;
-        const int rc = min(r, nvalid - 1);
-        g2lds16(reinterpret_cast<const uint16_t*>(b + (int64_t)rc * rs2 + 16 * swz<D>(r, cp)),
+        const uint32_t rc = (uint32_t)min(r, last);
+        g2lds16(reinterpret_cast<const uint16_t*>(b + rc * (uint32_t)rs2 + 16 * swz<D>(r, cp)),
                 lds + (wave + k * NW) * 512);
       }
     }
