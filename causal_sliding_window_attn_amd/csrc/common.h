@@ -92,61 +92,6 @@ __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// LDS tile layouts for a tile of R sequence rows x D features (bf16).
-//
-// Row-major tile ("normal"): row r, 16-byte chunk c stored at chunk (c ^ (r % (D/8))) of row r,
-// so the 32 rows read by one MFMA operand load fall on distinct banks.
-//
-// Transposed tile: feature d is a row of R sequence positions.  Inside every group of 16 rows the
-// sequence position k is stored at slot perm16(k) = 8 * ((k >> 2) & 1) + 4 * (k >> 3) + (k & 3),
-// so the 8 positions one lane half feeds to an MFMA sit in one 16-byte chunk; chunk index is
-// XOR-swizzled with (d % 8).
-// ---------------------------------------------------------------------------------------------
-template <int D>
-__device__ __forceinline__ int normal_off(int row, int chunk) {
-  return row * D + 8 * (chunk ^ (row & (D / 8 - 1)));
-}
-
-template <int R>
-__device__ __forceinline__ int trans_off(int d, int chunk) {
-  return d * R + 8 * (chunk ^ (d & 7));
-}
-
-// Store 4 consecutive sequence rows (4g .. 4g+3) x 8 features (8c .. 8c+7), held as four 16-byte
-// row chunks, into both the normal and (optionally) the transposed LDS tile.
-template <int D, int R, bool NORMAL, bool TRANS>
-__device__ __forceinline__ void store_group(uint16_t* sN, uint16_t* sT, int g, int c,
-                                            const uint4 (&x)[4]) {
-  if (NORMAL) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(sN + normal_off<D>(4 * g + i, c)) = x[i];
-  }
-  if (TRANS) {
-    // Rows 4g..4g+3 occupy 4 consecutive transposed slots: group-of-16 (g / 4), lane half (g & 1),
-    // j' = (g >> 1) & 1.
-    const int chunk = 2 * (g >> 2) + (g & 1);
-    const int sub = ((g >> 1) & 1) * 4;
-    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&x[0]);
-    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&x[1]);
-    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&x[2]);
-    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&x[3]);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      uint2 lo, hi;  // feature 8c + 2e (low halves) and 8c + 2e + 1 (high halves)
-      lo.x = (w0[e] & 0xffffu) | (w1[e] << 16);
-      lo.y = (w2[e] & 0xffffu) | (w3[e] << 16);
-      hi.x = (w0[e] >> 16) | (w1[e] & 0xffff0000u);
-      hi.y = (w2[e] >> 16) | (w3[e] & 0xffff0000u);
-      const int d0 = 8 * c + 2 * e;
-      *reinterpret_cast<uint2*>(sT + trans_off<R>(d0, chunk) + sub) = lo;
-      *reinterpret_cast<uint2*>(sT + trans_off<R>(d0 + 1, chunk) + sub) = hi;
-    }
-  }
-}
-
-
-// ---------------------------------------------------------------------------------------------
 // Direct global -> LDS tile streaming (global_load_lds_dwordx4) and transposed LDS reads
 // (ds_read_b64_tr_b16), with the lane semantics measured on gfx950:
 //   global_load_lds 16 B: lane l's 16 bytes land at (wave-uniform LDS base) + 16 * l.
@@ -269,35 +214,15 @@ struct RowDma {
   }
 };
 
-// The 16-byte row chunk c (features 8c .. 8c+7) of row r of a swizzled tile.
-template <int D>
-__device__ __forceinline__ uint4 row_chunk(const uint16_t* tile, int r, int c) {
-  return *reinterpret_cast<const uint4*>(tile + r * D + 8 * swz<D>(r, c));
-}
-
-// One MFMA A fragment of V^T for d-rows 32 * mb .. +32 and the 16 sequence rows starting at
-// `row0`, read from a row-major tile swizzled with swz: slot s of lane (d, half) holds
-// row row0 + 8 * (s / 4) + 4 * half + (s % 4).
-template <int D>
-__device__ __forceinline__ uint4 tr_frag(const uint16_t* tile, int row0, int mb, int lane) {
-  const int g = lane >> 4, j = (lane >> 2) & 3, c = lane & 3, h = g >> 1;
-  const int d = 32 * mb + 16 * (g & 1) + 4 * c;  // first of the 4 features this lane addresses
-  const int r1 = row0 + 4 * h + j, r2 = r1 + 8;
-  const int ch = d >> 3, sub = d & 7;
-  const uint2 lo = lds_tr16(tile + r1 * D + 8 * swz<D>(r1, ch) + sub);
-  const uint2 hi = lds_tr16(tile + r2 * D + 8 * swz<D>(r2, ch) + sub);
-  return make_uint4(lo.x, lo.y, hi.x, hi.y);
-}
-
-
-// Per-lane LDS element offsets for the two fragment reads, precomputed once per kernel.  With the
-// swizzle above, a fragment's address is (tile base) + (per-lane term that depends only on the
-// k-step t or the 32-row block mb) + (a compile-time row offset), so every read in the loop is one
-// VGPR plus an immediate:
-//   rc[t]:    row_chunk of row (l % 32) and chunk (2t + half), for a block whose first row is a
-//             multiple of 32 -- add 32 * D * (block) as a constant;
-//   tr[mb][e]: the two 8-byte transposed reads of tr_frag for row0 = 0 -- add row0 * D (row0 a
-//             multiple of 16) as a constant.
+// Per-lane LDS byte offsets of the two kinds of MFMA operand reads from a row-major swizzled tile,
+// computed once per kernel.  A read's address is (tile base) + (this per-lane offset) + (a
+// compile-time row offset), i.e. one VGPR add plus an immediate:
+//   rc[t]:     the 16-byte chunk (2t + half) of row (l % 32) -- an A or B fragment over D for
+//              k-step t; add 32 * D * 2 bytes per 32-row block;
+//   tr[mb][e]: the two ds_read_b64_tr_b16 reads that assemble an A fragment of the transposed tile
+//              (feature rows 32 mb .. +32, 16 sequence rows): slot s of lane (d, half) receives
+//              sequence row 8 (s / 4) + 4 half + (s % 4); add row0 * D * 2 bytes for the 16-row
+//              step starting at row0.
 template <int D>
 struct LdsOffsets {
   uint32_t rc[D / 16];     // byte offsets
