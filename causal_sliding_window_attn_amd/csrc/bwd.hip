@@ -53,7 +53,7 @@ __device__ __forceinline__ void dq_tile(const uint16_t* __restrict__ sK,
                                         int lane) {
   constexpr int BC = kBwdBC, DK = D / 16, MB = D / 32, NB = BC / 32;
   const int half = lane >> 5;
-#pragma unroll 1
+#pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     f32x16 s = zero16(), dp = zero16();
 #pragma unroll
@@ -165,14 +165,26 @@ __device__ __forceinline__ void dq_job(const BwdArgs& p, int bh, int qt, uint16_
   for (int m = 0; m < MB; ++m) dqacc[m] = zero16();
 
   const LdsOffsets<D> lo(lane);
+  // two tiles per trip, so that each stage's LDS base is a compile-time constant and every
+  // operand read is the lane's offset plus an immediate
   uint16_t* stage0 = smem;
   uint16_t* stage1 = smem + 2 * TILE;
-  for (int kt = kt_begin; kt <= kt_end; ++kt) {
+  int kt = kt_begin;
+  for (; kt < kt_end; kt += 2) {
     wait_vmcnt<0>();
     __syncthreads();
-    const bool even = ((kt - kt_begin) & 1) == 0;
-    dq_step<D, NW>(even ? stage0 : stage1, even ? stage1 : stage0, kt < kt_end, kb, vb, rs, T, kt,
-                   qa, qi, w, p.scale_log2, lse2, delta, qf, df, lo, dqacc, wave, lane);
+    dq_step<D, NW>(stage0, stage1, true, kb, vb, rs, T, kt, qa, qi, w, p.scale_log2, lse2, delta,
+                   qf, df, lo, dqacc, wave, lane);
+    wait_vmcnt<0>();
+    __syncthreads();
+    dq_step<D, NW>(stage1, stage0, kt + 1 < kt_end, kb, vb, rs, T, kt + 1, qa, qi, w,
+                   p.scale_log2, lse2, delta, qf, df, lo, dqacc, wave, lane);
+  }
+  if (kt == kt_end) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    dq_step<D, NW>(stage0, stage1, false, kb, vb, rs, T, kt, qa, qi, w, p.scale_log2, lse2, delta,
+                   qf, df, lo, dqacc, wave, lane);
   }
 
   if (!qvalid) return;
