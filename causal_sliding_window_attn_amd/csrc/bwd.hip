@@ -9,14 +9,16 @@
 //   dQ_i = sum_j dS_ij k_j / sqrt(D),  dK_j = sum_i dS_ij q_i / sqrt(D),  dV_j = sum_i P_ij dO_i.
 //
 // dQ pass: a workgroup owns NW x 32 queries (Q, dO in registers as B fragments, lane = query as in
-// the forward), computes Delta for them first and writes it to the workspace, then walks the
-// in-window key tiles: S^T = K Q^T, dP^T = V dO^T, dS^T, and dQ^T += K^T dS^T.
-// dK/dV pass: a workgroup owns 128 keys and walks the query tiles that can see them; half of its
-// waves compute S = Q K^T, P and dV^T += dO^T P, the other half, one tile behind, dP = dO V^T, dS
-// and dK^T += Q^T dS, taking P through LDS (lane = key in both).
-// Both passes stream their tiles global -> LDS with global_load_lds into a two-stage ring (one
-// tile ahead, one barrier per tile) and take every transposed operand (K^T, Q^T, dO^T) straight
-// from the row-major tile with ds_read_b64_tr_b16.
+// the forward), computes Delta and LSE * log2(e) for them first and writes both to the workspace,
+// then walks the in-window key tiles: S^T = K Q^T, dP^T = V dO^T, dS^T, and dQ^T += K^T dS^T.
+// dK/dV pass: a workgroup owns 128 keys and walks the query tiles that can see them, last tile
+// first; half of its waves compute S = Q K^T, P and dV^T += dO^T P, the other half, one tile
+// behind, dP = dO V^T, dS and dK^T += Q^T dS, taking P through LDS (lane = key in both).
+// Under the full causal mask both passes give each workgroup a pair of tiles of equal total work
+// (pair_job).  Tiles stream global -> LDS with global_load_lds, one tile ahead with one barrier per
+// tile: a two-stage K/V ring in the dQ pass, a three-stage Q/dO ring in the dK/dV pass (the dS
+// waves still read the tile before).  Every transposed operand (K^T, Q^T, dO^T) comes straight
+// from the row-major tile through ds_read_b64_tr_b16.
 #include "common.h"
 #include "launch.h"
 

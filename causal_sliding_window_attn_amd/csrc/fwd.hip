@@ -12,10 +12,11 @@
 // lane-local plus one v_permlane32_swap.  O^T = V^T P^T reuses the S^T accumulators directly as the
 // B operand (P split into bf16 hi + lo, two MFMAs on one V fragment); the V^T fragments come from
 // the row-major V tile through ds_read_b64_tr_b16.  K/V tiles stream global -> LDS with
-// global_load_lds into a two-stage ring, one tile ahead of the compute (one barrier per tile).  Tiles outside
-// [q0 - w + 1, q_end] are never loaded; per wave, tiles wholly outside the window are skipped and
-// only tiles crossing the diagonal or the window edge evaluate the mask.  O is rescaled lazily,
-// only when a row maximum grows by more than 2^8.
+// global_load_lds into a two-stage ring, one tile ahead of the compute (one barrier per tile).
+// Tiles outside [q0 - w + 1, q_end] are never loaded; per wave, tiles wholly outside the window
+// are skipped, and only tiles crossing the diagonal or the window edge run the masked loop.  O is
+// rescaled lazily, only when a row maximum grows by more than 2^8.  Under the full causal mask
+// (training) a workgroup owns a pair of query tiles of equal total work (pair_job).
 #include "common.h"
 #include "launch.h"
 
