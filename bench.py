@@ -12,7 +12,9 @@ Every part is bracketed by HIP events on the stream the kernels run on.
 The headline ``value`` is the d20 fwd+bwd rate in TFLOP/s counting unmasked FLOPs only (4D per
 visible (query, key) pair forward, 10D backward).  ``decode`` reports algorithmic HBM GB/s (every
 visible cache row read once, plus q and o), next to a plain streaming read of the same byte count
-(the rate this GPU sustains at that size); ``prefill`` TFLOP/s.  ``roofline`` describes the
+(the rate this GPU sustains at that size), and ``decode.step_graph`` the same decode step for all
+30 layers as one replay of a captured HIP graph (attn_decode_step: append and decode in one launch
+per layer); ``prefill`` TFLOP/s.  ``roofline`` describes the
 longest-running MFMA kernel; ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
 d20 workload on the host cores.  One JSON line goes to stdout; progress goes to stderr.
 """
@@ -127,6 +129,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-ref", action="store_true",
                     help="skip the streaming-read reference of the decode roofline")
+    ap.add_argument("--no-step-graph", action="store_true",
+                    help="skip the graph-replayed whole-model decode step measurement")
     ap.add_argument("--calib-copy-mib", type=int, default=1024,
                     help="after the timed region, one plain device copy of this size (the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -170,10 +174,16 @@ def main() -> int:
     Tq = int(lens0.max())
     log(f"allocating Engine caches: {E.n_layer} layers x 2 x {E.B}x{E.Lcap}x{E.H}x{E.D} bf16 ...")
     g = torch.Generator(device=dev).manual_seed(E.seed)
-    kcache = [torch.randn((E.B, E.Lcap, E.H, E.D), device=dev, dtype=torch.bfloat16, generator=g)
-              for _ in range(E.n_layer)]
-    vcache = [torch.randn((E.B, E.Lcap, E.H, E.D), device=dev, dtype=torch.bfloat16, generator=g)
-              for _ in range(E.n_layer)]
+    eng = sw.KVCache(E.n_layer, E.B, E.Lcap, E.H, E.D, device=dev,
+                     windows=[E.window(l) for l in range(E.n_layer)])
+    for l in range(E.n_layer):
+        eng.k[l].copy_(torch.randn((E.B, E.Lcap, E.H, E.D), device=dev, dtype=torch.bfloat16,
+                                   generator=g))
+    for l in range(E.n_layer):
+        eng.v[l].copy_(torch.randn((E.B, E.Lcap, E.H, E.D), device=dev, dtype=torch.bfloat16,
+                                   generator=g))
+    kcache = [eng.k[l] for l in range(E.n_layer)]
+    vcache = [eng.v[l] for l in range(E.n_layer)]
     qn = torch.randn((E.n_layer, E.B, E.H, E.D), device=dev, dtype=torch.bfloat16, generator=g)
     kn = torch.randn((E.n_layer, E.B, E.H, E.D), device=dev, dtype=torch.bfloat16, generator=g)
     vn = torch.randn((E.n_layer, E.B, E.H, E.D), device=dev, dtype=torch.bfloat16, generator=g)
@@ -283,6 +293,31 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    # the whole 30-layer decode step (append + decode per layer, one launch each) captured in one
+    # HIP graph and replayed per token; timed per replay with events, outside the timed region
+    step_graph = None
+    if not args.no_step_graph:
+        log("decode step graph: capture and replay ...")
+        sg = sw.DecodeStepGraph(eng)
+        sg.q.copy_(qn)
+        sg.k_new.copy_(kn)
+        sg.v_new.copy_(vn)
+        reps = max(args.steps, 5)
+        ev_g = [(Ev(), Ev()) for _ in range(reps + 2)]
+        for i in range(reps + 2):
+            eng.lens.copy_(pos_tab[i % E.steps])
+            ev_g[i][0].record()
+            sg.replay()
+            ev_g[i][1].record()
+        torch.cuda.synchronize()
+        t_g = sum(a.elapsed_time(b) for a, b in ev_g[2:]) / reps * 1e-3
+        g_bytes = sum(decode_bytes(i % E.steps) for i in range(2, reps + 2)) / reps
+        step_graph = {"us_per_layer_step": round(t_g / E.n_layer * 1e6, 2),
+                      "GB/s": round(g_bytes / t_g / 1e9, 1),
+                      "frac_of_hbm_peak": round(g_bytes / t_g / 1e9 / PEAK_HBM, 4),
+                      "us_per_token_all_layers": round(t_g * 1e6, 1), "replays": reps}
+        del sg
+
     # streaming-read reference: a plain read of the decode step's byte count, rotating over the
     # 30 layers' key caches (each larger than the last-level cache), outside the timed region
     stream_ref = None
@@ -322,7 +357,8 @@ def main() -> int:
                    "us_per_layer_step": round(t_dec / E.n_layer * 1e6, 2),
                    "bytes_per_layer_step": round(dec_bytes / E.n_layer),
                    "stream_read_ref_GB/s": stream_ref and round(stream_ref, 1),
-                   "frac_of_stream_read_ref": stream_ref and round(dec_gbs / stream_ref, 4)},
+                   "frac_of_stream_read_ref": stream_ref and round(dec_gbs / stream_ref, 4),
+                   "step_graph": step_graph},
         "prefill": {"TFLOP/s": round(pre_flops / t_pre / 1e12, 2), "ms_per_layer": round(t_pre * 1e3, 4)},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -19,8 +19,8 @@ from ._lib import SWATTN_BF16, SWATTN_F32, check, last_error, load
 __all__ = [
     "attn_abi_version", "attn_last_error", "attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv",
     "attn_bwd_workspace_bytes",
-    "attn_prefill", "attn_kv_append", "attn_decode", "attn_decode_workspace_bytes", "attention",
-    "KVCache", "FULL",
+    "attn_prefill", "attn_kv_append", "attn_decode", "attn_decode_step",
+    "attn_decode_workspace_bytes", "attention", "KVCache", "DecodeStepGraph", "FULL",
 ]
 
 FULL = 2 ** 31 - 1  # a window that is never smaller than the sequence: full causal attention
@@ -220,6 +220,36 @@ def attn_decode(q, kcache, vcache, lens, o=None, lse=None, window=None, ws=None,
     return o, lse
 
 
+def attn_decode_step(q, knew, vnew, kcache, vcache, pos, o=None, lse=None, window=None, ws=None,
+                     want_lse=False):
+    """Append + decode in one call: kcache[b, pos[b]] = knew[b] (and v), then q [B, H, D] attends
+    to cache rows .. pos[b].  pos int32 [B] on the device counts the cached tokens before the step."""
+    B, H, D = q.shape
+    Lcap = kcache.shape[1]
+    _need(q, "q", None, torch.bfloat16)
+    _need(knew, "knew", (B, H, D), torch.bfloat16)
+    _need(vnew, "vnew", (B, H, D), torch.bfloat16)
+    _need(kcache, "kcache", (B, Lcap, H, D), torch.bfloat16)
+    _need(vcache, "vcache", (B, Lcap, H, D), torch.bfloat16)
+    _need(pos, "pos", (B,), torch.int32)
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", (B, H, D), torch.bfloat16)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), device=q.device, dtype=torch.float32)
+    if lse is not None:
+        _need(lse, "lse", (B, H), torch.float32)
+    need = attn_decode_workspace_bytes(B, H, Lcap, D)
+    if ws is None:
+        ws = torch.empty(need, device=q.device, dtype=torch.uint8)
+    rc = load().attn_decode_step(q.data_ptr(), knew.data_ptr(), vnew.data_ptr(), kcache.data_ptr(),
+                                 vcache.data_ptr(), pos.data_ptr(), o.data_ptr(), _ptr(lse), B, H,
+                                 Lcap, D, _win(window, Lcap), ws.data_ptr(),
+                                 ws.numel() * ws.element_size(), _stream(q))
+    check(rc, "attn_decode_step")
+    return o, lse
+
+
 class _Attention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, window):
@@ -257,7 +287,6 @@ class KVCache:
         self.windows = list(windows) if windows is not None else [None] * n_layer
         self._ws = torch.empty(attn_decode_workspace_bytes(B, H, Lcap, D), device=device,
                                dtype=torch.uint8)
-        self._next = torch.empty_like(self.lens)
 
     def prefill(self, layer, q, k, v, lens):
         """Write prompts (padded [B, Tq, H, D]) into the cache and attend causally."""
@@ -271,12 +300,49 @@ class KVCache:
                             window=self.windows[layer])
         return o
 
-    def decode(self, layer, q, k_new, v_new):
-        torch.add(self.lens, 1, out=self._next)
-        attn_kv_append(self.k[layer], self.v[layer], k_new, v_new, self.lens)
-        o, _ = attn_decode(q, self.k[layer], self.v[layer], self._next,
-                           window=self.windows[layer], ws=self._ws)
+    def decode(self, layer, q, k_new, v_new, o=None):
+        """Append the new token's key / value at row ``lens`` and attend (one call)."""
+        o, _ = attn_decode_step(q, k_new, v_new, self.k[layer], self.v[layer], self.lens, o=o,
+                                window=self.windows[layer], ws=self._ws)
         return o
 
     def step(self):
         self.lens.add_(1)
+
+
+class DecodeStepGraph:
+    """One generated token's attention over every layer of a ``KVCache``, captured once in a HIP
+    graph (torch.cuda.CUDAGraph) and replayed per token.
+
+    The graph reads the per-layer inputs from fixed buffers ``q``, ``k_new``, ``v_new``
+    ([n_layer, B, H, D] bf16) and writes ``o`` ([n_layer, B, H, D]); it appends to the cache,
+    attends, and finally advances ``cache.lens`` by one.  Fill the inputs, call ``replay()``, read
+    ``o``.  Only library kernels and one elementwise add are captured (no memset nodes).
+    """
+
+    def __init__(self, cache: KVCache):
+        self.cache = cache
+        shape = (cache.n_layer, cache.B, cache.H, cache.D)
+        dev = cache.lens.device
+        self.q = torch.zeros(shape, device=dev, dtype=torch.bfloat16)
+        self.k_new = torch.zeros_like(self.q)
+        self.v_new = torch.zeros_like(self.q)
+        self.o = torch.zeros_like(self.q)
+        # one eager pass first, so every kernel is loaded before capture; pos = -1 writes nothing
+        idle = torch.full_like(cache.lens, -1)
+        for layer in range(cache.n_layer):
+            attn_decode_step(self.q[layer], self.k_new[layer], self.v_new[layer], cache.k[layer],
+                             cache.v[layer], idle, o=self.o[layer], window=cache.windows[layer],
+                             ws=cache._ws)
+        idle.add_(1)
+        torch.cuda.synchronize(dev)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            for layer in range(cache.n_layer):
+                cache.decode(layer, self.q[layer], self.k_new[layer], self.v_new[layer],
+                             o=self.o[layer])
+            cache.step()
+
+    def replay(self):
+        self.graph.replay()
+        return self.o

@@ -302,4 +302,53 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
                     "attn_decode launch");
 }
 
+int attn_decode_step(const void* q, const void* knew, const void* vnew, void* kcache, void* vcache,
+                     const int* pos, void* o, float* lse, int B, int H, int Lcap, int D,
+                     int window, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_dims("attn_decode_step", B, H, Lcap, "Lcap", D, window));
+  TRY(check_ptr(q, "q"));
+  TRY(check_ptr(knew, "knew"));
+  TRY(check_ptr(vnew, "vnew"));
+  TRY(check_ptr(kcache, "kcache"));
+  TRY(check_ptr(vcache, "vcache"));
+  if (!pos) return fail(SWATTN_EINVAL, "pos is NULL");
+  if (reinterpret_cast<uintptr_t>(pos) & 3u) return fail(SWATTN_EINVAL, "pos is not 4-byte aligned");
+  TRY(check_ptr(o, "o"));
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(SWATTN_EINVAL, "lse is not 4-byte aligned");
+  const size_t need = attn_decode_workspace_bytes(B, H, Lcap, D);
+  if (!ws)
+    return fail(SWATTN_EWORKSPACE, "attn_decode_step: workspace is NULL (%zu bytes needed)", need);
+  if (!aligned16(ws))
+    return fail(SWATTN_EINVAL, "attn_decode_step: workspace is not 16-byte aligned");
+  if (ws_bytes < need)
+    return fail(SWATTN_EWORKSPACE, "attn_decode_step: workspace of %zu bytes < %zu needed",
+                ws_bytes, need);
+  const int nc_max = decode_chunks(Lcap);
+  const size_t slots = (size_t)B * H * nc_max;
+  swattn::DecArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kc = static_cast<const uint16_t*>(kcache);
+  a.vc = static_cast<const uint16_t*>(vcache);
+  a.pos = pos;
+  a.kn = static_cast<const uint16_t*>(knew);
+  a.vn = static_cast<const uint16_t*>(vnew);
+  a.kcw = static_cast<uint16_t*>(kcache);
+  a.vcw = static_cast<uint16_t*>(vcache);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.ws_o = static_cast<float*>(ws);
+  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + align256(slots * D * sizeof(float)));
+  a.B = B;
+  a.H = H;
+  a.D = D;
+  a.Lcap = Lcap;
+  a.window = window;
+  a.nc_max = nc_max;
+  a.scale_log2 = scale_log2_for(D);
+  (void)hipGetLastError();
+  return hip_status(swattn::launch_decode(a, static_cast<hipStream_t>(stream)),
+                    "attn_decode_step launch");
+}
+
 }  // extern "C"

@@ -14,6 +14,11 @@
 //   few pairs (long contexts, small batch): one wave per (head, chunk, sequence) writes its chunk's
 //   (max, sum, unnormalised output) to the workspace and a second kernel merges the chunks.
 // Both merge with the log-sum-exp rule and write O (bf16) and LSE.
+//
+// Decode step (STEP): the same kernels also append the step's new key / value row at pos[b] and
+// attend over rows .. pos[b].  The chunk ending at the new row takes that row's key / value from
+// the new-row inputs instead of the cache, and one wave copies the row into the cache after its
+// own loads, so no launch reads a cache row written in the same launch.
 #include "common.h"
 #include "launch.h"
 
@@ -40,7 +45,65 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Cache rows the query of sequence b sees the end of: a decode clamps lens to [0, Lcap]; a decode
+// step appends at pos (valid in [0, Lcap)) and sees pos + 1 rows, or none for an invalid pos.
+template <bool STEP>
+__device__ __forceinline__ int dec_len(const DecArgs& p, int b) {
+  if (STEP) {
+    const int ps = p.pos[b];
+    return (ps >= 0 && ps < p.Lcap) ? ps + 1 : 0;
+  }
+  return min(max(p.lens[b], 0), p.Lcap);
+}
+
+// K and V rows of the decode step's last 64-key chunk, which ends at the new row L - 1: that row's
+// key / value come from the new-row inputs; rows past ce re-read row ce - 1 (masked later).
 template <int D>
+__device__ __forceinline__ void dec_load_chunk(const DecArgs& p, const uint16_t* kb,
+                                               const uint16_t* vb, int64_t rowstride, int b, int h,
+                                               int cs, int ce, int L, int kq, int dc,
+                                               uint4 (&kr)[kDecodeChunk / (64 / (D / 8))],
+                                               uint4 (&vr)[kDecodeChunk / (64 / (D / 8))]) {
+  constexpr int KPI = 64 / (D / 8), NL = kDecodeChunk / KPI;
+  const int64_t nrow = ((int64_t)b * p.H + h) * D + 8 * dc;
+#pragma unroll
+  for (int r = 0; r < NL; ++r) {
+    const int j = min(cs + r * KPI + kq, ce - 1);
+    const uint16_t* ks = kb + j * rowstride;
+    const uint16_t* vs = vb + j * rowstride;
+    if (j == L - 1) {
+      ks = p.kn + nrow;
+      vs = p.vn + nrow;
+    }
+    kr[r] = ldg16(ks);
+    vr[r] = ldg16(vs);
+  }
+}
+
+// Decode step: the new row of head h of sequence b (16 bytes per lane over lanes 0 .. D / 8 - 1)
+// is loaded when a kernel starts, without waiting, and written to cache row L - 1 after the
+// kernel's own loads, so the copy adds no wait to the attention.
+template <int D>
+struct NewRow {
+  uint4 k, v;
+  bool mine;
+  __device__ __forceinline__ void load(const DecArgs& p, int b, int h, int lane, bool owner) {
+    mine = owner && lane < D / 8;
+    if (mine) {
+      const int64_t src = ((int64_t)b * p.H + h) * D + 8 * lane;
+      k = ldg16(p.kn + src);
+      v = ldg16(p.vn + src);
+    }
+  }
+  __device__ __forceinline__ void store(const DecArgs& p, int b, int h, int L, int lane) const {
+    if (!mine) return;
+    const int64_t dst = (((int64_t)b * p.Lcap + (L - 1)) * p.H + h) * D + 8 * lane;
+    *reinterpret_cast<uint4*>(p.kcw + dst) = k;
+    *reinterpret_cast<uint4*>(p.vcw + dst) = v;
+  }
+};
+
+template <int D, bool STEP>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecArgs p) {
   constexpr int LPK = D / 8;      // lanes per key row (16 bytes each)
   constexpr int KPI = 64 / LPK;   // key rows per load instruction
@@ -48,7 +111,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecArgs p) {
   constexpr int NL = C / KPI;     // loads per lane per tensor
 
   const int h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;  // heads fastest: adjacent bytes
-  const int L = min(max(p.lens[b], 0), p.Lcap);
+  const int L = dec_len<STEP>(p, b);
   if (L == 0) return;
   const int nvis = min(p.window, L);
   const int j0 = L - nvis;
@@ -63,16 +126,22 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecArgs p) {
   const uint16_t* kb = p.kc + ((int64_t)b * p.Lcap) * rowstride + h * D + 8 * dc;
   const uint16_t* vb = p.vc + ((int64_t)b * p.Lcap) * rowstride + h * D + 8 * dc;
 
+  NewRow<D> nr;
+  if (STEP) nr.load(p, b, h, lane, c == nc - 1);
   uint4 kr[NL], vr[NL];
+  if (STEP && c == nc - 1) {  // the chunk ending at the new row
+    dec_load_chunk<D>(p, kb, vb, rowstride, b, h, cs, ce, L, kq, dc, kr, vr);
+  } else {
 #pragma unroll
-  for (int r = 0; r < NL; ++r) {
-    const int j = cs + r * KPI + kq;
-    if (j < ce) {
-      kr[r] = ldg16(kb + j * rowstride);
-      vr[r] = ldg16(vb + j * rowstride);
-    } else {
-      kr[r] = make_uint4(0, 0, 0, 0);
-      vr[r] = make_uint4(0, 0, 0, 0);
+    for (int r = 0; r < NL; ++r) {
+      const int j = cs + r * KPI + kq;
+      if (j < ce) {
+        kr[r] = ldg16(kb + j * rowstride);
+        vr[r] = ldg16(vb + j * rowstride);
+      } else {
+        kr[r] = make_uint4(0, 0, 0, 0);
+        vr[r] = make_uint4(0, 0, 0, 0);
+      }
     }
   }
   float qv[8];
@@ -122,6 +191,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecArgs p) {
       ov[2 * e + 1] = fmaf(pr, bf16_hi(vw[e]), ov[2 * e + 1]);
     }
   }
+  if (STEP) nr.store(p, b, h, L, lane);
   // reduce over the key-row groups: lanes with equal dc
 #pragma unroll
   for (int off = LPK; off < 32; off <<= 1) {
@@ -147,13 +217,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecArgs p) {
   }
 }
 
-template <int D>
+template <int D, bool STEP>
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecArgs p) {
   constexpr int DPL = D / 64;  // features per lane
   const int bh = blockIdx.x;
   const int b = bh / p.H;
   const int lane = threadIdx.x;
-  const int L = min(max(p.lens[b], 0), p.Lcap);
+  const int L = dec_len<STEP>(p, b);
   uint16_t* ob = p.o + (int64_t)bh * D + lane * DPL;
   if (L == 0) {
 #pragma unroll
@@ -189,7 +259,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecArgs p) {
 // dealt round-robin to the waves (split-K inside the workgroup); each wave keeps a running online
 // softmax over its chunks, and the NW partial results are merged in LDS with the log-sum-exp rule.
 // Used when there are enough (sequence, head) pairs to fill the GPU; no workspace is touched.
-template <int D, int NW>
+template <int D, int NW, bool STEP>
 __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(DecArgs p) {
   constexpr int LPK = D / 8, KPI = 64 / LPK, C = kDecodeChunk, NL = C / KPI;
   __shared__ float s_o[NW][D];
@@ -198,7 +268,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(DecArgs p) {
   const int bh = blockIdx.x;  // consecutive workgroups: consecutive heads, adjacent bytes
   const int b = bh / p.H, h = bh % p.H;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int L = min(max(p.lens[b], 0), p.Lcap);
+  const int L = dec_len<STEP>(p, b);
   uint16_t* ob = p.o + (int64_t)bh * D;
   if (L == 0) {
     for (int d = threadIdx.x; d < D; d += 64 * NW) ob[d] = 0;
@@ -223,6 +293,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(DecArgs p) {
       qv[2 * e + 1] = bf16_hi(qw[e]) * p.scale_log2;
     }
   }
+  NewRow<D> nr;
+  if (STEP) nr.load(p, b, h, lane, wave == NW - 1);
   float m_run = -INFINITY, l_run = 0.f;  // l_run: this lane's key rows only
   float ov[8];
 #pragma unroll
@@ -232,11 +304,15 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(DecArgs p) {
     const int cs = j0 + c * C;
     const int ce = min(cs + C, L);
     uint4 kr[NL], vr[NL];
+    if (STEP && c == nc - 1) {  // the chunk ending at the new row
+      dec_load_chunk<D>(p, kb, vb, rowstride, b, h, cs, ce, L, kq, dc, kr, vr);
+    } else {
 #pragma unroll
-    for (int r = 0; r < NL; ++r) {
-      const int j = min(cs + r * KPI + kq, ce - 1);  // rows past the chunk re-read a valid row
-      kr[r] = ldg16(kb + j * rowstride);
-      vr[r] = ldg16(vb + j * rowstride);
+      for (int r = 0; r < NL; ++r) {
+        const int j = min(cs + r * KPI + kq, ce - 1);  // rows past the chunk re-read a valid row
+        kr[r] = ldg16(kb + j * rowstride);
+        vr[r] = ldg16(vb + j * rowstride);
+      }
     }
     float sc[NL];
     float mx = -INFINITY;
@@ -274,6 +350,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(DecArgs p) {
       }
     }
   }
+  if (STEP) nr.store(p, b, h, L, lane);
   // this wave's partial: sum over the key-row groups (lanes with equal dc)
 #pragma unroll
   for (int off = LPK; off < 32; off <<= 1) {
@@ -329,23 +406,25 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs p) {
   *reinterpret_cast<uint4*>(p.vc + dst) = ldg16(p.vn + src);
 }
 
-template <int D>
+template <int D, bool STEP>
 static hipError_t launch_decode_d(const DecArgs& a, hipStream_t s) {
   if (decode_uses_fused(a.B, a.H)) {
-    hipLaunchKernelGGL((decode_fused_kernel<D, 8>), dim3(a.B * a.H), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((decode_fused_kernel<D, 8, STEP>), dim3(a.B * a.H), dim3(512), 0, s, a);
     return hipGetLastError();
   }
   const int vis_max = a.window < a.Lcap ? a.window : a.Lcap;
   const int nc = (vis_max + kDecodeChunk - 1) / kDecodeChunk;
-  hipLaunchKernelGGL((decode_split_kernel<D>), dim3(a.H, nc, a.B), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((decode_split_kernel<D, STEP>), dim3(a.H, nc, a.B), dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.H), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((decode_combine_kernel<D, STEP>), dim3(a.B * a.H), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecArgs& a, hipStream_t s) {
-  return a.D == 64 ? launch_decode_d<64>(a, s) : launch_decode_d<128>(a, s);
+  if (a.pos)
+    return a.D == 64 ? launch_decode_d<64, true>(a, s) : launch_decode_d<128, true>(a, s);
+  return a.D == 64 ? launch_decode_d<64, false>(a, s) : launch_decode_d<128, false>(a, s);
 }
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s) {

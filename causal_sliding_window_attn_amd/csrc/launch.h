@@ -50,7 +50,12 @@ struct DecArgs {
   const uint16_t* q;   // [B, H, D]
   const uint16_t* kc;  // [B, Lcap, H, D]
   const uint16_t* vc;
-  const int* lens;
+  const int* lens;     // decode: cached tokens including the new one
+  const int* pos;      // decode step (append + decode): the new row's index, or null
+  const uint16_t* kn;  // decode step: the new row's key / value [B, H, D]
+  const uint16_t* vn;
+  uint16_t* kcw;       // decode step: the caches, written at row pos
+  uint16_t* vcw;
   uint16_t* o;         // [B, H, D]
   float* lse;          // [B, H] or null
   float* ws_o;         // [B*H, nc_max, D]

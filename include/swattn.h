@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define SWATTN_ABI_VERSION 1
+#define SWATTN_ABI_VERSION 2  /* 2: attn_decode_step added */
 
 typedef enum { SWATTN_BF16 = 0, SWATTN_F32 = 1 } swattn_dtype;
 
@@ -140,6 +140,28 @@ size_t attn_decode_workspace_bytes(int B, int H, int Lcap, int D);
 int attn_decode(const void* q, const void* kcache, const void* vcache, const int* lens, void* o,
                 float* lse, int B, int H, int Lcap, int D, int window, void* ws, size_t ws_bytes,
                 void* stream);
+
+/*
+ * One Engine decode step, KV append and decode together: for each sequence b with
+ * 0 <= pos[b] < Lcap, writes knew[b] / vnew[b] to cache row pos[b], then the query (at position
+ * pos[b]) attends to rows max(0, pos[b] - window + 1) .. pos[b] of the updated cache.  The same
+ * operation as attn_kv_append(pos) followed by attn_decode(lens = pos + 1), in one launch when
+ * B * H >= 512 (two otherwise); no launch reads a cache row written in the same launch.  It makes
+ * no host synchronisation and issues no memset, so a model's whole decode step (one call per
+ * layer) can be captured in one HIP graph and replayed per generated token.
+ * (Operation: walkthrough, section "Pretraining", Engine paragraph -- the decode phase over the
+ * KV cache.)
+ *   q, knew, vnew [B, H, D] bf16 (read); kcache, vcache [B, Lcap, H, D] bf16 (row pos[b] written).
+ *   pos    device int32 [B]: cached tokens before this step.  A sequence with pos[b] outside
+ *          [0, Lcap) is not written and gets o = 0, lse = -inf.
+ *   o      [B, H, D] bf16 (written);  lse [B, H] float32 or NULL.
+ *   window keys visible to the query, counting itself.
+ *   ws / ws_bytes: caller-owned device scratch of at least attn_decode_workspace_bytes().
+ * Errors as attn_decode.
+ */
+int attn_decode_step(const void* q, const void* knew, const void* vnew, void* kcache, void* vcache,
+                     const int* pos, void* o, float* lse, int B, int H, int Lcap, int D,
+                     int window, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -28,9 +28,9 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = set(declared_functions())
-    assert {"attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_decode", "attn_prefill", "attn_kv_append",
-            "attn_bwd_workspace_bytes", "attn_decode_workspace_bytes", "attn_last_error",
-            "attn_abi_version"} == names
+    assert {"attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_decode", "attn_prefill",
+            "attn_kv_append", "attn_decode_step", "attn_bwd_workspace_bytes",
+            "attn_decode_workspace_bytes", "attn_last_error", "attn_abi_version"} == names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -54,7 +54,7 @@ def test_nm_lists_only_c_symbols(lib):
 
 
 def test_abi_version(lib):
-    assert lib.attn_abi_version() == 1
+    assert lib.attn_abi_version() == 2
 
 
 P = 4096  # an aligned, non-null stand-in pointer: validation must fail before it is ever used
@@ -120,6 +120,30 @@ def test_prefill_append_decode_validation(lib):
     assert lib.attn_decode(P, P, P, P, P, None, 2, 2, 100, 128, 8, None, need, None) == -3
     assert lib.attn_decode(P, P, P, P, P, None, 2, 2, 100, 128, 0, P, need, None) == -1
     assert lib.attn_decode(P, P, P, None, P, None, 2, 2, 100, 128, 8, P, need, None) == -1
+
+
+def test_decode_step_validation(lib):
+    need = lib.attn_decode_workspace_bytes(2, 2, 100, 128)
+    # q, knew, vnew, kcache, vcache, pos, o, lse, B, H, Lcap, D, window, ws, ws_bytes, stream
+    ok = [P, P, P, P, P, P, P, None, 2, 2, 100, 128, 8, P, need, None]
+
+    def call(**change):
+        a = list(ok)
+        for i, val in change.items():
+            a[int(i[1:])] = val
+        return lib.attn_decode_step(*a)
+
+    assert call(a13=P, a14=need - 1) == -3
+    assert call(a13=None) == -3
+    assert "workspace" in err(lib)
+    assert call(a12=0) == -1  # window
+    assert call(a5=None) == -1 and "pos" in err(lib)
+    assert call(a5=P + 2) == -1  # pos alignment
+    assert call(a1=None) == -1 and "knew" in err(lib)
+    assert call(a4=None) == -1 and "vcache" in err(lib)
+    assert call(a7=P + 2) == -1  # lse alignment
+    assert call(a11=80) == -2  # head dimension
+    assert call(a10=0) == -1  # Lcap
 
 
 def test_last_error_is_thread_local(lib):

@@ -386,3 +386,77 @@ def test_autograd_wrapper_and_kvcache(sw):
     kc, vc = f64(cache.k[1]), f64(cache.v[1])
     od_r, _ = ref.decode(f64(qn), kc, vc, np.array([4, 11]), 8)
     assert np.abs(f64(od) - od_r).max() <= O_TOL
+
+
+# ------------------------------------------------------------------ decode step (append + decode)
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("B,H", [(8, 3), (64, 8)])  # split-K across workgroups / within one
+def test_decode_step_equals_append_then_decode(sw, D, B, H):
+    """attn_decode_step(pos) is attn_kv_append(pos) then attn_decode(lens = pos + 1), bit for bit,
+    and matches the oracle; a pos outside [0, Lcap) writes nothing and gives o = 0, lse = -inf."""
+    Lcap = 200
+    edge = [0, 1, 63, 64, 65, 128, 199, -1, 200]
+    pos = torch.tensor([edge[b % len(edge)] for b in range(B)], dtype=torch.int32)
+    valid = ((pos >= 0) & (pos < Lcap)).numpy()
+    g = torch.Generator().manual_seed(21 + D)
+    kc = torch.randn(B, Lcap, H, D, generator=g).to(torch.bfloat16)
+    vc = torch.randn(B, Lcap, H, D, generator=g).to(torch.bfloat16)
+    q, kn, vn = (torch.randn(B, H, D, generator=g).to(torch.bfloat16) for _ in range(3))
+    qd, knd, vnd, posd = q.to(DEV), kn.to(DEV), vn.to(DEV), pos.to(DEV)
+    lens_after = torch.where(pos >= 0, pos + 1, torch.zeros_like(pos)).to(DEV)
+    kc_r, vc_r = f64(kc), f64(vc)
+    vb = np.nonzero(valid)[0]  # the oracle's append covers in-range rows only
+    kc_r[vb], vc_r[vb] = ref.kv_append(kc_r[vb], vc_r[vb], f64(kn)[vb], f64(vn)[vb],
+                                       pos.numpy()[vb])
+    for window in (None, 1, 2, 64, 65, 100):
+        k1, v1 = kc.to(DEV), vc.to(DEV)
+        o1, lse1 = sw.attn_decode_step(qd, knd, vnd, k1, v1, posd, window=window, want_lse=True)
+        k2, v2 = kc.to(DEV), vc.to(DEV)
+        sw.attn_kv_append(k2, v2, knd, vnd, posd)
+        o2, lse2 = sw.attn_decode(qd, k2, v2, lens_after, window=window, want_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(k1, k2) and torch.equal(v1, v2), f"cache after the step, window {window}"
+        assert torch.equal(o1[valid], o2[valid]) and torch.equal(lse1[valid], lse2[valid]), window
+        assert torch.all(o1[~valid] == 0) and torch.all(torch.isneginf(lse1[~valid]))
+        o_r, lse_r = ref.decode(f64(q), kc_r, vc_r, np.where(valid, pos.numpy() + 1, 0), window)
+        assert np.abs(f64(o1) - o_r).max() <= O_TOL, f"window {window}"
+        assert np.abs(f64(lse1)[valid] - lse_r[valid]).max() <= LSE_TOL
+
+
+@pytest.mark.parametrize("B,H", [(4, 2), (64, 8)])
+def test_decode_step_graph_replays_match_eager(sw, B, H):
+    """A captured decode step over every layer, replayed token after token with unrelated eager
+    work and synchronisations in between, equals the same steps run eagerly, bit for bit."""
+    n_layer, Lcap, D = 3, 96, 128
+    windows = [None, 5, 40]
+    g = torch.Generator().manual_seed(31 + B)
+    lens0 = torch.randint(1, 60, (B,), generator=g, dtype=torch.int32)
+    Tq = int(lens0.max())
+    caches = [sw.KVCache(n_layer, B, Lcap, H, D, windows=windows) for _ in range(2)]
+    prompt = [[torch.randn(B, Tq, H, D, generator=g).to(torch.bfloat16).to(DEV) for _ in range(3)]
+              for _ in range(n_layer)]
+    for c in caches:
+        for layer in range(n_layer):
+            c.prefill(layer, *prompt[layer], lens0.to(DEV))
+    eager, graphed = caches
+    step_graph = sw.DecodeStepGraph(graphed)
+    junk = torch.randn(512, 512, device=DEV)
+    for s in range(4):
+        ins = [torch.randn(n_layer, B, H, D, generator=g).to(torch.bfloat16).to(DEV)
+               for _ in range(3)]
+        o_e = torch.stack([eager.decode(layer, ins[0][layer], ins[1][layer], ins[2][layer])
+                           for layer in range(n_layer)])
+        eager.step()
+        step_graph.q.copy_(ins[0])
+        step_graph.k_new.copy_(ins[1])
+        step_graph.v_new.copy_(ins[2])
+        o_g = step_graph.replay()
+        junk = (junk @ junk).tanh_()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_e), f"replay {s}"
+        assert torch.equal(graphed.lens, eager.lens)
+        assert torch.equal(graphed.k, eager.k) and torch.equal(graphed.v, eager.v), f"replay {s}"
+        # the eager path itself against the oracle, last layer
+        lens_now = f64(eager.lens).astype(np.int64)
+        o_r, _ = ref.decode(f64(ins[0][-1]), f64(eager.k[-1]), f64(eager.v[-1]), lens_now, 40)
+        assert np.abs(f64(o_e[-1]) - o_r).max() <= O_TOL, f"replay {s}"
