@@ -14,7 +14,8 @@ visible (query, key) pair forward, 10D backward).  ``decode`` reports algorithmi
 visible cache row read once, plus q and o), next to a plain streaming read of the same byte count
 (the rate this GPU sustains at that size), and ``decode.step_graph`` the same decode step for all
 30 layers as one replay of a captured HIP graph (attn_decode_step: append and decode in one launch
-per layer); ``prefill`` TFLOP/s.  ``roofline`` describes the
+per layer); ``prefill`` TFLOP/s; ``varlen`` the d20 rows re-read as packed documents that attend
+only to themselves (attn_fwd_varlen / attn_bwd_varlen).  ``roofline`` describes the
 longest-running MFMA kernel; ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
 d20 workload on the host cores.  One JSON line goes to stdout; progress goes to stderr.
 """
@@ -131,6 +132,8 @@ def main() -> int:
                     help="skip the streaming-read reference of the decode roofline")
     ap.add_argument("--no-step-graph", action="store_true",
                     help="skip the graph-replayed whole-model decode step measurement")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the packed-document (varlen) fwd+bwd measurement")
     ap.add_argument("--calib-copy-mib", type=int, default=1024,
                     help="after the timed region, one plain device copy of this size (the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -293,6 +296,42 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    # packed documents in the same d20 rows (each document attends only to itself; the sequence
+    # offsets come from workloads.d20_packed_cu): the same q, k, v, dO viewed as [B*T, H, D],
+    # forward + backward timed with events, outside the timed region
+    varlen = None
+    if not args.no_varlen:
+        log("packed-document d20 rows: forward + backward ...")
+        cu_h = W.d20_packed_cu(B, T)
+        lens_d = (cu_h[1:] - cu_h[:-1]).tolist()
+        ms = max(lens_d)
+        cu_d = cu_h.to(dev)
+        qv, kv, vv, dov = (t.view(B * T, H, D) for t in (q, k, v, do))
+        ov = torch.empty_like(qv)
+        lsev = torch.empty((H, B * T), device=dev, dtype=torch.float32)
+        gv = [torch.empty_like(qv) for _ in range(3)]
+        wsv = torch.empty(sw.attn_bwd_workspace_bytes(1, H, B * T, D), device=dev,
+                          dtype=torch.uint8)
+        reps = max(args.steps, 5)
+        ev_v = [[Ev() for _ in range(3)] for _ in range(reps + 2)]
+        for i in range(reps + 2):
+            ev_v[i][0].record()
+            sw.attn_fwd_varlen(qv, kv, vv, cu_d, ms, o=ov, lse=lsev, window=win)
+            ev_v[i][1].record()
+            sw.attn_bwd_varlen(qv, kv, vv, ov, lsev, dov, cu_d, ms, window=win, dq=gv[0], dk=gv[1],
+                               dv=gv[2], ws=wsv)
+            ev_v[i][2].record()
+        torch.cuda.synchronize()
+        tv_f = sum(e[0].elapsed_time(e[1]) for e in ev_v[2:]) / reps * 1e-3
+        tv_b = sum(e[1].elapsed_time(e[2]) for e in ev_v[2:]) / reps * 1e-3
+        pv = sum(pairs(L, win) for L in lens_d) * H
+        varlen = {"TFLOP/s": round(14 * D * pv / (tv_f + tv_b) / 1e12, 2),
+                  "fwd_ms": round(tv_f * 1e3, 4), "bwd_ms": round(tv_b * 1e3, 4),
+                  "documents": len(lens_d), "max_seqlen": ms, "visible_pairs": pv,
+                  "workload": "d20 rows B32 T2048 H10 D128 holding packed documents (log-normal "
+                              "lengths, median 600, cut at row ends), same q, k, v, dO"}
+        del ov, lsev, gv, wsv
+
     # the whole 30-layer decode step (append + decode per layer, one launch each) captured in one
     # HIP graph and replayed per token; timed per replay with events, outside the timed region
     step_graph = None
@@ -360,6 +399,7 @@ def main() -> int:
                    "frac_of_stream_read_ref": stream_ref and round(dec_gbs / stream_ref, 4),
                    "step_graph": step_graph},
         "prefill": {"TFLOP/s": round(pre_flops / t_pre / 1e12, 2), "ms_per_layer": round(t_pre * 1e3, 4)},
+        "varlen": varlen,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "device": props.name,

@@ -20,7 +20,8 @@ __all__ = [
     "attn_abi_version", "attn_last_error", "attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv",
     "attn_bwd_workspace_bytes",
     "attn_prefill", "attn_kv_append", "attn_decode", "attn_decode_step",
-    "attn_decode_workspace_bytes", "attention", "KVCache", "DecodeStepGraph", "FULL",
+    "attn_decode_workspace_bytes", "attn_fwd_varlen", "attn_bwd_varlen", "attention",
+    "attention_varlen", "KVCache", "DecodeStepGraph", "FULL",
 ]
 
 FULL = 2 ** 31 - 1  # a window that is never smaller than the sequence: full causal attention
@@ -250,6 +251,63 @@ def attn_decode_step(q, knew, vnew, kcache, vcache, pos, o=None, lse=None, windo
     return o, lse
 
 
+def _cu(cu_seqlens, device):
+    _need(cu_seqlens, "cu_seqlens", None, torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be int32 [nseq + 1] with nseq >= 1")
+    if cu_seqlens.device != device:
+        raise ValueError("cu_seqlens must be on the same device as q")
+    return cu_seqlens.numel() - 1
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, o=None, lse=None, window=None,
+                    want_lse=True):
+    """Packed sequences: q, k, v [total, H, D] bf16, sequence s = rows cu_seqlens[s] ..
+    cu_seqlens[s + 1] - 1 attending only to itself.  Returns (o, lse [H, total] or None)."""
+    total, H, D = q.shape
+    _need(q, "q", None, torch.bfloat16)
+    _need(k, "k", (total, H, D), torch.bfloat16)
+    _need(v, "v", (total, H, D), torch.bfloat16)
+    nseq = _cu(cu_seqlens, q.device)
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", (total, H, D), torch.bfloat16)
+    if lse is None and want_lse:
+        lse = torch.empty((H, total), device=q.device, dtype=torch.float32)
+    if lse is not None:
+        _need(lse, "lse", (H, total), torch.float32)
+    rc = load().attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse),
+                                cu_seqlens.data_ptr(), nseq, total, int(max_seqlen), H, D,
+                                _win(window, int(max_seqlen)), _stream(q))
+    check(rc, "attn_fwd_varlen")
+    return o, lse
+
+
+def attn_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen, window=None, dq=None, dk=None,
+                    dv=None, ws=None):
+    """Backward of attn_fwd_varlen.  Returns (dq, dk, dv), each [total, H, D] bf16."""
+    total, H, D = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _need(t, n, (total, H, D), torch.bfloat16)
+    _need(lse, "lse", (H, total), torch.float32)
+    nseq = _cu(cu_seqlens, q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need(t, n, (total, H, D), torch.bfloat16)
+    need = attn_bwd_workspace_bytes(1, H, total, D)
+    if ws is None:
+        ws = torch.empty(need, device=q.device, dtype=torch.uint8)
+    rc = load().attn_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                dv.data_ptr(), cu_seqlens.data_ptr(), nseq, total, int(max_seqlen),
+                                H, D, _win(window, int(max_seqlen)), ws.data_ptr(),
+                                ws.numel() * ws.element_size(), _stream(q))
+    check(rc, "attn_bwd_varlen")
+    return dq, dk, dv
+
+
 class _Attention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, window):
@@ -268,6 +326,27 @@ class _Attention(torch.autograd.Function):
 def attention(q, k, v, window=None):
     """Differentiable windowed causal attention over [B, T, H, D] bf16 tensors."""
     return _Attention.apply(q, k, v, window)
+
+
+class _AttentionVarlen(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, cu_seqlens, max_seqlen, window):
+        o, lse = attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, window=window)
+        ctx.save_for_backward(q, k, v, o, lse, cu_seqlens)
+        ctx.max_seqlen, ctx.window = max_seqlen, window
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse, cu = ctx.saved_tensors
+        dq, dk, dv = attn_bwd_varlen(q, k, v, o, lse, do.contiguous(), cu, ctx.max_seqlen,
+                                     window=ctx.window)
+        return dq, dk, dv, None, None, None
+
+
+def attention_varlen(q, k, v, cu_seqlens, max_seqlen, window=None):
+    """Differentiable attention over packed sequences (documents): q, k, v [total, H, D] bf16."""
+    return _AttentionVarlen.apply(q, k, v, cu_seqlens, max_seqlen, window)
 
 
 class KVCache:

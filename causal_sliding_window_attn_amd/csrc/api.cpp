@@ -351,4 +351,96 @@ int attn_decode_step(const void* q, const void* knew, const void* vnew, void* kc
                     "attn_decode_step launch");
 }
 
+// Packed sequences (documents): shared argument checks of attn_fwd_varlen / attn_bwd_varlen.
+static int check_varlen(const char* what, const int* cu, int nseq, int total, int max_seqlen,
+                        int H, int D, int window) {
+  TRY(check_dims(what, nseq, H, max_seqlen, "max_seqlen", D, window));
+  if (total < 1) return fail(SWATTN_EINVAL, "%s: total = %d must be >= 1", what, total);
+  if (max_seqlen > total)
+    return fail(SWATTN_EINVAL, "%s: max_seqlen = %d exceeds total = %d", what, max_seqlen, total);
+  if (!cu) return fail(SWATTN_EINVAL, "%s: cu_seqlens is NULL", what);
+  if (reinterpret_cast<uintptr_t>(cu) & 3u)
+    return fail(SWATTN_EINVAL, "%s: cu_seqlens is not 4-byte aligned", what);
+  return SWATTN_OK;
+}
+
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens, int nseq, int total, int max_seqlen, int H, int D,
+                    int window, void* stream) {
+  TRY(check_varlen("attn_fwd_varlen", cu_seqlens, nseq, total, max_seqlen, H, D, window));
+  TRY(check_ptr(q, "q"));
+  TRY(check_ptr(k, "k"));
+  TRY(check_ptr(v, "v"));
+  TRY(check_ptr(o, "o"));
+  TRY(check_ptr(lse, "lse", true));
+  swattn::FwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.cu = cu_seqlens;
+  a.total = total;
+  a.row_stride = H * D;
+  a.H = H;
+  a.BH = nseq * H;
+  a.D = D;
+  a.T = max_seqlen;
+  a.kv_len = max_seqlen;
+  a.window = window;
+  a.scale_log2 = scale_log2_for(D);
+  (void)hipGetLastError();
+  return hip_status(swattn::launch_fwd(a, false, static_cast<hipStream_t>(stream)),
+                    "attn_fwd_varlen launch");
+}
+
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dout, void* dq, void* dk, void* dv, const int* cu_seqlens,
+                    int nseq, int total, int max_seqlen, int H, int D, int window, void* ws,
+                    size_t ws_bytes, void* stream) {
+  const char* what = "attn_bwd_varlen";
+  TRY(check_varlen(what, cu_seqlens, nseq, total, max_seqlen, H, D, window));
+  TRY(check_ptr(q, "q"));
+  TRY(check_ptr(k, "k"));
+  TRY(check_ptr(v, "v"));
+  TRY(check_ptr(o, "o"));
+  TRY(check_ptr(lse, "lse"));
+  TRY(check_ptr(dout, "dout"));
+  TRY(check_ptr(dq, "dq"));
+  TRY(check_ptr(dk, "dk"));
+  TRY(check_ptr(dv, "dv"));
+  const size_t need = attn_bwd_workspace_bytes(1, H, total, D);
+  if (!ws) return fail(SWATTN_EWORKSPACE, "%s: workspace is NULL (%zu bytes needed)", what, need);
+  if (!aligned16(ws)) return fail(SWATTN_EINVAL, "%s: workspace is not 16-byte aligned", what);
+  if (ws_bytes < need)
+    return fail(SWATTN_EWORKSPACE, "%s: workspace of %zu bytes < %zu needed", what, ws_bytes, need);
+  swattn::BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.lse = lse;
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.delta = static_cast<float*>(ws);
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + need / 2);
+  a.cu = cu_seqlens;
+  a.total = total;
+  a.row_stride = H * D;
+  a.H = H;
+  a.BH = nseq * H;
+  a.D = D;
+  a.T = max_seqlen;
+  a.window = window;
+  a.scale = (float)(1.0 / sqrt((double)D));
+  a.scale_log2 = scale_log2_for(D);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const int rc = hip_status(swattn::launch_bwd_dq(a, s), what);
+  if (rc != SWATTN_OK) return rc;
+  return hip_status(swattn::launch_bwd_dkdv(a, s), what);
+}
+
 }  // extern "C"

@@ -27,6 +27,31 @@ namespace swattn {
 constexpr int kBwdBC = 64;  // keys per tile in the dQ pass
 constexpr int kBwdBQ = 64;  // queries per tile in the dK/dV pass
 
+// Rows of head h of sequence b: dense [B, T, H, D] (statistics [B, H, T]) or packed sequences
+// ([total, H, D] rows cu[b] .. cu[b + 1] - 1, statistics [H, total]); packed offsets are clamped
+// so that any cu stays inside the buffers.
+struct BwdRows {
+  int T;         // rows of the sequence
+  int64_t base;  // element offset of its row 0 at head h
+  int64_t stat;  // index of its row 0 in lse, Delta and LSE * log2(e)
+};
+
+template <bool VARLEN>
+__device__ __forceinline__ BwdRows bwd_rows(const BwdArgs& p, int b, int h, int D) {
+  BwdRows r;
+  if constexpr (VARLEN) {
+    const int off = min(max(p.cu[b], 0), p.total);
+    r.T = min(min(max(p.cu[b + 1], off), p.total) - off, p.T);
+    r.base = (int64_t)off * p.row_stride + h * D;
+    r.stat = (int64_t)h * p.total + off;
+  } else {
+    r.T = p.T;
+    r.base = (int64_t)b * p.bstride + h * D;
+    r.stat = (int64_t)(b * p.H + h) * p.T;
+  }
+  return r;
+}
+
 // ------------------------------------------------------------------------------------------ dQ
 // dS^T = P^T (dP^T - Delta) for one 32-key block, in place in the S^T accumulator.
 template <bool MASK>
@@ -101,21 +126,23 @@ __device__ __forceinline__ void dq_step(const uint16_t* __restrict__ cur,
 
 // One job: query tile qt (NW waves x 32 queries) of head bh.  Returns with every wave past its
 // last read of the two-stage ring.
-template <int D, int NW>
+template <int D, int NW, bool VARLEN>
 __device__ __forceinline__ void dq_job(const BwdArgs& p, int bh, int qt, uint16_t* smem, int wave,
                                        int lane) {
   constexpr int BR = 32 * NW, BC = kBwdBC;
   constexpr int DK = D / 16, MB = D / 32, TILE = BC * D;
   const int half = lane >> 5, l32 = lane & 31;
   const int b = bh / p.H, h = bh % p.H;
-  const int T = p.T;
+  const BwdRows rw = bwd_rows<VARLEN>(p, b, h, D);
+  const int T = rw.T;
   const int q0 = qt * BR;
+  if (q0 >= T) return;
   const int w = min(p.window, T);
   const int kstart = max(0, q0 - w + 1);
   const int qend = min(q0 + BR, T);
   const int kt_begin = kstart / BC, kt_end = (qend - 1) / BC;
 
-  const int64_t base = (int64_t)b * p.bstride + h * D;
+  const int64_t base = rw.base;
   const int rs = p.row_stride;
   const uint16_t* kb = p.k + base;
   const uint16_t* vb = p.v + base;
@@ -137,7 +164,7 @@ __device__ __forceinline__ void dq_job(const BwdArgs& p, int bh, int qt, uint16_
     df[t] = ldg16(p.dout + roff + 16 * t);
     of[t] = ldg16(p.o + roff + 16 * t);
   }
-  const float lse_raw = p.lse[(int64_t)bh * T + qc];
+  const float lse_raw = p.lse[rw.stat + qc];
   float dsum = 0.f;
 #pragma unroll
   for (int t = 0; t < DK; ++t) {
@@ -157,8 +184,8 @@ __device__ __forceinline__ void dq_job(const BwdArgs& p, int bh, int qt, uint16_
   }
   const float delta = sum_with_partner(dsum);
   if (qvalid && half == 0) {
-    p.delta[(int64_t)bh * T + qi] = delta;
-    p.lse2[(int64_t)bh * T + qi] = lse_raw * kLog2e;  // the dK/dV pass reads LSE in base 2
+    p.delta[rw.stat + qi] = delta;
+    p.lse2[rw.stat + qi] = lse_raw * kLog2e;  // the dK/dV pass reads LSE in base 2
   }
   const float lse2 = qvalid ? lse_raw * kLog2e : 0.f;
 
@@ -205,7 +232,7 @@ __device__ __forceinline__ void dq_job(const BwdArgs& p, int bh, int qt, uint16_
 
 // Full-causal training pass (p.paired): workgroup = head + query-tile pair (j, n - 1 - j), short
 // tile first (pair_job).  Otherwise: workgroup = one query tile, longest tiles first.
-template <int D, int NW>
+template <int D, int NW, bool VARLEN>
 __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs p) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * kBwdBC * D];  // [stage][K|V]
   const int tid = threadIdx.x;
@@ -226,7 +253,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs p) {
 #pragma unroll 1
   for (int jx = 0; jx < njobs; ++jx) {
     if (jx) __syncthreads();  // every wave is done with the ring before the next job refills it
-    dq_job<D, NW>(p, bh, jx ? qt1 : qt0, smem, wave, lane);
+    dq_job<D, NW, VARLEN>(p, bh, jx ? qt1 : qt0, smem, wave, lane);
   }
 }
 
@@ -434,7 +461,7 @@ __device__ __forceinline__ void dkdv_loop(uint16_t* smem, uint16_t* myP, int qt_
 
 // One job: key tile kt (128 keys) of head bh, walking the query tiles that see it from the last
 // one down.  Returns with every wave past its last read of the ring and the P buffers.
-template <int D>
+template <int D, bool VARLEN>
 __device__ __forceinline__ void dkdv_job(const BwdArgs& p, int bh, int kt, uint16_t* smem,
                                          uint16_t* sPbuf, int wave, int lane) {
   constexpr int NW = kDkdvWaves, BK = 128, BQ = kBwdBQ;
@@ -444,18 +471,20 @@ __device__ __forceinline__ void dkdv_job(const BwdArgs& p, int bh, int kt, uint1
   const int kblk = wave & 3;
 
   const int b = bh / p.H, h = bh % p.H;
-  const int T = p.T;
+  const BwdRows rw = bwd_rows<VARLEN>(p, b, h, D);
+  const int T = rw.T;
   const int k0 = kt * BK;
+  if (k0 >= T) return;
   const int w = min(p.window, T);
   const int q_last = min(T, k0 + BK - 1 + w) - 1;
   const int qt_lo = k0 / BQ, qt_hi = q_last / BQ;
 
-  const int64_t base = (int64_t)b * p.bstride + h * D;
+  const int64_t base = rw.base;
   const int rs = p.row_stride;
   const uint16_t* qb = p.q + base;
   const uint16_t* db = p.dout + base;
-  const float* lseb = p.lse2 + (int64_t)bh * T;  // LSE * log2(e), from the dQ pass
-  const float* delb = p.delta + (int64_t)bh * T;
+  const float* lseb = p.lse2 + rw.stat;  // LSE * log2(e), from the dQ pass
+  const float* delb = p.delta + rw.stat;
 
   const RowDma<D, NW, BQ> dma(rs, wave, lane);
   dkdv_issue<D, NW>(dma, qb, db, lseb, delb, rs, qt_hi, T, smem, wave, lane);
@@ -502,7 +531,7 @@ __device__ __forceinline__ void dkdv_job(const BwdArgs& p, int bh, int kt, uint1
 // Full-causal training pass (p.paired): workgroup = head + key-tile pair (n - 1 - j, j), the short
 // tile (fewest queries) first, so that a head's workgroups start on the same query tiles together
 // (pair_job).  Otherwise: workgroup = one key tile, those seeing the most queries first.
-template <int D>
+template <int D, bool VARLEN>
 __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs p) {
   constexpr int SE = DkdvStage<D>::ELEMS, PE = DkdvStage<D>::PELEMS;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[kDkdvStages * SE];
@@ -525,7 +554,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs p)
 #pragma unroll 1
   for (int jx = 0; jx < njobs; ++jx) {
     if (jx) __syncthreads();  // every wave is done with the ring and P before the next job
-    dkdv_job<D>(p, bh, jx ? kt1 : kt0, smem, sPbuf, wave, lane);
+    dkdv_job<D, VARLEN>(p, bh, jx ? kt1 : kt0, smem, sPbuf, wave, lane);
   }
 }
 
@@ -535,10 +564,14 @@ static hipError_t launch_dq_d(const BwdArgs& a, hipStream_t s) {
   constexpr int NW = 4;
   BwdArgs p = a;
   p.n_tiles = (p.T + 32 * NW - 1) / (32 * NW);
-  p.paired = p.window >= p.T ? 1 : 0;  // tile pairs carry equal work under the full causal mask
+  // tile pairs carry equal work under the full causal mask over equal-length sequences
+  p.paired = (p.cu == nullptr && p.window >= p.T) ? 1 : 0;
   const unsigned per_head = p.paired ? (unsigned)(p.n_tiles + 1) / 2 : (unsigned)p.n_tiles;
   const unsigned grid = per_head * (unsigned)p.BH;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, NW>), dim3(grid), dim3(64 * NW), 0, s, p);
+  if (p.cu)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, true>), dim3(grid), dim3(64 * NW), 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, false>), dim3(grid), dim3(64 * NW), 0, s, p);
   return hipGetLastError();
 }
 
@@ -546,10 +579,14 @@ template <int D>
 static hipError_t launch_dkdv_d(const BwdArgs& a, hipStream_t s) {
   BwdArgs p = a;
   p.n_tiles = (p.T + 127) / 128;  // 128 keys per job
-  p.paired = p.window >= p.T ? 1 : 0;  // tile pairs carry equal work under the full causal mask
+  // tile pairs carry equal work under the full causal mask over equal-length sequences
+  p.paired = (p.cu == nullptr && p.window >= p.T) ? 1 : 0;
   const unsigned per_head = p.paired ? (unsigned)(p.n_tiles + 1) / 2 : (unsigned)p.n_tiles;
   const unsigned grid = per_head * (unsigned)p.BH;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(grid), dim3(64 * kDkdvWaves), 0, s, p);
+  if (p.cu)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(grid), dim3(64 * kDkdvWaves), 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(grid), dim3(64 * kDkdvWaves), 0, s, p);
   return hipGetLastError();
 }
 

@@ -216,7 +216,7 @@ __device__ __forceinline__ void fwd_run(int kt0, int kt1, int kt_end, int& st, u
 
 // One job: query tile qt (NW waves x 32 queries) of head bh, NS-stage K/V ring (prefetch NS - 1
 // tiles ahead).  Returns with every wave past its last read of the ring.
-template <int D, int NW, int NS>
+template <int D, int NW, int NS, bool VARLEN>
 __device__ __forceinline__ void fwd_job(const FwdArgs& p, int bh, int qt, uint16_t* smem,
                                         int wave, int lane) {
   constexpr int BR = 32 * NW;
@@ -228,7 +228,16 @@ __device__ __forceinline__ void fwd_job(const FwdArgs& p, int bh, int qt, uint16
   const int b = bh / p.H, h = bh % p.H;
 
   int L = p.kv_len;
-  if (p.lens) L = min(max(p.lens[b], 0), p.kv_len);
+  int64_t q_row0 = (int64_t)b * p.q_bstride, kv_row0 = (int64_t)b * p.kv_bstride;
+  int64_t lse0 = (int64_t)bh * p.lse_T;
+  if constexpr (VARLEN) {  // packed sequences; offsets clamped so any cu stays inside the buffers
+    const int off = min(max(p.cu[b], 0), p.total);
+    L = min(min(max(p.cu[b + 1], off), p.total) - off, p.kv_len);
+    q_row0 = kv_row0 = (int64_t)off * p.row_stride;
+    lse0 = (int64_t)h * p.total + off;
+  } else if (p.lens) {
+    L = min(max(p.lens[b], 0), p.kv_len);
+  }
   const int q0 = qt * BR;
   if (q0 >= L) return;
   const int w = min(p.window, L);
@@ -236,9 +245,9 @@ __device__ __forceinline__ void fwd_job(const FwdArgs& p, int bh, int qt, uint16
   const int qend = min(q0 + BR, L);
   const int kt_begin = kstart / BC, kt_end = (qend - 1) / BC;
 
-  const uint16_t* qb = p.q + (int64_t)b * p.q_bstride + h * D;
-  const uint16_t* kb = p.k + (int64_t)b * p.kv_bstride + h * D;
-  const uint16_t* vb = p.v + (int64_t)b * p.kv_bstride + h * D;
+  const uint16_t* qb = p.q + q_row0 + h * D;
+  const uint16_t* kb = p.k + kv_row0 + h * D;
+  const uint16_t* vb = p.v + kv_row0 + h * D;
   const int rs = p.row_stride;
 
   const int qa = q0 + 32 * wave;  // this wave's first query
@@ -288,7 +297,7 @@ __device__ __forceinline__ void fwd_job(const FwdArgs& p, int bh, int qt, uint16
   const float l_tot = sum_with_partner(S.l_run);
   if (!qvalid) return;
   const float inv = 1.f / l_tot;
-  uint16_t* ob = p.o + (int64_t)b * p.q_bstride + h * D + (int64_t)qi * rs;
+  uint16_t* ob = p.o + q_row0 + h * D + (int64_t)qi * rs;
 #pragma unroll
   for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -298,14 +307,13 @@ __device__ __forceinline__ void fwd_job(const FwdArgs& p, int bh, int qt, uint16
       st.y = pack_bf16x2(S.oacc[m][4 * j + 2] * inv, S.oacc[m][4 * j + 3] * inv);
       *reinterpret_cast<uint2*>(ob + m * 32 + 8 * j + 4 * half) = st;
     }
-  if (p.lse && half == 0)
-    p.lse[(int64_t)bh * p.lse_T + qi] = (S.m_use + __log2f(l_tot)) * kLn2;
+  if (p.lse && half == 0) p.lse[lse0 + qi] = (S.m_use + __log2f(l_tot)) * kLn2;
 }
 
 // PAIRED (full-causal training forward): workgroup = head + query-tile pair (j, n - 1 - j), the
 // short tile first, so that a head's workgroups start on the same K/V tiles together (pair_job).
 // Otherwise (prefill, sliding window): workgroup = one query tile, longest tiles first.
-template <int D, int NW, int NS, bool PAIRED>
+template <int D, int NW, int NS, bool PAIRED, bool VARLEN>
 __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 1 : 2)) void fwd_bf16_kernel(FwdArgs p) {
   static_assert((kFwdBC * D / 512) % NW == 0, "every wave issues the same number of DMA loads");
   __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * 2 * kFwdBC * D];  // [stage][K|V]
@@ -316,13 +324,13 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 1 : 2)) void fwd_bf16_kernel(Fw
   if (PAIRED) {
     const PairJob jb = pair_job(bid, p.BH, (p.n_qtiles + 1) / 2);
     const int qt1 = p.n_qtiles - 1 - jb.j;
-    fwd_job<D, NW, NS>(p, jb.bh, jb.j, smem, wave, lane);
+    fwd_job<D, NW, NS, false>(p, jb.bh, jb.j, smem, wave, lane);
     if (qt1 != jb.j) {
       __syncthreads();  // every wave is done with the ring before the next job refills it
-      fwd_job<D, NW, NS>(p, jb.bh, qt1, smem, wave, lane);
+      fwd_job<D, NW, NS, false>(p, jb.bh, qt1, smem, wave, lane);
     }
   } else {
-    fwd_job<D, NW, NS>(p, bid % p.BH, p.n_qtiles - 1 - bid / p.BH, smem, wave, lane);
+    fwd_job<D, NW, NS, VARLEN>(p, bid % p.BH, p.n_qtiles - 1 - bid / p.BH, smem, wave, lane);
   }
 }
 
@@ -442,12 +450,17 @@ static hipError_t launch_bf16(const FwdArgs& a, hipStream_t s) {
   FwdArgs p = a;
   p.n_qtiles = (p.T + 32 * NW - 1) / (32 * NW);
   // tile pairs carry equal work only when every query sees all earlier keys
-  if (p.lens == nullptr && p.window >= p.T && p.kv_len == p.T) {
-    const unsigned grid = (unsigned)(p.n_qtiles + 1) / 2 * (unsigned)p.BH;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, true>), dim3(grid), dim3(64 * NW), 0, s, p);
+  const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.BH;
+  if (p.cu) {
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, false, true>), dim3(grid), dim3(64 * NW), 0, s,
+                       p);
+  } else if (p.lens == nullptr && p.window >= p.T && p.kv_len == p.T) {
+    const unsigned pairs = (unsigned)(p.n_qtiles + 1) / 2 * (unsigned)p.BH;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, true, false>), dim3(pairs), dim3(64 * NW), 0, s,
+                       p);
   } else {
-    const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.BH;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, false>), dim3(grid), dim3(64 * NW), 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, false, false>), dim3(grid), dim3(64 * NW), 0, s,
+                       p);
   }
   return hipGetLastError();
 }

@@ -13,6 +13,9 @@ struct FwdArgs {
   uint16_t* o;
   float* lse;          // [BH, lse_T] or null
   const int* lens;     // per-batch valid length (prefill) or null (training: every row valid)
+  const int* cu;       // packed sequences: sequence b is rows cu[b] .. cu[b + 1] - 1 of
+                       // [total, H, D] (lse [H, total]), or null
+  int total;           // packed sequences: rows in q / k / v / o
   int64_t q_bstride;   // elements between batches of q / o
   int64_t kv_bstride;  // elements between batches of k / v
   int row_stride;      // elements between consecutive tokens (H * D)
@@ -37,6 +40,9 @@ struct BwdArgs {
   uint16_t* dv;
   float* delta;      // [BH, T] workspace: Delta_i = dO_i . O_i (written by the dQ pass)
   float* lse2;       // [BH, T] workspace: LSE_i * log2(e) (written by the dQ pass)
+  const int* cu;     // packed sequences (rows cu[b] .. cu[b + 1] - 1 of [total, H, D]; lse,
+                     // Delta and LSE * log2(e) as [H, total]), or null; T is then the longest
+  int total;         // packed sequences: rows in q / k / v / o / dO
   int64_t bstride;   // T * H * D
   int row_stride;    // H * D
   int H, BH, D, T, window;

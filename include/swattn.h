@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define SWATTN_ABI_VERSION 2  /* 2: attn_decode_step added */
+#define SWATTN_ABI_VERSION 3  /* 2: attn_decode_step; 3: attn_fwd_varlen, attn_bwd_varlen */
 
 typedef enum { SWATTN_BF16 = 0, SWATTN_F32 = 1 } swattn_dtype;
 
@@ -162,6 +162,32 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
 int attn_decode_step(const void* q, const void* knew, const void* vnew, void* kcache, void* vcache,
                      const int* pos, void* o, float* lse, int B, int H, int Lcap, int D,
                      int window, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Packed variable-length sequences (documents), for training and packed prefill.  A row of
+ * training data holds several documents separated by the beginning-of-sequence token (walkthrough,
+ * section "Midtraining": that token separates documents); here each document is one sequence and
+ * attends only to itself:
+ *   sequence s occupies rows cu_seqlens[s] .. cu_seqlens[s + 1] - 1 of q, k, v, o, dout, dq, dk,
+ *   dv, each [total, H, D] bf16; query i of s sees key j of s iff 0 <= i - j < window (positions
+ *   counted from the sequence's first row).  No key of another sequence is ever visible.
+ *   lse    [H, total] float32 (natural log); optional (NULL) in the forward, read by the backward.
+ *   cu_seqlens  device int32 [nseq + 1]: non-decreasing offsets, cu_seqlens[0] = 0 and
+ *          cu_seqlens[nseq] = total.  Values are clamped to [0, total] on the device, so no value
+ *          makes a kernel leave the buffers; an empty sequence is skipped.
+ *   max_seqlen  host int >= the longest sequence (it sizes the launch; rows of a longer sequence
+ *          past max_seqlen are not computed).  1 <= max_seqlen <= total.
+ *   ws / ws_bytes (backward): at least attn_bwd_workspace_bytes(1, H, total, D).
+ * bf16 only.  Each sequence gives, bit for bit, what attn_fwd / attn_bwd give for it alone
+ * (B = 1, T = its length).  Errors as attn_fwd / attn_bwd.
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens, int nseq, int total, int max_seqlen, int H, int D,
+                    int window, void* stream);
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dout, void* dq, void* dk, void* dv, const int* cu_seqlens,
+                    int nseq, int total, int max_seqlen, int H, int D, int window, void* ws,
+                    size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

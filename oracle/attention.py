@@ -13,6 +13,9 @@ What is computed, and where it comes from
 * The KV-cache Engine with its two inference phases, prefill and decode: walkthrough "A fully
   hand-made copy of ChatGPT for $100 and 8,000 lines of code" (followin.io), section "Pretraining",
   closing paragraph; and the nanochat launch post (web3.ouchyi.army), feature list.
+* Packed documents: training rows hold several documents separated by the beginning-of-sequence
+  token (same walkthrough, section "Midtraining").  ``forward_varlen`` / ``backward_varlen`` take
+  packed sequences in which each document attends only to itself.
 
 The pages print no formula.  The definition below is textbook scaled dot-product attention; the
 readings of what the pages leave open are:
@@ -50,6 +53,8 @@ __all__ = [
     "prefill",
     "kv_append",
     "decode",
+    "forward_varlen",
+    "backward_varlen",
 ]
 
 
@@ -264,3 +269,51 @@ def decode(q, kcache, vcache, lens, window=None):
             o[b, h] = (e @ vv) / l
             lse[b, h] = m + math.log(l)
     return o, lse
+
+
+def _segments(cu_seqlens):
+    cu = [int(x) for x in np.asarray(cu_seqlens).reshape(-1)]
+    return [(cu[s], cu[s + 1]) for s in range(len(cu) - 1)]
+
+
+def forward_varlen(q, k, v, cu_seqlens, window=None, threads=None):
+    """Packed sequences (documents): q, k, v [total, H, D]; sequence s is rows
+    cu_seqlens[s] .. cu_seqlens[s + 1] - 1 and attends only to itself, causally, with the window
+    counted from its own first row.  Returns O [total, H, D] and LSE [H, total] (float64)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    total, H, D = q.shape
+    segs = _segments(cu_seqlens)
+    o = np.full((total, H, D), np.nan)
+    lse = np.full((H, total), np.nan)
+    items = [(a, e, h) for a, e in segs if e > a for h in range(H)]
+
+    def one(item):
+        a, e, h = item
+        return head_forward(q[a:e, h], k[a:e, h], v[a:e, h], _eff_window(window, e - a))
+
+    for (a, e, h), (oh, lh) in zip(items, _map_heads(one, items, threads)):
+        o[a:e, h] = oh
+        lse[h, a:e] = lh
+    return o, lse
+
+
+def backward_varlen(q, k, v, do, cu_seqlens, window=None, threads=None):
+    """Backward of ``forward_varlen``: dQ, dK, dV [total, H, D] (float64)."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    total, H, D = q.shape
+    segs = _segments(cu_seqlens)
+    dq = np.full((total, H, D), np.nan)
+    dk = np.full((total, H, D), np.nan)
+    dv = np.full((total, H, D), np.nan)
+    items = [(a, e, h) for a, e in segs if e > a for h in range(H)]
+
+    def one(item):
+        a, e, h = item
+        return head_backward(q[a:e, h], k[a:e, h], v[a:e, h], do[a:e, h],
+                             _eff_window(window, e - a))
+
+    for (a, e, h), (gq, gk, gv, _) in zip(items, _map_heads(one, items, threads)):
+        dq[a:e, h] = gq
+        dk[a:e, h] = gk
+        dv[a:e, h] = gv
+    return dq, dk, dv

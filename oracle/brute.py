@@ -33,3 +33,29 @@ def fwd(q, k, v, w: int):
     p = softmax(scores, axis=1)
     lse = logsumexp(scores, axis=1)
     return p @ v, lse, p
+
+
+def doc_mask(cu_seqlens, w: int) -> np.ndarray:
+    """Allowed-set mask over packed documents, by explicit loops: query i sees key j iff both lie
+    in the same document, j <= i and i - j < w."""
+    cu = [int(x) for x in cu_seqlens]
+    total = cu[-1]
+    doc = np.empty(total, dtype=np.int64)
+    for s in range(len(cu) - 1):
+        for t in range(cu[s], cu[s + 1]):
+            doc[t] = s
+    m = np.zeros((total, total), dtype=bool)
+    for i in range(total):
+        for j in range(total):
+            m[i, j] = (doc[i] == doc[j]) and (j <= i) and (i - j < w)
+    return m
+
+
+def fwd_masked(q, k, v, m):
+    """One head over an explicit mask: q, k, v [N, D], m [N, N] -> O [N, D], LSE [N]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    scores = np.einsum("id,jd->ij", q, k) / np.sqrt(q.shape[1])
+    scores = np.where(m, scores, -np.inf)
+    return softmax(scores, axis=1) @ v, logsumexp(scores, axis=1)

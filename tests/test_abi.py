@@ -29,8 +29,9 @@ def lib():
 def test_header_declares_the_entry_points():
     names = set(declared_functions())
     assert {"attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_decode", "attn_prefill",
-            "attn_kv_append", "attn_decode_step", "attn_bwd_workspace_bytes",
-            "attn_decode_workspace_bytes", "attn_last_error", "attn_abi_version"} == names
+            "attn_kv_append", "attn_decode_step", "attn_fwd_varlen", "attn_bwd_varlen",
+            "attn_bwd_workspace_bytes", "attn_decode_workspace_bytes", "attn_last_error",
+            "attn_abi_version"} == names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -54,7 +55,7 @@ def test_nm_lists_only_c_symbols(lib):
 
 
 def test_abi_version(lib):
-    assert lib.attn_abi_version() == 2
+    assert lib.attn_abi_version() == 3
 
 
 P = 4096  # an aligned, non-null stand-in pointer: validation must fail before it is ever used
@@ -144,6 +145,44 @@ def test_decode_step_validation(lib):
     assert call(a7=P + 2) == -1  # lse alignment
     assert call(a11=80) == -2  # head dimension
     assert call(a10=0) == -1  # Lcap
+
+
+def test_varlen_validation(lib):
+    # q, k, v, o, lse, cu, nseq, total, max_seqlen, H, D, window, stream
+    ok = [P, P, P, P, None, P, 3, 100, 50, 2, 128, 8, None]
+
+    def fwd(**change):
+        a = list(ok)
+        for i, val in change.items():
+            a[int(i[1:])] = val
+        return lib.attn_fwd_varlen(*a)
+
+    assert fwd(a5=None) == -1 and "cu_seqlens" in err(lib)
+    assert fwd(a5=P + 2) == -1
+    assert fwd(a6=0) == -1  # nseq
+    assert fwd(a7=0) == -1  # total
+    assert fwd(a8=0) == -1  # max_seqlen
+    assert fwd(a8=101) == -1 and "max_seqlen" in err(lib)
+    assert fwd(a10=96) == -2  # head dimension
+    assert fwd(a11=0) == -1  # window
+    assert fwd(a0=None) == -1 and "q" in err(lib)
+    assert fwd(a4=P + 4) == -1  # lse alignment
+    need = lib.attn_bwd_workspace_bytes(1, 2, 100, 128)
+    # q, k, v, o, lse, dout, dq, dk, dv, cu, nseq, total, max_seqlen, H, D, window, ws, ws_bytes
+    bok = [P] * 10 + [3, 100, 50, 2, 128, 8, P, need, None]
+
+    def bwd(**change):
+        a = list(bok)
+        for i, val in change.items():
+            a[int(i[1:])] = val
+        return lib.attn_bwd_varlen(*a)
+
+    assert bwd(a17=need - 1) == -3 and "workspace" in err(lib)
+    assert bwd(a16=None) == -3
+    assert bwd(a4=None) == -1 and "lse" in err(lib)
+    assert bwd(a9=None) == -1 and "cu_seqlens" in err(lib)
+    assert bwd(a5=None) == -1 and "dout" in err(lib)
+    assert bwd(a12=200) == -1
 
 
 def test_last_error_is_thread_local(lib):

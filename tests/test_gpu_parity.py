@@ -460,3 +460,76 @@ def test_decode_step_graph_replays_match_eager(sw, B, H):
         lens_now = f64(eager.lens).astype(np.int64)
         o_r, _ = ref.decode(f64(ins[0][-1]), f64(eager.k[-1]), f64(eager.v[-1]), lens_now, 40)
         assert np.abs(f64(o_e[-1]) - o_r).max() <= O_TOL, f"replay {s}"
+
+
+# ------------------------------------------------------------- packed documents (varlen)
+def _packed(lengths, H, D, seed):
+    g = torch.Generator().manual_seed(seed)
+    total = int(sum(lengths))
+    cu = torch.tensor([0] + [int(x) for x in np.cumsum(lengths)], dtype=torch.int32)
+    q, k, v, do = (torch.randn(total, H, D, generator=g).to(torch.bfloat16) for _ in range(4))
+    return cu, q, k, v, do
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_varlen_matches_oracle(sw, D):
+    """Packed documents of assorted lengths (tile edges, a single token, an empty one) against the
+    oracle, forward and backward, for several windows."""
+    lengths = [129, 1, 64, 0, 300, 31, 65, 128, 33, 200]
+    H = 3
+    cu, q, k, v, do = _packed(lengths, H, D, 90 + D)
+    qd, kd, vd, dod, cud = (t.to(DEV) for t in (q, k, v, do, cu))
+    for window in (None, 1, 17, 64, 100):
+        o, lse = sw.attn_fwd_varlen(qd, kd, vd, cud, max(lengths), window=window)
+        g = sw.attn_bwd_varlen(qd, kd, vd, o, lse, dod, cud, max(lengths), window=window)
+        torch.cuda.synchronize()
+        o_r, lse_r = ref.forward_varlen(f64(q), f64(k), f64(v), cu.numpy(), window)
+        assert np.abs(f64(o) - o_r).max() <= O_TOL, f"window {window}"
+        assert np.abs(f64(lse) - lse_r).max() <= LSE_TOL, f"window {window}"
+        g_r = ref.backward_varlen(f64(q), f64(k), f64(v), f64(do), cu.numpy(), window)
+        check_grads(g, g_r, tag=f"varlen D{D} window {window}")
+
+
+def test_varlen_is_each_document_alone_bit_for_bit(sw):
+    """Each packed document gives exactly what the dense entry points give for it alone."""
+    lengths = [70, 1, 129, 256, 0, 33]
+    H, D = 2, 128
+    cu, q, k, v, do = _packed(lengths, H, D, 95)
+    qd, kd, vd, dod, cud = (t.to(DEV) for t in (q, k, v, do, cu))
+    for window in (None, 40):
+        o, lse = sw.attn_fwd_varlen(qd, kd, vd, cud, max(lengths), window=window)
+        dq, dk, dv = sw.attn_bwd_varlen(qd, kd, vd, o, lse, dod, cud, max(lengths), window=window)
+        for a, e in zip(cu[:-1].tolist(), cu[1:].tolist()):
+            if e == a:
+                continue
+            sl = slice(a, e)
+            one = [t[sl].unsqueeze(0).contiguous() for t in (qd, kd, vd, dod)]
+            od, lsed = sw.attn_fwd(one[0], one[1], one[2], window=window)
+            gd = sw.attn_bwd(one[0], one[1], one[2], od, lsed, one[3], window=window)
+            torch.cuda.synchronize()
+            assert torch.equal(o[sl], od[0]) and torch.equal(lse[:, sl], lsed[0]), (window, a)
+            for x, y in zip((dq, dk, dv), gd):
+                assert torch.equal(x[sl], y[0]), (window, a)
+
+
+def test_varlen_autograd_and_rows_past_max_seqlen(sw):
+    lengths = [40, 90, 7]
+    H, D = 2, 64
+    cu, q, k, v, do = _packed(lengths, H, D, 97)
+    cud = cu.to(DEV)
+    qd, kd, vd = (t.to(DEV).requires_grad_() for t in (q, k, v))
+    o = sw.attention_varlen(qd, kd, vd, cud, max(lengths), window=25)
+    o.backward(do.to(DEV))
+    g_r = ref.backward_varlen(f64(q), f64(k), f64(v), f64(do), cu.numpy(), 25)
+    check_grads((qd.grad, kd.grad, vd.grad), g_r, tag="varlen autograd")
+    # max_seqlen below the longest document: its rows past max_seqlen are left untouched, the
+    # rows before it (which see only earlier keys) are exact
+    o2 = torch.full_like(qd, 7.0, requires_grad=False)
+    sw.attn_fwd_varlen(qd.detach(), kd.detach(), vd.detach(), cud, 64, o=o2, window=25,
+                       want_lse=False)
+    torch.cuda.synchronize()
+    o_r, _ = ref.forward_varlen(f64(q), f64(k), f64(v), cu.numpy(), 25)
+    a = int(cu[1])
+    assert torch.all(o2[a + 64:a + 90] == 7.0)
+    assert np.abs(f64(o2[a:a + 64]) - o_r[a:a + 64]).max() <= O_TOL
+    assert np.abs(f64(o2[:a]) - o_r[:a]).max() <= O_TOL

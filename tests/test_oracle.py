@@ -394,3 +394,67 @@ def _mut_scale(qr, qpos, k, v, w, return_p=False):  # 1/D instead of 1/sqrt(D)
 def test_planted_mistake_is_caught(monkeypatch, target, mutant):
     monkeypatch.setattr(A, target, mutant)
     assert not _pins_pass()
+
+
+# ---------------------------------------------------------------- packed documents (varlen)
+# Training rows hold several documents separated by the beginning-of-sequence token (walkthrough,
+# section "Midtraining"); each packed document attends only to itself.
+VARLEN_CU = [0, 1, 9, 9, 26, 40]  # lengths 1, 8, 0 (empty), 17, 14
+
+
+@pytest.mark.parametrize("w", [1, 3, 8, 100])
+def test_varlen_forward_matches_brute_document_mask(w):
+    rng = np.random.default_rng(50 + w)
+    total, H, D = VARLEN_CU[-1], 2, 8
+    q, k, v = (rng.standard_normal((total, H, D)) for _ in range(3))
+    o, lse = A.forward_varlen(q, k, v, VARLEN_CU, w)
+    m = brute.doc_mask(VARLEN_CU, w)
+    for h in range(H):
+        ob, lb = brute.fwd_masked(q[:, h], k[:, h], v[:, h], m)
+        np.testing.assert_allclose(o[:, h], ob, atol=1e-12)
+        np.testing.assert_allclose(lse[h], lb, atol=1e-12)
+
+
+@pytest.mark.parametrize("w", [2, 100])
+def test_varlen_backward_matches_autograd_of_document_mask(w):
+    rng = np.random.default_rng(60 + w)
+    total, H, D = VARLEN_CU[-1], 2, 8
+    q, k, v, g = (rng.standard_normal((total, H, D)) for _ in range(4))
+    dq, dk, dv = A.backward_varlen(q, k, v, g, VARLEN_CU, w)
+    m = torch.tensor(brute.doc_mask(VARLEN_CU, w))
+    for h in range(H):
+        tq, tk, tv = (torch.tensor(x[:, h], requires_grad=True) for x in (q, k, v))
+        s = ((tq @ tk.T) / math.sqrt(D)).masked_fill(~m, float("-inf"))
+        (torch.softmax(s, dim=1) @ tv).backward(torch.tensor(g[:, h]))
+        np.testing.assert_allclose(dq[:, h], tq.grad.numpy(), atol=1e-10)
+        np.testing.assert_allclose(dk[:, h], tk.grad.numpy(), atol=1e-10)
+        np.testing.assert_allclose(dv[:, h], tv.grad.numpy(), atol=1e-10)
+
+
+def test_varlen_documents_are_isolated():
+    """Changing one document's tokens leaves every other document's outputs unchanged, and a
+    boundary moved by one row changes them (the pin sees the boundary)."""
+    rng = np.random.default_rng(70)
+    total, H, D = VARLEN_CU[-1], 1, 8
+    q, k, v = (rng.standard_normal((total, H, D)) for _ in range(3))
+    o1, _ = A.forward_varlen(q, k, v, VARLEN_CU)
+    k2 = k.copy()
+    k2[9:26] += rng.standard_normal((17, H, D))
+    o2, _ = A.forward_varlen(q, k2, v, VARLEN_CU)
+    assert np.array_equal(o1[:9], o2[:9]) and np.array_equal(o1[26:], o2[26:])
+    assert not np.allclose(o1[9:26], o2[9:26])
+    shifted = [0, 1, 10, 10, 26, 40]
+    o3, _ = A.forward_varlen(q, k, v, shifted)
+    m = brute.doc_mask(VARLEN_CU, total)
+    ob, _ = brute.fwd_masked(q[:, 0], k[:, 0], v[:, 0], m)
+    assert np.abs(o3[:, 0] - ob).max() > 1e-3
+
+
+def test_varlen_one_sequence_is_the_dense_forward():
+    rng = np.random.default_rng(80)
+    T, H, D = 23, 2, 8
+    q, k, v, g = (rng.standard_normal((T, H, D)) for _ in range(4))
+    o, lse = A.forward_varlen(q, k, v, [0, T], 5)
+    od, lsed = A.forward(q[None], k[None], v[None], 5)
+    np.testing.assert_allclose(o, od[0], atol=1e-13)
+    np.testing.assert_allclose(lse, lsed[0], atol=1e-13)

@@ -44,6 +44,33 @@ D26_WINDOWS = (512, None, 512, None)
 D26_B, D26_T, D26_H, D26_D, D26_SEED = 16, 2048, 13, 128, 3
 
 
+# Packed documents in the d20 rows: each of the 32 rows of 2048 tokens holds consecutive
+# documents, which the beginning-of-sequence token separates (walkthrough, section "Midtraining");
+# a document that runs past the end of a row is cut there and continues as the next row's first
+# document, so every row boundary is a document boundary.  The pages give no document-length
+# distribution (FineWeb-EDU is not used here): lengths are seeded log-normal draws, median 600
+# tokens, log-sigma 1.0, rounded and clipped to [16, 8192].
+D20_PACKED_SEED = 5
+
+
+def d20_packed_cu(B: int = 32, T: int = 2048, seed: int = D20_PACKED_SEED, median: float = 600.0,
+                  sigma: float = 1.0) -> torch.Tensor:
+    """Sequence offsets (int32 [nseq + 1]) of the packed documents over B rows of T tokens."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    cu, carry = [0], 0
+    for b in range(B):
+        pos = 0
+        while pos < T:
+            if carry == 0:
+                z = float(torch.randn((), generator=g, dtype=torch.float64))
+                carry = int(min(max(round(median * float(torch.tensor(sigma * z).exp())), 16), 8192))
+            take = min(carry, T - pos)
+            pos += take
+            carry -= take
+            cu.append(b * T + pos)
+    return torch.tensor(cu, dtype=torch.int32)
+
+
 def _unit_rms(x: torch.Tensor) -> torch.Tensor:
     # per-(b, t, h) rescaling of the raw draw to unit root-mean-square over D (input shaping only)
     return x / x.pow(2).mean(dim=-1, keepdim=True).sqrt()
