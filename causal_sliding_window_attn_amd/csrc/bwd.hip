@@ -380,7 +380,18 @@ __device__ __forceinline__ void dkdv_swave(const uint16_t* __restrict__ cur,
 #pragma unroll
   for (int qb2 = 0; qb2 < BQ / 32; ++qb2) {
     if (!dkdv_block_live(qt, qb2, ka, T, w)) continue;
-    f32x16 dp = zero16();
+    // the accumulator starts at the rows' Delta (the broadcast reads land in its own row order)
+    // and vf holds -V, so the chain leaves Delta - dP and dS = P * that carries a sign that the
+    // final scale of dK removes
+    f32x16 dp;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 d4 = *reinterpret_cast<const float4*>(sDl + 32 * qb2 + 8 * j + 4 * half);
+      dp[4 * j + 0] = d4.x;
+      dp[4 * j + 1] = d4.y;
+      dp[4 * j + 2] = d4.z;
+      dp[4 * j + 3] = d4.w;
+    }
 #pragma unroll
     for (int t = 0; t < DK; ++t) dp = mfma32(rc_frag<D>(sO, lo, qb2, t), vf[t], dp);
     sched_mfma_chain<DK, 1, DK>();
@@ -388,16 +399,10 @@ __device__ __forceinline__ void dkdv_swave(const uint16_t* __restrict__ cur,
     const uint4 pw[2] = {src[lane], src[64 + lane]};
     const uint32_t* pu = reinterpret_cast<const uint32_t*>(pw);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 d4 = *reinterpret_cast<const float4*>(sDl + 32 * qb2 + 8 * j + 4 * half);
-      const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * j + i;  // P slot r is bf16 element r of the packed pair (u = r / 8)
-        const uint32_t word = pu[r >> 1];
-        const float pr = (r & 1) ? bf16_hi(word) : bf16_lo(word);
-        dp[r] = pr * (dp[r] - dv[i]);
-      }
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t word = pu[r >> 1];  // P slot r is bf16 element r of the packed pair
+      const float pr = (r & 1) ? bf16_hi(word) : bf16_lo(word);
+      dp[r] = pr * dp[r];
     }
     const uint4 df0 = pack_frag(dp, 0), df1 = pack_frag(dp, 1);
     __builtin_amdgcn_sched_barrier(0);
@@ -508,6 +513,14 @@ __device__ __forceinline__ void dkdv_job(const BwdArgs& p, int bh, int kt, uint1
   if (!kvalid)
 #pragma unroll
     for (int t = 0; t < DK; ++t) frag[t] = make_uint4(0, 0, 0, 0);
+  if (!pwave)  // -V: the dS waves' dP chain accumulates onto Delta
+#pragma unroll
+    for (int t = 0; t < DK; ++t) {
+      frag[t].x ^= 0x80008000u;
+      frag[t].y ^= 0x80008000u;
+      frag[t].z ^= 0x80008000u;
+      frag[t].w ^= 0x80008000u;
+    }
   f32x16 acc[MB];  // dV^T (P waves) or dK^T (dS waves)
 #pragma unroll
   for (int m = 0; m < MB; ++m) acc[m] = zero16();
@@ -522,7 +535,7 @@ __device__ __forceinline__ void dkdv_job(const BwdArgs& p, int bh, int kt, uint1
                             p.scale_log2, frag, acc, lo, dma, wave, lane);
 
   if (!kvalid) return;
-  const float sc = pwave ? 1.f : p.scale;
+  const float sc = pwave ? 1.f : -p.scale;  // the dS waves accumulated -dK^T
   uint16_t* out = (pwave ? p.dv : p.dk) + base + (int64_t)kj * rs;
 #pragma unroll
   for (int m = 0; m < MB; ++m)
