@@ -15,7 +15,8 @@ visible cache row read once, plus q and o), next to a plain streaming read of th
 (the rate this GPU sustains at that size), and ``decode.step_graph`` the same decode step for all
 30 layers as one replay of a captured HIP graph (attn_decode_step: append and decode in one launch
 per layer); ``prefill`` TFLOP/s; ``varlen`` the d20 rows re-read as packed documents that attend
-only to themselves (attn_fwd_varlen / attn_bwd_varlen).  ``roofline`` describes the
+only to themselves (attn_fwd_varlen / attn_bwd_varlen); ``qknorm`` the d20 layer with RMS-normalised
+q and k (attn_fwd_qknorm / attn_bwd_qknorm).  ``roofline`` describes the
 longest-running MFMA kernel; ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
 d20 workload on the host cores.  One JSON line goes to stdout; progress goes to stderr.
 """
@@ -132,6 +133,8 @@ def main() -> int:
                     help="skip the streaming-read reference of the decode roofline")
     ap.add_argument("--no-step-graph", action="store_true",
                     help="skip the graph-replayed whole-model decode step measurement")
+    ap.add_argument("--no-qknorm", action="store_true",
+                    help="skip the QK-norm (normalised q, k) fwd+bwd measurement")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the packed-document (varlen) fwd+bwd measurement")
     ap.add_argument("--calib-copy-mib", type=int, default=1024,
@@ -332,6 +335,29 @@ def main() -> int:
                               "lengths, median 600, cut at row ends), same q, k, v, dO"}
         del ov, lsev, gv, wsv
 
+    # QK-norm on the d20 layer: the same q, k, v, dO; forward = norm pass + attention on the
+    # normalised rows, backward = both passes with the norm's backward in their epilogues
+    qknorm = None
+    if not args.no_qknorm:
+        log("QK-norm d20 layer: forward + backward ...")
+        reps = max(args.steps, 5)
+        ev_q = [[Ev() for _ in range(3)] for _ in range(reps + 2)]
+        gq = [torch.empty_like(q) for _ in range(3)]
+        for i in range(reps + 2):
+            ev_q[i][0].record()
+            oq, lq, qn_, kn_, rq_, rk_ = sw.attn_fwd_qknorm(q, k, v, window=win)
+            ev_q[i][1].record()
+            sw.attn_bwd_qknorm(qn_, kn_, v, oq, lq, do, rq_, rk_, window=win, dq=gq[0], dk=gq[1],
+                               dv=gq[2], ws=ws_b)
+            ev_q[i][2].record()
+        torch.cuda.synchronize()
+        tq_f = sum(e[0].elapsed_time(e[1]) for e in ev_q[2:]) / reps * 1e-3
+        tq_b = sum(e[1].elapsed_time(e[2]) for e in ev_q[2:]) / reps * 1e-3
+        qknorm = {"TFLOP/s": round((F_fwd + F_dq + F_dkdv) / (tq_f + tq_b) / 1e12, 2),
+                  "fwd_ms": round(tq_f * 1e3, 4), "bwd_ms": round(tq_b * 1e3, 4),
+                  "note": "fwd includes the norm pass; FLOPs are the attention's only"}
+        del gq, oq, lq, qn_, kn_, rq_, rk_
+
     # the whole 30-layer decode step (append + decode per layer, one launch each) captured in one
     # HIP graph and replayed per token; timed per replay with events, outside the timed region
     step_graph = None
@@ -400,6 +426,7 @@ def main() -> int:
                    "step_graph": step_graph},
         "prefill": {"TFLOP/s": round(pre_flops / t_pre / 1e12, 2), "ms_per_layer": round(t_pre * 1e3, 4)},
         "varlen": varlen,
+        "qknorm": qknorm,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "device": props.name,

@@ -20,9 +20,12 @@ __all__ = [
     "attn_abi_version", "attn_last_error", "attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv",
     "attn_bwd_workspace_bytes",
     "attn_prefill", "attn_kv_append", "attn_decode", "attn_decode_step",
-    "attn_decode_workspace_bytes", "attn_fwd_varlen", "attn_bwd_varlen", "attention",
-    "attention_varlen", "KVCache", "DecodeStepGraph", "FULL",
+    "attn_decode_workspace_bytes", "attn_fwd_varlen", "attn_bwd_varlen", "attn_fwd_qknorm",
+    "attn_bwd_qknorm", "attention", "attention_varlen", "attention_qknorm", "KVCache",
+    "DecodeStepGraph", "FULL", "QKNORM_EPS",
 ]
+
+QKNORM_EPS = 1e-6  # default eps of the QK RMS norm (the pages do not give one)
 
 FULL = 2 ** 31 - 1  # a window that is never smaller than the sequence: full causal attention
 
@@ -308,6 +311,51 @@ def attn_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen, window=None, 
     return dq, dk, dv
 
 
+def attn_fwd_qknorm(q, k, v, window=None, eps=QKNORM_EPS, o=None, want_lse=True):
+    """Attention over RMS-normalised q and k rows ([B, T, H, D] bf16).  Returns
+    (o, lse, qn, kn, rq, rk): the normalised rows and 1 / rms per row [B, H, T] feed the backward."""
+    B, T, H, D = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, (B, T, H, D), torch.bfloat16)
+    qn, kn = torch.empty_like(q), torch.empty_like(k)
+    rq = torch.empty((B, H, T), device=q.device, dtype=torch.float32)
+    rk = torch.empty_like(rq)
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", (B, T, H, D), torch.bfloat16)
+    lse = torch.empty((B, H, T), device=q.device, dtype=torch.float32) if want_lse else None
+    rc = load().attn_fwd_qknorm(q.data_ptr(), k.data_ptr(), v.data_ptr(), qn.data_ptr(),
+                                kn.data_ptr(), rq.data_ptr(), rk.data_ptr(), o.data_ptr(),
+                                _ptr(lse), B, H, T, D, _win(window, T), float(eps), _stream(q))
+    check(rc, "attn_fwd_qknorm")
+    return o, lse, qn, kn, rq, rk
+
+
+def attn_bwd_qknorm(qn, kn, v, o, lse, dout, rq, rk, window=None, dq=None, dk=None, dv=None,
+                    ws=None):
+    """Backward of attn_fwd_qknorm: (dq, dk, dv) with respect to the raw q, k and v."""
+    B, T, H, D = qn.shape
+    for t, n in ((qn, "qn"), (kn, "kn"), (v, "v"), (o, "o"), (dout, "dout")):
+        _need(t, n, (B, T, H, D), torch.bfloat16)
+    for t, n in ((lse, "lse"), (rq, "rq"), (rk, "rk")):
+        _need(t, n, (B, H, T), torch.float32)
+    dq = torch.empty_like(qn) if dq is None else dq
+    dk = torch.empty_like(kn) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need(t, n, (B, T, H, D), torch.bfloat16)
+    need = attn_bwd_workspace_bytes(B, H, T, D)
+    if ws is None:
+        ws = torch.empty(need, device=qn.device, dtype=torch.uint8)
+    rc = load().attn_bwd_qknorm(qn.data_ptr(), kn.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), dout.data_ptr(), rq.data_ptr(), rk.data_ptr(),
+                                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, T, D,
+                                _win(window, T), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                _stream(qn))
+    check(rc, "attn_bwd_qknorm")
+    return dq, dk, dv
+
+
 class _Attention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, window):
@@ -342,6 +390,27 @@ class _AttentionVarlen(torch.autograd.Function):
         dq, dk, dv = attn_bwd_varlen(q, k, v, o, lse, do.contiguous(), cu, ctx.max_seqlen,
                                      window=ctx.window)
         return dq, dk, dv, None, None, None
+
+
+class _AttentionQKNorm(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, window, eps):
+        o, lse, qn, kn, rq, rk = attn_fwd_qknorm(q, k, v, window=window, eps=eps)
+        ctx.save_for_backward(qn, kn, v, o, lse, rq, rk)
+        ctx.window = window
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        qn, kn, v, o, lse, rq, rk = ctx.saved_tensors
+        dq, dk, dv = attn_bwd_qknorm(qn, kn, v, o, lse, do.contiguous(), rq, rk, window=ctx.window)
+        return dq, dk, dv, None, None
+
+
+def attention_qknorm(q, k, v, window=None, eps=QKNORM_EPS):
+    """Differentiable attention over RMS-normalised q and k ([B, T, H, D] bf16): the norm has no
+    parameters; gradients flow back to the raw q and k."""
+    return _AttentionQKNorm.apply(q, k, v, window, eps)
 
 
 def attention_varlen(q, k, v, cu_seqlens, max_seqlen, window=None):

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libswattn.so")
-SOURCES = ["api.cpp", "fwd.hip", "bwd.hip", "decode.hip"]
+SOURCES = ["api.cpp", "fwd.hip", "bwd.hip", "decode.hip", "norm.hip"]
 # measurement helper used by bench.py only (streaming-read reference for the decode roofline)
 PROBE_LIB = os.path.join(PKG, "libswattn_probe.so")
 PROBE_SOURCES = ["stream_probe.hip"]

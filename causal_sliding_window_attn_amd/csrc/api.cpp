@@ -121,7 +121,7 @@ enum BwdPass { kBoth, kDq, kDkdv };
 int bwd_common(const char* what, BwdPass pass, const void* q, const void* k, const void* v,
                const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
                int B, int H, int T, int D, int window, int dtype, void* ws, size_t ws_bytes,
-               void* stream) {
+               void* stream, const float* rq = nullptr, const float* rk = nullptr) {
   TRY(check_dims(what, B, H, T, "T", D, window));
   if (dtype != SWATTN_BF16)
     return fail(SWATTN_EUNSUPPORTED, "%s: only bf16 (dtype 0) is implemented, got %d", what, dtype);
@@ -160,6 +160,8 @@ int bwd_common(const char* what, BwdPass pass, const void* q, const void* k, con
   a.D = D;
   a.T = T;
   a.window = window;
+  a.rq = rq;
+  a.rk = rk;
   a.scale = (float)(1.0 / sqrt((double)D));
   a.scale_log2 = scale_log2_for(D);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -441,6 +443,67 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
   const int rc = hip_status(swattn::launch_bwd_dq(a, s), what);
   if (rc != SWATTN_OK) return rc;
   return hip_status(swattn::launch_bwd_dkdv(a, s), what);
+}
+
+int attn_fwd_qknorm(const void* q, const void* k, const void* v, void* qn, void* kn, float* rq,
+                    float* rk, void* o, float* lse, int B, int H, int T, int D, int window,
+                    float eps, void* stream) {
+  TRY(check_dims("attn_fwd_qknorm", B, H, T, "T", D, window));
+  if (!(eps >= 0.f) || !isfinite(eps))
+    return fail(SWATTN_EINVAL, "attn_fwd_qknorm: eps = %g must be finite and >= 0", (double)eps);
+  TRY(check_ptr(q, "q"));
+  TRY(check_ptr(k, "k"));
+  TRY(check_ptr(v, "v"));
+  TRY(check_ptr(qn, "qn"));
+  TRY(check_ptr(kn, "kn"));
+  TRY(check_ptr(rq, "rq"));
+  TRY(check_ptr(rk, "rk"));
+  TRY(check_ptr(o, "o"));
+  TRY(check_ptr(lse, "lse", true));
+  swattn::NormArgs na{};
+  na.q = static_cast<const uint16_t*>(q);
+  na.k = static_cast<const uint16_t*>(k);
+  na.qn = static_cast<uint16_t*>(qn);
+  na.kn = static_cast<uint16_t*>(kn);
+  na.rq = rq;
+  na.rk = rk;
+  na.B = B;
+  na.T = T;
+  na.H = H;
+  na.D = D;
+  na.eps = eps;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  TRY(hip_status(swattn::launch_qk_rmsnorm(na, s), "attn_fwd_qknorm norm launch"));
+  swattn::FwdArgs a{};
+  a.q = static_cast<const uint16_t*>(qn);
+  a.k = static_cast<const uint16_t*>(kn);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.q_bstride = a.kv_bstride = (int64_t)T * H * D;
+  a.row_stride = H * D;
+  a.H = H;
+  a.BH = B * H;
+  a.D = D;
+  a.T = T;
+  a.kv_len = T;
+  a.window = window;
+  a.lse_T = T;
+  a.scale_log2 = scale_log2_for(D);
+  return hip_status(swattn::launch_fwd(a, false, s), "attn_fwd_qknorm launch");
+}
+
+int attn_bwd_qknorm(const void* qn, const void* kn, const void* v, const void* o, const float* lse,
+                    const void* dout, const float* rq, const float* rk, void* dq, void* dk,
+                    void* dv, int B, int H, int T, int D, int window, void* ws, size_t ws_bytes,
+                    void* stream) {
+  if (!rq) return fail(SWATTN_EINVAL, "attn_bwd_qknorm: rq is NULL");
+  if (!rk) return fail(SWATTN_EINVAL, "attn_bwd_qknorm: rk is NULL");
+  if (!aligned16(rq) || !aligned16(rk))
+    return fail(SWATTN_EINVAL, "attn_bwd_qknorm: rq / rk are not 16-byte aligned");
+  return bwd_common("attn_bwd_qknorm", kBoth, qn, kn, v, o, lse, dout, dq, dk, dv, B, H, T, D,
+                    window, SWATTN_BF16, ws, ws_bytes, stream, rq, rk);
 }
 
 }  // extern "C"

@@ -36,6 +36,41 @@ struct BwdRows {
   int64_t stat;  // index of its row 0 in lse, Delta and LSE * log2(e)
 };
 
+// QK-norm backward, fused into a pass's epilogue.  With y = x / rms(x) the normalised row (the
+// attention's input, re-read here in the accumulator's element order), g = acc * sc the gradient
+// with respect to y and r = 1 / rms(x):  dx = r (g - y (g . y) / D).  A lane and its partner
+// (lane ^ 32) hold the two halves of the row.
+template <int D>
+__device__ __forceinline__ void store_through_rmsnorm(const f32x16 (&acc)[D / 32], float sc,
+                                                      const uint16_t* yrow, float r,
+                                                      uint16_t* out, int half) {
+  constexpr int MB = D / 32;
+  uint2 y[MB][4];
+  float dot = 0.f;
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      y[m][j] = *reinterpret_cast<const uint2*>(yrow + m * 32 + 8 * j + 4 * half);
+      dot = fmaf(acc[m][4 * j + 0] * sc, bf16_lo(y[m][j].x), dot);
+      dot = fmaf(acc[m][4 * j + 1] * sc, bf16_hi(y[m][j].x), dot);
+      dot = fmaf(acc[m][4 * j + 2] * sc, bf16_lo(y[m][j].y), dot);
+      dot = fmaf(acc[m][4 * j + 3] * sc, bf16_hi(y[m][j].y), dot);
+    }
+  const float c = sum_with_partner(dot) / (float)D;
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint2 st;
+      st.x = pack_bf16x2(r * (acc[m][4 * j + 0] * sc - bf16_lo(y[m][j].x) * c),
+                         r * (acc[m][4 * j + 1] * sc - bf16_hi(y[m][j].x) * c));
+      st.y = pack_bf16x2(r * (acc[m][4 * j + 2] * sc - bf16_lo(y[m][j].y) * c),
+                         r * (acc[m][4 * j + 3] * sc - bf16_hi(y[m][j].y) * c));
+      *reinterpret_cast<uint2*>(out + m * 32 + 8 * j + 4 * half) = st;
+    }
+}
+
 template <bool VARLEN>
 __device__ __forceinline__ BwdRows bwd_rows(const BwdArgs& p, int b, int h, int D) {
   BwdRows r;
@@ -126,7 +161,7 @@ __device__ __forceinline__ void dq_step(const uint16_t* __restrict__ cur,
 
 // One job: query tile qt (NW waves x 32 queries) of head bh.  Returns with every wave past its
 // last read of the two-stage ring.
-template <int D, int NW, bool VARLEN>
+template <int D, int NW, bool VARLEN, bool QKN>
 __device__ __forceinline__ void dq_job(const BwdArgs& p, int bh, int qt, uint16_t* smem, int wave,
                                        int lane) {
   constexpr int BR = 32 * NW, BC = kBwdBC;
@@ -219,6 +254,11 @@ __device__ __forceinline__ void dq_job(const BwdArgs& p, int bh, int qt, uint16_
   if (!qvalid) return;
   const float sc = p.scale;
   uint16_t* out = p.dq + base + (int64_t)qi * rs;
+  if constexpr (QKN) {  // dq with respect to the raw rows; p.q holds the normalised ones
+    store_through_rmsnorm<D>(dqacc, sc, p.q + base + (int64_t)qi * rs, p.rq[rw.stat + qi], out,
+                             half);
+    return;
+  }
 #pragma unroll
   for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -232,7 +272,7 @@ __device__ __forceinline__ void dq_job(const BwdArgs& p, int bh, int qt, uint16_
 
 // Full-causal training pass (p.paired): workgroup = head + query-tile pair (j, n - 1 - j), short
 // tile first (pair_job).  Otherwise: workgroup = one query tile, longest tiles first.
-template <int D, int NW, bool VARLEN>
+template <int D, int NW, bool VARLEN, bool QKN>
 __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs p) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * kBwdBC * D];  // [stage][K|V]
   const int tid = threadIdx.x;
@@ -253,7 +293,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs p) {
 #pragma unroll 1
   for (int jx = 0; jx < njobs; ++jx) {
     if (jx) __syncthreads();  // every wave is done with the ring before the next job refills it
-    dq_job<D, NW, VARLEN>(p, bh, jx ? qt1 : qt0, smem, wave, lane);
+    dq_job<D, NW, VARLEN, QKN>(p, bh, jx ? qt1 : qt0, smem, wave, lane);
   }
 }
 
@@ -473,7 +513,7 @@ __device__ __forceinline__ void dkdv_loop(uint16_t* smem, uint16_t* myP, int qt_
 
 // One job: key tile kt (128 keys) of head bh, walking the query tiles that see it from the last
 // one down.  Returns with every wave past its last read of the ring and the P buffers.
-template <int D, bool VARLEN>
+template <int D, bool VARLEN, bool QKN>
 __device__ __forceinline__ void dkdv_job(const BwdArgs& p, int bh, int kt, uint16_t* smem,
                                          uint16_t* sPbuf, int wave, int lane) {
   constexpr int NW = kDkdvWaves, BK = 128, BQ = kBwdBQ;
@@ -537,6 +577,13 @@ __device__ __forceinline__ void dkdv_job(const BwdArgs& p, int bh, int kt, uint1
   if (!kvalid) return;
   const float sc = pwave ? 1.f : -p.scale;  // the dS waves accumulated -dK^T
   uint16_t* out = (pwave ? p.dv : p.dk) + base + (int64_t)kj * rs;
+  if constexpr (QKN) {  // dk with respect to the raw rows; p.k holds the normalised ones
+    if (!pwave) {
+      store_through_rmsnorm<D>(acc, sc, p.k + base + (int64_t)kj * rs, p.rk[rw.stat + kj], out,
+                               half);
+      return;
+    }
+  }
 #pragma unroll
   for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -551,7 +598,7 @@ __device__ __forceinline__ void dkdv_job(const BwdArgs& p, int bh, int kt, uint1
 // Full-causal training pass (p.paired): workgroup = head + key-tile pair (n - 1 - j, j), the short
 // tile (fewest queries) first, so that a head's workgroups start on the same query tiles together
 // (pair_job).  Otherwise: workgroup = one key tile, those seeing the most queries first.
-template <int D, bool VARLEN>
+template <int D, bool VARLEN, bool QKN>
 __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs p) {
   constexpr int SE = DkdvStage<D>::ELEMS, PE = DkdvStage<D>::PELEMS;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[kDkdvStages * SE];
@@ -574,7 +621,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs p)
 #pragma unroll 1
   for (int jx = 0; jx < njobs; ++jx) {
     if (jx) __syncthreads();  // every wave is done with the ring and P before the next job
-    dkdv_job<D, VARLEN>(p, bh, jx ? kt1 : kt0, smem, sPbuf, wave, lane);
+    dkdv_job<D, VARLEN, QKN>(p, bh, jx ? kt1 : kt0, smem, sPbuf, wave, lane);
   }
 }
 
@@ -589,9 +636,11 @@ static hipError_t launch_dq_d(const BwdArgs& a, hipStream_t s) {
   const unsigned per_head = p.paired ? (unsigned)(p.n_tiles + 1) / 2 : (unsigned)p.n_tiles;
   const unsigned grid = per_head * (unsigned)p.BH;
   if (p.cu)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, true>), dim3(grid), dim3(64 * NW), 0, s, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, true, false>), dim3(grid), dim3(64 * NW), 0, s, p);
+  else if (p.rq)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, false, true>), dim3(grid), dim3(64 * NW), 0, s, p);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, false>), dim3(grid), dim3(64 * NW), 0, s, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, false, false>), dim3(grid), dim3(64 * NW), 0, s, p);
   return hipGetLastError();
 }
 
@@ -604,9 +653,14 @@ static hipError_t launch_dkdv_d(const BwdArgs& a, hipStream_t s) {
   const unsigned per_head = p.paired ? (unsigned)(p.n_tiles + 1) / 2 : (unsigned)p.n_tiles;
   const unsigned grid = per_head * (unsigned)p.BH;
   if (p.cu)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(grid), dim3(64 * kDkdvWaves), 0, s, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false>), dim3(grid), dim3(64 * kDkdvWaves), 0, s,
+                       p);
+  else if (p.rk)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true>), dim3(grid), dim3(64 * kDkdvWaves), 0, s,
+                       p);
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(grid), dim3(64 * kDkdvWaves), 0, s, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false>), dim3(grid), dim3(64 * kDkdvWaves), 0, s,
+                       p);
   return hipGetLastError();
 }
 

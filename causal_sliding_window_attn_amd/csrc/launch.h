@@ -43,6 +43,8 @@ struct BwdArgs {
   const int* cu;     // packed sequences (rows cu[b] .. cu[b + 1] - 1 of [total, H, D]; lse,
                      // Delta and LSE * log2(e) as [H, total]), or null; T is then the longest
   int total;         // packed sequences: rows in q / k / v / o / dO
+  const float* rq;   // QK-norm backward: 1 / rms of each q row [BH, T] (q holds the normalised
+  const float* rk;   // rows), and of each k row; dq, dk are then taken back through the norm
   int64_t bstride;   // T * H * D
   int row_stride;    // H * D
   int H, BH, D, T, window;
@@ -70,6 +72,18 @@ struct DecArgs {
   float scale_log2;
 };
 
+// Parameter-free RMS normalisation of the q and k rows ([B, T, H, D] bf16).
+struct NormArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  uint16_t* qn;  // q / rms(q), bf16
+  uint16_t* kn;
+  float* rq;     // 1 / rms per row, [B, H, T]
+  float* rk;
+  int B, T, H, D;
+  float eps;
+};
+
 struct AppendArgs {
   uint16_t* kc;
   uint16_t* vc;
@@ -90,5 +104,6 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecArgs& a, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_qk_rmsnorm(const NormArgs& a, hipStream_t s);
 
 }  // namespace swattn

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define SWATTN_ABI_VERSION 3  /* 2: attn_decode_step; 3: attn_fwd_varlen, attn_bwd_varlen */
+#define SWATTN_ABI_VERSION 4  /* 2: attn_decode_step; 3: *_varlen; 4: *_qknorm */
 
 typedef enum { SWATTN_BF16 = 0, SWATTN_F32 = 1 } swattn_dtype;
 
@@ -188,6 +188,27 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
                     const void* dout, void* dq, void* dk, void* dv, const int* cu_seqlens,
                     int nseq, int total, int max_seqlen, int H, int D, int window, void* ws,
                     size_t ws_bytes, void* stream);
+
+/*
+ * QK-norm: attention over parameter-free RMS-normalised queries and keys (the model's RMS norms
+ * carry no trainable parameters: walkthrough, section "Pretraining", the paragraph on the
+ * optimisers).  Per row (one token of one head): r = 1 / sqrt(mean_d x_d^2 + eps), x_hat = x r.
+ *   attn_fwd_qknorm: writes qn = bf16(q r_q), kn = bf16(k r_k) ([B, T, H, D]) and rq, rk (r per
+ *     row, float32 [B, H, T]), then runs attn_fwd on (qn, kn, v): o, lse as attn_fwd.
+ *     eps >= 0 and finite.  Two launches (the normalisation, then the attention).
+ *   attn_bwd_qknorm: the backward of the whole map (q, k, v) -> o, given the forward's qn, kn, rq,
+ *     rk, o, lse: dq, dk are gradients with respect to the raw q and k (the norm's backward,
+ *     dx = r (dx_hat - x_hat (dx_hat . x_hat) / D), runs inside the passes' epilogues), dv as
+ *     attn_bwd.  Workspace as attn_bwd.
+ * bf16 only; errors as attn_fwd / attn_bwd.
+ */
+int attn_fwd_qknorm(const void* q, const void* k, const void* v, void* qn, void* kn, float* rq,
+                    float* rk, void* o, float* lse, int B, int H, int T, int D, int window,
+                    float eps, void* stream);
+int attn_bwd_qknorm(const void* qn, const void* kn, const void* v, const void* o, const float* lse,
+                    const void* dout, const float* rq, const float* rk, void* dq, void* dk,
+                    void* dv, int B, int H, int T, int D, int window, void* ws, size_t ws_bytes,
+                    void* stream);
 
 #ifdef __cplusplus
 }

@@ -16,6 +16,11 @@ What is computed, and where it comes from
 * Packed documents: training rows hold several documents separated by the beginning-of-sequence
   token (same walkthrough, section "Midtraining").  ``forward_varlen`` / ``backward_varlen`` take
   packed sequences in which each document attends only to itself.
+* QK-norm: the model's RMS norms carry no trainable parameters (same walkthrough, section
+  "Pretraining", the paragraph on the optimisers).  ``forward_qknorm`` / ``backward_qknorm``
+  normalise each q and k row, r = 1 / sqrt(mean x^2 + eps), before the attention; by default the
+  normalised rows are rounded to bf16 (they are stored activations), and the norm's backward uses
+  its exact Jacobian at the raw rows.
 
 The pages print no formula.  The definition below is textbook scaled dot-product attention; the
 readings of what the pages leave open are:
@@ -55,6 +60,9 @@ __all__ = [
     "decode",
     "forward_varlen",
     "backward_varlen",
+    "rmsnorm",
+    "forward_qknorm",
+    "backward_qknorm",
 ]
 
 
@@ -317,3 +325,42 @@ def backward_varlen(q, k, v, do, cu_seqlens, window=None, threads=None):
         dk[a:e, h] = gk
         dv[a:e, h] = gv
     return dq, dk, dv
+
+
+
+def rmsnorm(x, eps):
+    """Parameter-free RMS norm over the last axis: returns (x * r, r), r = 1 / sqrt(mean x^2 + eps)."""
+    x = _f64(x)
+    r = 1.0 / np.sqrt((x * x).mean(axis=-1) + eps)
+    return x * r[..., None], r
+
+
+def _bf16(x):
+    import torch  # rounding to bf16 (round to nearest even) through the library cast
+
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).double().numpy()
+
+
+def forward_qknorm(q, k, v, window=None, eps=1e-6, round_bf16=True, threads=None):
+    """Attention over RMS-normalised q, k ([B, T, H, D]).  Returns O, LSE and the normalised rows
+    (qn, kn, as the attention saw them)."""
+    qn, _ = rmsnorm(q, eps)
+    kn, _ = rmsnorm(k, eps)
+    if round_bf16:
+        qn, kn = _bf16(qn), _bf16(kn)
+    o, lse = forward(qn, kn, v, window, threads=threads)
+    return o, lse, qn, kn
+
+
+def _rmsnorm_backward(x, g, eps):
+    # y = x r, r = (mean x^2 + eps)^(-1/2):  dx = r (g - y (g . y) / D)
+    y, r = rmsnorm(x, eps)
+    D = y.shape[-1]
+    return r[..., None] * (g - y * ((g * y).sum(axis=-1) / D)[..., None])
+
+
+def backward_qknorm(q, k, v, do, window=None, eps=1e-6, round_bf16=True, threads=None):
+    """Gradients of ``forward_qknorm``'s O with respect to the raw q, k and v."""
+    _, _, qn, kn = forward_qknorm(q, k, v, window, eps, round_bf16, threads)
+    gqn, gkn, gv = backward(qn, kn, v, do, window, threads=threads)
+    return _rmsnorm_backward(q, gqn, eps), _rmsnorm_backward(k, gkn, eps), gv

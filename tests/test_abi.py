@@ -30,8 +30,8 @@ def test_header_declares_the_entry_points():
     names = set(declared_functions())
     assert {"attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_decode", "attn_prefill",
             "attn_kv_append", "attn_decode_step", "attn_fwd_varlen", "attn_bwd_varlen",
-            "attn_bwd_workspace_bytes", "attn_decode_workspace_bytes", "attn_last_error",
-            "attn_abi_version"} == names
+            "attn_fwd_qknorm", "attn_bwd_qknorm", "attn_bwd_workspace_bytes",
+            "attn_decode_workspace_bytes", "attn_last_error", "attn_abi_version"} == names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -55,7 +55,7 @@ def test_nm_lists_only_c_symbols(lib):
 
 
 def test_abi_version(lib):
-    assert lib.attn_abi_version() == 3
+    assert lib.attn_abi_version() == 4
 
 
 P = 4096  # an aligned, non-null stand-in pointer: validation must fail before it is ever used
@@ -183,6 +183,38 @@ def test_varlen_validation(lib):
     assert bwd(a9=None) == -1 and "cu_seqlens" in err(lib)
     assert bwd(a5=None) == -1 and "dout" in err(lib)
     assert bwd(a12=200) == -1
+
+
+def test_qknorm_validation(lib):
+    # q, k, v, qn, kn, rq, rk, o, lse, B, H, T, D, window, eps, stream
+    ok = [P] * 8 + [None, 2, 3, 64, 128, 8, 1e-6, None]
+
+    def fwd(**change):
+        a = list(ok)
+        for i, val in change.items():
+            a[int(i[1:])] = val
+        return lib.attn_fwd_qknorm(*a)
+
+    assert fwd(a14=-1.0) == -1 and "eps" in err(lib)
+    assert fwd(a14=float("nan")) == -1
+    assert fwd(a3=None) == -1 and "qn" in err(lib)
+    assert fwd(a6=None) == -1 and "rk" in err(lib)
+    assert fwd(a12=80) == -2
+    assert fwd(a13=0) == -1
+    need = lib.attn_bwd_workspace_bytes(2, 3, 64, 128)
+    # qn, kn, v, o, lse, dout, rq, rk, dq, dk, dv, B, H, T, D, window, ws, ws_bytes, stream
+    bok = [P] * 11 + [2, 3, 64, 128, 8, P, need, None]
+
+    def bwd(**change):
+        a = list(bok)
+        for i, val in change.items():
+            a[int(i[1:])] = val
+        return lib.attn_bwd_qknorm(*a)
+
+    assert bwd(a6=None) == -1 and "rq" in err(lib)
+    assert bwd(a7=P + 4) == -1
+    assert bwd(a17=need - 1) == -3
+    assert bwd(a5=None) == -1 and "dout" in err(lib)
 
 
 def test_last_error_is_thread_local(lib):

@@ -533,3 +533,60 @@ def test_varlen_autograd_and_rows_past_max_seqlen(sw):
     assert torch.all(o2[a + 64:a + 90] == 7.0)
     assert np.abs(f64(o2[a:a + 64]) - o_r[a:a + 64]).max() <= O_TOL
     assert np.abs(f64(o2[:a]) - o_r[:a]).max() <= O_TOL
+
+
+# ------------------------------------------------------------------------------ QK-norm
+@pytest.mark.parametrize("D", [64, 128])
+def test_qknorm_matches_oracle(sw, D):
+    """Attention over RMS-normalised q, k against the oracle (normalised rows rounded to bf16, as
+    stored); q and k are drawn far from unit RMS so that the norm matters."""
+    B, T, H, eps = 2, 300, 3, 1e-6
+    g = torch.Generator().manual_seed(110 + D)
+    q = (3.0 * torch.randn(B, T, H, D, generator=g)).to(torch.bfloat16)
+    k = (0.5 * torch.randn(B, T, H, D, generator=g)).to(torch.bfloat16)
+    v, do = (torch.randn(B, T, H, D, generator=g).to(torch.bfloat16) for _ in range(2))
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    for window in (None, 50):
+        o, lse, qn, kn, rq, rk = sw.attn_fwd_qknorm(qd, kd, vd, window=window, eps=eps)
+        g3 = sw.attn_bwd_qknorm(qn, kn, vd, o, lse, dod, rq, rk, window=window)
+        torch.cuda.synchronize()
+        o_r, lse_r, qn_r, kn_r = ref.forward_qknorm(f64(q), f64(k), f64(v), window, eps)
+        # normalised rows: within one bf16 rounding step of the oracle's (fp32 vs fp64 scale)
+        for a, b in ((qn, qn_r), (kn, kn_r)):
+            assert np.abs(f64(a) - b).max() <= 2 ** -7 * np.abs(b).max()
+        _, r_q = ref.rmsnorm(f64(q), eps)
+        assert np.abs(f64(rq) - r_q.transpose(0, 2, 1)).max() <= 1e-5 * np.abs(r_q).max()
+        assert np.abs(f64(o) - o_r).max() <= O_TOL, f"window {window}"
+        assert np.abs(f64(lse) - lse_r).max() <= LSE_TOL, f"window {window}"
+        g_r = ref.backward_qknorm(f64(q), f64(k), f64(v), f64(do), window, eps)
+        check_grads(g3, g_r, tag=f"qknorm D{D} window {window}")
+
+
+def test_qknorm_fused_epilogue_equals_unfused_composition(sw):
+    """The norm's backward inside the passes' epilogues equals the plain composition: attn_bwd on
+    the normalised rows, then dx = r (g - y (g . y) / D) in float32 on the device."""
+    B, T, H, D = 1, 200, 2, 128
+    g = torch.Generator().manual_seed(120)
+    q, k, v, do = (torch.randn(B, T, H, D, generator=g).mul(s).to(torch.bfloat16).to(DEV)
+                   for s in (2.0, 0.7, 1.0, 1.0))
+    o, lse, qn, kn, rq, rk = sw.attn_fwd_qknorm(q, k, v, window=64)
+    dq, dk, dv = sw.attn_bwd_qknorm(qn, kn, v, o, lse, do, rq, rk, window=64)
+    gq, gk, gv = sw.attn_bwd(qn, kn, v, o, lse, do, window=64)
+
+    def through(gr, y, r):
+        gr, y = gr.float(), y.float()
+        rr = r.permute(0, 2, 1).unsqueeze(-1)  # [B, T, H, 1]
+        return rr * (gr - y * (gr * y).sum(-1, keepdim=True) / D)
+
+    for fused, unfused in ((dq, through(gq, qn, rq)), (dk, through(gk, kn, rk)), (dv, gv.float())):
+        e = rel_fro(f64(fused), f64(unfused))
+        assert e <= 1e-2, e
+
+
+def test_qknorm_autograd_wrapper(sw):
+    q, k, v, do = W.random_attn(1, 96, 2, 64, seed=121)
+    qd, kd, vd = (t.to(DEV).requires_grad_() for t in (q, k, v))
+    o = sw.attention_qknorm(qd, kd, vd, window=40, eps=1e-5)
+    o.backward(do.to(DEV))
+    g_r = ref.backward_qknorm(f64(q), f64(k), f64(v), f64(do), 40, 1e-5)
+    check_grads((qd.grad, kd.grad, vd.grad), g_r, tag="qknorm autograd")

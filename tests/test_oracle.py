@@ -458,3 +458,47 @@ def test_varlen_one_sequence_is_the_dense_forward():
     od, lsed = A.forward(q[None], k[None], v[None], 5)
     np.testing.assert_allclose(o, od[0], atol=1e-13)
     np.testing.assert_allclose(lse, lsed[0], atol=1e-13)
+
+
+# ---------------------------------------------------------------- QK-norm
+def test_rmsnorm_closed_forms():
+    rng = np.random.default_rng(90)
+    x = rng.standard_normal((3, 5, 2, 16))
+    y, r = A.rmsnorm(x, 0.0)
+    np.testing.assert_allclose((y * y).mean(-1), 1.0, atol=1e-13)  # unit RMS
+    y2, _ = A.rmsnorm(7.5 * x, 0.0)
+    np.testing.assert_allclose(y2, y, atol=1e-13)  # scale invariance
+    np.testing.assert_allclose(r, 1 / np.sqrt((x * x).mean(-1)), rtol=1e-14)
+    tr = torch.nn.functional.rms_norm(torch.tensor(x), (16,), eps=1e-3).numpy()
+    np.testing.assert_allclose(A.rmsnorm(x, 1e-3)[0], tr, atol=1e-13)  # the library routine
+
+
+@pytest.mark.parametrize("w", [3, 100])
+def test_qknorm_forward_and_backward_match_autograd(w):
+    """fp64 autograd through torch's rms_norm and the masked softmax attention."""
+    rng = np.random.default_rng(91 + w)
+    B, T, H, D, eps = 1, 19, 2, 8, 1e-3
+    q, k, v, g = (rng.standard_normal((B, T, H, D)) * s for s in (3.0, 0.5, 1.0, 1.0))
+    o, lse, _, _ = A.forward_qknorm(q, k, v, w, eps, round_bf16=False)
+    dq, dk, dv = A.backward_qknorm(q, k, v, g, w, eps, round_bf16=False)
+    m = torch.tensor(brute.mask(T, w))
+    for h in range(H):
+        tq, tk, tv = (torch.tensor(x[0, :, h], requires_grad=True) for x in (q, k, v))
+        nq = torch.nn.functional.rms_norm(tq, (D,), eps=eps)
+        nk = torch.nn.functional.rms_norm(tk, (D,), eps=eps)
+        s = ((nq @ nk.T) / math.sqrt(D)).masked_fill(~m, float("-inf"))
+        to = torch.softmax(s, dim=1) @ tv
+        np.testing.assert_allclose(o[0, :, h], to.detach().numpy(), atol=1e-12)
+        to.backward(torch.tensor(g[0, :, h]))
+        np.testing.assert_allclose(dq[0, :, h], tq.grad.numpy(), atol=1e-10)
+        np.testing.assert_allclose(dk[0, :, h], tk.grad.numpy(), atol=1e-10)
+        np.testing.assert_allclose(dv[0, :, h], tv.grad.numpy(), atol=1e-10)
+
+
+def test_qknorm_gradient_is_orthogonal_to_the_row():
+    """The norm is scale invariant (eps = 0), so dq . q = 0 and dk . k = 0 for every row."""
+    rng = np.random.default_rng(93)
+    q, k, v, g = (rng.standard_normal((1, 12, 1, 8)) for _ in range(4))
+    dq, dk, _ = A.backward_qknorm(q, k, v, g, None, 0.0, round_bf16=False)
+    assert np.abs((dq * q).sum(-1)).max() < 1e-12
+    assert np.abs((dk * k).sum(-1)).max() < 1e-12
