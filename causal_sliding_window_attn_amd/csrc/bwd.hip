@@ -19,6 +19,14 @@
 // tile: a two-stage K/V ring in the dQ pass, a three-stage Q/dO ring in the dK/dV pass (the dS
 // waves still read the tile before).  Every transposed operand (K^T, Q^T, dO^T) comes straight
 // from the row-major tile through ds_read_b64_tr_b16.
+//
+// Modes (template flags; the dense instantiation is unchanged by them):
+//   VARLEN  packed documents (rows cu[s] .. cu[s+1] - 1 of [total, H, D], each attending only to
+//           itself -- walkthrough, section "Midtraining": documents separated by the
+//           beginning-of-sequence token): a workgroup reads its document's offset and length and
+//           runs the dense job on that slice;
+//   QKN     q and k are RMS-normalised rows (norm.hip); the epilogues take dQ and dK back through
+//           the parameter-free norm before storing (store_through_rmsnorm).
 #include "common.h"
 #include "launch.h"
 

@@ -16,7 +16,9 @@
 // Tiles outside [q0 - w + 1, q_end] are never loaded; per wave, tiles wholly outside the window
 // are skipped, and only tiles crossing the diagonal or the window edge run the masked loop.  O is
 // rescaled lazily, only when a row maximum grows by more than 2^8.  Under the full causal mask
-// (training) a workgroup owns a pair of query tiles of equal total work (pair_job).
+// (training) a workgroup owns a pair of query tiles of equal total work (pair_job).  VARLEN:
+// packed documents (walkthrough, section "Midtraining"), each attending only to itself; a
+// workgroup reads its document's offset and length from cu and runs the same job on that slice.
 #include "common.h"
 #include "launch.h"
 
