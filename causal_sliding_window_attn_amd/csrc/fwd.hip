@@ -106,19 +106,24 @@ __device__ __forceinline__ void fwd_block_exp(f32x16& s, float sl2, FwdState<D>&
   pack_frag_split(s, 1, ph[1], pl[1]);
 }
 
-// O^T += V^T P^T for one 32-key block.
+// O^T += V^T P^T for one 32-key block: the hi MFMAs of all D / 32 accumulators, then the lo
+// ones, so that no two consecutive MFMAs update the same accumulator (each keeps its hi-then-lo
+// order; 0.5-2.5% off the forward and the prefill, bit-identical).
 template <int D>
 __device__ __forceinline__ void fwd_block_pv(const uint16_t* sV, const LdsOffsets<D>& lo, int nb,
                                              const uint4 (&ph)[2], const uint4 (&pl)[2],
                                              FwdState<D>& S) {
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < 2; ++u) {
+    uint4 a[D / 32];
 #pragma unroll
     for (int m = 0; m < D / 32; ++m) {
-      const uint4 a = tr_frag_o<D>(sV, lo, nb * 32 + 16 * u, m);
-      S.oacc[m] = mfma32(a, ph[u], S.oacc[m]);
-      S.oacc[m] = mfma32(a, pl[u], S.oacc[m]);
+      a[m] = tr_frag_o<D>(sV, lo, nb * 32 + 16 * u, m);
+      S.oacc[m] = mfma32(a[m], ph[u], S.oacc[m]);
     }
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) S.oacc[m] = mfma32(a[m], pl[u], S.oacc[m]);
+  }
 }
 
 // S^T of one key tile (two 32-key blocks) and its softmax bookkeeping.  Only this part differs
