@@ -341,14 +341,14 @@ def _bf16(x):
     return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).double().numpy()
 
 
-def forward_qknorm(q, k, v, window=None, eps=1e-6, round_bf16=True, threads=None):
+def forward_qknorm(q, k, v, window=None, eps=1e-6, round_bf16=True, threads=None, heads=None):
     """Attention over RMS-normalised q, k ([B, T, H, D]).  Returns O, LSE and the normalised rows
-    (qn, kn, as the attention saw them)."""
+    (qn, kn, as the attention saw them); ``heads`` as in ``forward``."""
     qn, _ = rmsnorm(q, eps)
     kn, _ = rmsnorm(k, eps)
     if round_bf16:
         qn, kn = _bf16(qn), _bf16(kn)
-    o, lse = forward(qn, kn, v, window, threads=threads)
+    o, lse = forward(qn, kn, v, window, heads=heads, threads=threads)
     return o, lse, qn, kn
 
 
@@ -359,8 +359,13 @@ def _rmsnorm_backward(x, g, eps):
     return r[..., None] * (g - y * ((g * y).sum(axis=-1) / D)[..., None])
 
 
-def backward_qknorm(q, k, v, do, window=None, eps=1e-6, round_bf16=True, threads=None):
-    """Gradients of ``forward_qknorm``'s O with respect to the raw q, k and v."""
-    _, _, qn, kn = forward_qknorm(q, k, v, window, eps, round_bf16, threads)
-    gqn, gkn, gv = backward(qn, kn, v, do, window, threads=threads)
+def backward_qknorm(q, k, v, do, window=None, eps=1e-6, round_bf16=True, threads=None,
+                    heads=None):
+    """Gradients of ``forward_qknorm``'s O with respect to the raw q, k and v; ``heads`` as in
+    ``backward`` (other heads NaN)."""
+    qn, _ = rmsnorm(q, eps)
+    kn, _ = rmsnorm(k, eps)
+    if round_bf16:
+        qn, kn = _bf16(qn), _bf16(kn)
+    gqn, gkn, gv = backward(qn, kn, v, do, window, heads=heads, threads=threads)
     return _rmsnorm_backward(q, gqn, eps), _rmsnorm_backward(k, gkn, eps), gv

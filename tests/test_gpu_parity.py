@@ -169,6 +169,7 @@ def test_d30_engine_prefill_and_decode(sw, layer):
     # decode steps: append, then attend with lens + 1
     kc_ref, vc_ref = f64(kc), f64(vc)
     kc_bf, vc_bf = kc.clone(), vc.clone()
+    kcs, vcs = kcd.clone(), vcd.clone()  # the same steps through attn_decode_step
     cur = lens.clone()
     ws = torch.empty(sw.attn_decode_workspace_bytes(E.B, E.H, E.Lcap, E.D), device=DEV,
                      dtype=torch.uint8)
@@ -179,7 +180,11 @@ def test_d30_engine_prefill_and_decode(sw, layer):
         sw.attn_kv_append(kcd, vcd, kn.to(DEV), vn.to(DEV), pos)
         od, lsed = sw.attn_decode(qn.to(DEV), kcd, vcd, (cur + 1).to(DEV), window=window, ws=ws,
                                   want_lse=True)
+        os_, lses = sw.attn_decode_step(qn.to(DEV), kn.to(DEV), vn.to(DEV), kcs, vcs, pos,
+                                        window=window, ws=ws, want_lse=True)
         torch.cuda.synchronize()
+        assert torch.equal(os_, od) and torch.equal(lses, lsed), f"decode step {s}"
+
         for b in range(E.B):
             kc_ref[b, int(cur[b])] = f64(kn[b])
             vc_ref[b, int(cur[b])] = f64(vn[b])
@@ -193,6 +198,7 @@ def test_d30_engine_prefill_and_decode(sw, layer):
         cur += 1
     # the device cache holds exactly what the reference appended
     assert torch.equal(kcd.cpu(), kc_bf) and torch.equal(vcd.cpu(), vc_bf)
+    assert torch.equal(kcs, kcd) and torch.equal(vcs, vcd)
 
 
 # --------------------------------------------------------------------------- edge sweep
@@ -590,3 +596,54 @@ def test_qknorm_autograd_wrapper(sw):
     o.backward(do.to(DEV))
     g_r = ref.backward_qknorm(f64(q), f64(k), f64(v), f64(do), 40, 1e-5)
     check_grads((qd.grad, kd.grad, vd.grad), g_r, tag="qknorm autograd")
+
+
+# ------------------------------------------------- full-size NEXT workloads, sampled outputs
+@pytest.mark.slow
+def test_d20_packed_documents_sampled(sw):
+    """The bench's packed-document d20 rows (same q, k, v, dO as the d20 layer), forward and
+    backward in the bench's launch configuration; the shortest, a median and the longest document
+    checked on two heads against the oracle run on each document alone."""
+    c = W.D20_LAYER
+    q, k, v, do = W.attn_inputs(c)
+    B, T, H, D = q.shape
+    cu = W.d20_packed_cu(B, T)
+    lens = (cu[1:] - cu[:-1]).tolist()
+    ms = max(lens)
+    qp, kp, vp, dop = (t.reshape(B * T, H, D) for t in (q, k, v, do))
+    qd, kd, vd, dod = (t.to(DEV) for t in (qp, kp, vp, dop))
+    o, lse = sw.attn_fwd_varlen(qd, kd, vd, cu.to(DEV), ms, window=c.window)
+    g = sw.attn_bwd_varlen(qd, kd, vd, o, lse, dod, cu.to(DEV), ms, window=c.window)
+    torch.cuda.synchronize()
+    order = sorted(range(len(lens)), key=lambda i: lens[i])
+    heads = [0, H - 1]
+    for s in (order[0], order[len(order) // 2], order[-1]):
+        a, e = int(cu[s]), int(cu[s + 1])
+        one = [f64(t[a:e]).reshape(1, e - a, H, D) for t in (qp, kp, vp, dop)]
+        hh = [(0, h) for h in heads]
+        o_r, lse_r = ref.forward(one[0], one[1], one[2], c.window, heads=hh)
+        g_r = ref.backward(*one, c.window, heads=hh)
+        for h in heads:
+            assert np.abs(f64(o[a:e, h]) - o_r[0, :, h]).max() <= O_TOL, (s, h)
+            assert np.abs(f64(lse[h, a:e]) - lse_r[0, h]).max() <= LSE_TOL, (s, h)
+            for gg, rr in zip(g, g_r):
+                assert rel_fro(f64(gg[a:e, h]), rr[0, :, h]) <= G_TOL, (s, h, e - a)
+    for t in (o, lse) + tuple(g):
+        assert torch.isfinite(t).all()
+
+
+@pytest.mark.slow
+def test_d20_qknorm_sampled_heads(sw):
+    """QK-norm on the d20 layer in the bench's configuration, sampled heads against the oracle."""
+    c = W.D20_LAYER
+    q, k, v, do = W.attn_inputs(c)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse, qn, kn, rq, rk = sw.attn_fwd_qknorm(qd, kd, vd, window=c.window)
+    g = sw.attn_bwd_qknorm(qn, kn, vd, o, lse, dod, rq, rk, window=c.window)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (31, 9)]
+    Q, K, V, DO = (f64(t) for t in (q, k, v, do))
+    o_r, lse_r, _, _ = ref.forward_qknorm(Q, K, V, c.window, heads=heads)
+    check_fwd(o, lse, o_r, lse_r, heads=heads, tag="d20 qknorm")
+    check_grads(g, ref.backward_qknorm(Q, K, V, DO, c.window, heads=heads), heads=heads,
+                tag="d20 qknorm")
