@@ -202,7 +202,7 @@ def test_d30_engine_prefill_and_decode(sw, layer):
 
 
 # --------------------------------------------------------------------------- edge sweep
-EDGE_T = [1, 17, 63, 64, 65, 127, 128, 129, 300]
+EDGE_T = [1, 17, 63, 64, 65, 127, 128, 129, 300, 1000]
 
 
 def edge_windows(T):
@@ -329,6 +329,28 @@ def test_determinism_and_full_window_bitwise(sw):
     ge = sw.attn_bwd(qd, kd, vd, eq[0], eq[1], dod, window=333)
     for a, b in zip(gf, ge):
         assert torch.equal(a, b)
+
+
+def test_decode_deterministic_and_schedule_independent(sw):
+    """Decode repeats bit for bit, and its two schedules agree: the same 8 sequences decoded
+    within a batch of 64 (one workgroup per (sequence, head), B * H >= 512) and alone (64-key
+    chunks across workgroups, then a merge kernel, B * H < 512)."""
+    B, H, D, Lcap = 64, 8, 128, 700
+    g = torch.Generator().manual_seed(130)
+    lens = torch.randint(1, Lcap + 1, (B,), generator=g, dtype=torch.int32)
+    kc, vc = (torch.randn(B, Lcap, H, D, generator=g).to(torch.bfloat16).to(DEV) for _ in range(2))
+    q = torch.randn(B, H, D, generator=g).to(torch.bfloat16).to(DEV)
+    ld = lens.to(DEV)
+    for window in (None, 100):
+        runs = [sw.attn_decode(q, kc, vc, ld, window=window, want_lse=True) for _ in range(3)]
+        small = sw.attn_decode(q[:8].contiguous(), kc[:8].contiguous(), vc[:8].contiguous(),
+                               ld[:8].contiguous(), window=window, want_lse=True)
+        torch.cuda.synchronize()
+        for o, l in runs[1:]:
+            assert torch.equal(o, runs[0][0]) and torch.equal(l, runs[0][1])
+        o, l = runs[0]
+        assert (o[:8].float() - small[0].float()).abs().max().item() <= 2 ** -7 * o.abs().max().item()
+        assert (l[:8] - small[1]).abs().max().item() <= 1e-4
 
 
 def test_split_passes_equal_attn_bwd(sw):
