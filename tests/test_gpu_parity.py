@@ -373,6 +373,11 @@ def test_gradient_sum_invariants(sw):
     scale = np.abs(dk64).sum(1).max()
     assert np.abs(dk64.sum(1)).max() <= 2e-2 * scale
     assert np.abs(dv64.sum(1) - do64.sum(1)).max() <= 2e-2 * np.abs(do64).sum(1).max()
+    # sum_i q_i . dQ_i = sum_j k_j . dK_j (both equal sum_ij dS_ij q_i . k_j / sqrt(D)), per head
+    q64, k64, dq64 = f64(q), f64(k), f64(dq)
+    lhs = (q64 * dq64).sum(axis=(1, 3))
+    rhs = (k64 * dk64).sum(axis=(1, 3))
+    assert np.abs(lhs - rhs).max() <= 2e-2 * np.abs(q64 * dq64).sum(axis=(1, 3)).max()
 
 
 def test_decode_matches_prefill_last_row(sw):
