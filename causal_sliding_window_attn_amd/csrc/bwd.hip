@@ -12,8 +12,8 @@
 // the forward), computes Delta and LSE * log2(e) for them first and writes both to the workspace,
 // then walks the in-window key tiles: S^T = K Q^T, dP^T = V dO^T, dS^T, and dQ^T += K^T dS^T.
 // dK/dV pass: a workgroup owns 128 keys and walks the query tiles that can see them, last tile
-// first; half of its waves compute S = Q K^T, P and dV^T += dO^T P, the other half, one tile
-// behind, dP = dO V^T, dS and dK^T += Q^T dS, taking P through LDS (lane = key in both).
+// first; half of its waves compute S = Q K^T and P, the other half, one tile behind,
+// dP = dO V^T, dS, dV^T += dO^T P and dK^T += Q^T dS, taking P through LDS (lane = key in both).
 // Under the full causal mask both passes give each workgroup a pair of tiles of equal total work
 // (pair_job).  Tiles stream global -> LDS with global_load_lds, one tile ahead with one barrier per
 // tile: a two-stage K/V ring in the dQ pass, a three-stage Q/dO ring in the dK/dV pass (the dS
@@ -306,13 +306,15 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs p) {
 }
 
 // ---------------------------------------------------------------------------------------- dK/dV
-// Eight waves own 128 keys: waves 0-3 ("P waves") compute S = Q K^T and P for key block w and
-// accumulate dV^T += dO^T P; waves 4-7 ("dS waves") compute dP = dO V^T for the same key block and
-// accumulate dK^T += Q^T dS.  The dS waves run one query tile behind: in iteration i the P waves
-// handle tile i and leave its P (bf16, register order) in one of two LDS buffers, while the dS
-// waves handle tile i - 1 with the P left there in iteration i - 1.  A three-stage Q/dO ring keeps
-// tiles i + 1 (in flight), i and i - 1 resident, so one barrier per tile suffices and each wave
-// runs its own 32 MFMAs per tile without waiting for the other role.
+// Eight waves own 128 keys: waves 0-3 ("P waves") compute S = Q K^T and P for key block w;
+// waves 4-7 ("dS waves") compute dP = dO V^T for the same key block and accumulate both
+// dV^T += dO^T P and dK^T += Q^T dS.  The dS waves run one query tile behind: in iteration i the
+// P waves handle tile i and leave its P (bf16, register order) in one of two LDS buffers, while the
+// dS waves handle tile i - 1 with the P left there in iteration i - 1.  A three-stage Q/dO ring
+// keeps tiles i + 1 (in flight), i and i - 1 resident, so one barrier per tile suffices.  The split
+// of the work gives the P waves the exponentials and 8 MFMAs per 32-query block and the dS waves
+// 24 MFMAs and little VALU work, so the two waves sharing a SIMD lean on different units (with
+// dV on the P waves, 16 MFMAs each, the pass was 4-5% slower).
 constexpr int kDkdvWaves = 8;
 constexpr int kDkdvStages = 3;
 // The P waves (0-3) alone issue the ring's DMA: the dS waves finish each tile last, and taking the
@@ -375,17 +377,15 @@ __device__ __forceinline__ bool dkdv_block_live(int qt, int qb2, int ka, int T, 
   return !(ka >= T || qz < ka || qs - kz >= w || qs >= T);
 }
 
-// P waves, one query tile: S, P (to sP, bf16), dV^T += dO^T P.
+// P waves, one query tile: S and P (to sP, bf16).
 template <int D>
 __device__ __forceinline__ void dkdv_pwave(const uint16_t* __restrict__ cur,
                                            uint16_t* __restrict__ sP, int qt, int ka, int kj,
                                            int T, int w, float sl2, const uint4 (&kf)[D / 16],
-                                           f32x16 (&dvacc)[D / 32], const LdsOffsets<D>& lo,
-                                           int lane) {
-  constexpr int BQ = kBwdBQ, DK = D / 16, MB = D / 32, TILE = DkdvStage<D>::TILE;
+                                           const LdsOffsets<D>& lo, int lane) {
+  constexpr int BQ = kBwdBQ, DK = D / 16, TILE = DkdvStage<D>::TILE;
   const int half = lane >> 5;
   const uint16_t* sQ = cur;
-  const uint16_t* sO = cur + TILE;
   const float* sL = reinterpret_cast<const float*>(cur + 2 * TILE);
 #pragma unroll
   for (int qb2 = 0; qb2 < BQ / 32; ++qb2) {
@@ -404,22 +404,17 @@ __device__ __forceinline__ void dkdv_pwave(const uint16_t* __restrict__ cur,
     dst[lane] = pf0;
     dst[64 + lane] = pf1;
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      dvacc[m] = mfma32(tr_frag_o<D>(sO, lo, 32 * qb2, m), pf0, dvacc[m]);
-      dvacc[m] = mfma32(tr_frag_o<D>(sO, lo, 32 * qb2 + 16, m), pf1, dvacc[m]);
-    }
-    sched_mfma_chain<2 * MB, 2, 4>();
   }
 }
 
-// dS waves, one query tile: dP, dS = P (dP - Delta) with P from sP, dK^T += Q^T dS.
+// dS waves, one query tile: dP, dS = P (dP - Delta) with P from sP, dV^T += dO^T P and
+// dK^T += Q^T dS.
 template <int D>
 __device__ __forceinline__ void dkdv_swave(const uint16_t* __restrict__ cur,
                                            const uint16_t* __restrict__ sP, int qt, int ka, int T,
                                            int w, const uint4 (&vf)[D / 16],
-                                           f32x16 (&dkacc)[D / 32], const LdsOffsets<D>& lo,
-                                           int lane) {
+                                           f32x16 (&dkacc)[D / 32], f32x16 (&dvacc)[D / 32],
+                                           const LdsOffsets<D>& lo, int lane) {
   constexpr int BQ = kBwdBQ, DK = D / 16, MB = D / 32, TILE = DkdvStage<D>::TILE;
   const int half = lane >> 5;
   const uint16_t* sQ = cur;
@@ -456,10 +451,15 @@ __device__ __forceinline__ void dkdv_swave(const uint16_t* __restrict__ cur,
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
+      dvacc[m] = mfma32(tr_frag_o<D>(sO, lo, 32 * qb2, m), pw[0], dvacc[m]);
+      dvacc[m] = mfma32(tr_frag_o<D>(sO, lo, 32 * qb2 + 16, m), pw[1], dvacc[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
       dkacc[m] = mfma32(tr_frag_o<D>(sQ, lo, 32 * qb2, m), df0, dkacc[m]);
       dkacc[m] = mfma32(tr_frag_o<D>(sQ, lo, 32 * qb2 + 16, m), df1, dkacc[m]);
     }
-    sched_mfma_chain<2 * MB, 2, 4>();
+    sched_mfma_chain<4 * MB, 2, 4>();
   }
 }
 
@@ -476,16 +476,17 @@ __device__ __forceinline__ void dkdv_step(const uint16_t* __restrict__ curp,
                                           const float* lseb, const float* delb, int rs, int qt_p,
                                           int qt_s, int qt_next, int ka, int kj, int T, int w,
                                           float sl2, const uint4 (&frag)[D / 16],
-                                          f32x16 (&acc)[D / 32], const LdsOffsets<D>& lo,
+                                          f32x16 (&acc)[D / 32], f32x16 (&acc2)[D / 32],
+                                          const LdsOffsets<D>& lo,
                                           const RowDma<D, kDkdvDmaWaves, kBwdBQ>& dma, int wave,
                                           int lane) {
   if (issue_next)
     dkdv_issue<D, kDkdvDmaWaves>(dma, qb, db, lseb, delb, rs, qt_next, T, nxt, wave, lane);
   if (!on) return;
   if (PW)
-    dkdv_pwave<D>(curp, pw, qt_p, ka, kj, T, w, sl2, frag, acc, lo, lane);
+    dkdv_pwave<D>(curp, pw, qt_p, ka, kj, T, w, sl2, frag, lo, lane);
   else
-    dkdv_swave<D>(curs, pr, qt_s, ka, T, w, frag, acc, lo, lane);
+    dkdv_swave<D>(curs, pr, qt_s, ka, T, w, frag, acc, acc2, lo, lane);
 }
 
 // The tile loop of one role over query tiles qt_hi down to qt_lo (stage 0 holds tile qt_hi on
@@ -498,7 +499,7 @@ __device__ __forceinline__ void dkdv_loop(uint16_t* smem, uint16_t* myP, int qt_
                                           const float* lseb, const float* delb, int rs, int ka,
                                           int kj, int T, int w, float sl2,
                                           const uint4 (&frag)[D / 16], f32x16 (&acc)[D / 32],
-                                          const LdsOffsets<D>& lo,
+                                          f32x16 (&acc2)[D / 32], const LdsOffsets<D>& lo,
                                           const RowDma<D, kDkdvDmaWaves, kBwdBQ>& dma, int wave,
                                           int lane) {
   constexpr int SE = DkdvStage<D>::ELEMS, PE = DkdvStage<D>::PELEMS;
@@ -511,7 +512,7 @@ __device__ __forceinline__ void dkdv_loop(uint16_t* smem, uint16_t* myP, int qt_
     const int qt = qt_hi - i;
     dkdv_step<D, NW, PW>(smem + s0, smem + s1, smem + s2, myP + pb, myP + (PE - pb), i + 1 < n,
                          PW ? (i < n) : (i >= 1), qb, db, lseb, delb, rs, qt, qt + 1, qt - 1, ka,
-                         kj, T, w, sl2, frag, acc, lo, dma, wave, lane);
+                         kj, T, w, sl2, frag, acc, acc2, lo, dma, wave, lane);
     const int t = s1;  // rotate: the stage just read one behind becomes the next DMA target
     s1 = s0;
     s0 = s2;
@@ -569,28 +570,38 @@ __device__ __forceinline__ void dkdv_job(const BwdArgs& p, int bh, int kt, uint1
       frag[t].z ^= 0x80008000u;
       frag[t].w ^= 0x80008000u;
     }
-  f32x16 acc[MB];  // dV^T (P waves) or dK^T (dS waves)
+  f32x16 acc[MB], acc2[MB];  // dS waves: dK^T, dV^T
 #pragma unroll
-  for (int m = 0; m < MB; ++m) acc[m] = zero16();
+  for (int m = 0; m < MB; ++m) acc[m] = acc2[m] = zero16();
 
   const LdsOffsets<D> lo(lane);
   uint16_t* myP = sPbuf + kblk * (PE / 4);  // this key block's part of each P buffer
   if (pwave)
     dkdv_loop<D, NW, true>(smem, myP, qt_lo, qt_hi, qb, db, lseb, delb, rs, ka, kj, T, w,
-                           p.scale_log2, frag, acc, lo, dma, wave, lane);
+                           p.scale_log2, frag, acc, acc2, lo, dma, wave, lane);
   else
     dkdv_loop<D, NW, false>(smem, myP, qt_lo, qt_hi, qb, db, lseb, delb, rs, ka, kj, T, w,
-                            p.scale_log2, frag, acc, lo, dma, wave, lane);
+                            p.scale_log2, frag, acc, acc2, lo, dma, wave, lane);
 
-  if (!kvalid) return;
-  const float sc = pwave ? 1.f : -p.scale;  // the dS waves accumulated -dK^T
-  uint16_t* out = (pwave ? p.dv : p.dk) + base + (int64_t)kj * rs;
+  if (!kvalid || pwave) return;
+  {
+    uint16_t* out = p.dv + base + (int64_t)kj * rs;
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint2 a;
+        a.x = pack_bf16x2(acc2[m][4 * j + 0], acc2[m][4 * j + 1]);
+        a.y = pack_bf16x2(acc2[m][4 * j + 2], acc2[m][4 * j + 3]);
+        *reinterpret_cast<uint2*>(out + m * 32 + 8 * j + 4 * half) = a;
+      }
+  }
+  const float sc = -p.scale;  // the dS waves accumulated -dK^T
+  uint16_t* out = p.dk + base + (int64_t)kj * rs;
   if constexpr (QKN) {  // dk with respect to the raw rows; p.k holds the normalised ones
-    if (!pwave) {
-      store_through_rmsnorm<D>(acc, sc, p.k + base + (int64_t)kj * rs, p.rk[rw.stat + kj], out,
-                               half);
-      return;
-    }
+    store_through_rmsnorm<D>(acc, sc, p.k + base + (int64_t)kj * rs, p.rk[rw.stat + kj], out,
+                             half);
+    return;
   }
 #pragma unroll
   for (int m = 0; m < MB; ++m)
