@@ -5,7 +5,8 @@ One step is one pass over every part of the path, on synthetic data of the pages
   * the d20 training layer (B=32, T=2048, H=10, D=128, bf16, full causal): forward, dQ pass,
     dK/dV pass;
   * one Engine decode step of the d30-style model (30 layers, B=64, H=15, D=128, cache 2048,
-    prompts U[32,1024], window 1024 on odd layers): per layer, KV append + split-K decode;
+    prompts U[32,1024], window 1024 on odd layers): per layer, KV append + decode (split-K
+    inside each workgroup at this batch);
   * one Engine prefill layer (the same prompts, layer step % 30).
 Every part is bracketed by HIP events on the stream the kernels run on.
 
@@ -14,7 +15,9 @@ visible (query, key) pair forward, 10D backward).  ``decode`` reports algorithmi
 visible cache row read once, plus q and o), next to a plain streaming read of the same byte count
 (the rate this GPU sustains at that size), and ``decode.step_graph`` the same decode step for all
 30 layers as one replay of a captured HIP graph (attn_decode_step: append and decode in one launch
-per layer); ``prefill`` TFLOP/s; ``varlen`` the d20 rows re-read as packed documents that attend
+per layer); ``decode.small_batch`` the first 8 sequences alone, and ``decode.long_context`` 2
+sequences over 16384 cached rows, where the decode takes its two-kernel schedule (split-K partials
+across workgroups, then the merge kernel); ``prefill`` TFLOP/s; ``varlen`` the d20 rows re-read as packed documents that attend
 only to themselves (attn_fwd_varlen / attn_bwd_varlen); ``qknorm`` the d20 layer with RMS-normalised
 q and k (attn_fwd_qknorm / attn_bwd_qknorm).  ``roofline`` describes the
 longest-running MFMA kernel; ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
@@ -137,6 +140,11 @@ def main() -> int:
                     help="skip the QK-norm (normalised q, k) fwd+bwd measurement")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the packed-document (varlen) fwd+bwd measurement")
+    ap.add_argument("--no-small-batch", action="store_true",
+                    help="skip the small-batch decode measurement")
+    ap.add_argument("--no-long-context", action="store_true",
+                    help="skip the long-context decode (split-K across workgroups + merge kernel) "
+                         "measurement")
     ap.add_argument("--calib-copy-mib", type=int, default=1024,
                     help="after the timed region, one plain device copy of this size (the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -203,14 +211,14 @@ def main() -> int:
     ws_d = torch.empty(sw.attn_decode_workspace_bytes(E.B, E.H, E.Lcap, E.D), device=dev,
                        dtype=torch.uint8)
 
-    def decode_bytes(s: int) -> int:
+    def decode_bytes(s: int, nb: int = E.B) -> int:
         tot = 0
         for l in range(E.n_layer):
             w = E.window(l)
-            for b in range(E.B):
+            for b in range(nb):
                 L = int(lens0[b]) + s + 1
                 tot += E.H * (min(L, w) if w else L) * E.D * 2 * 2
-            tot += 2 * E.B * E.H * E.D * 2  # q read, o written
+            tot += 2 * nb * E.H * E.D * 2  # q read, o written
         return tot
 
     def prefill_flops(layer: int) -> int:
@@ -383,6 +391,76 @@ def main() -> int:
                       "us_per_token_all_layers": round(t_g * 1e6, 1), "replays": reps}
         del sg
 
+    # Short decode calls take less GPU time than the host needs to launch them, so the two figures
+    # below time whole passes of calls queued behind ~1 ms of unrelated GPU work (a bf16 matmul):
+    # by the time the first call runs, the host has queued them all.
+    busy = torch.randn((8192, 8192), device=dev, dtype=torch.bfloat16)
+
+    def queued_pass_time(calls, reps):
+        evs = [(Ev(), Ev()) for _ in range(reps + 2)]
+        for i in range(reps + 2):
+            torch.matmul(busy, busy)
+            evs[i][0].record()
+            for c in calls:
+                c(i)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs[2:]) / reps * 1e-3
+
+    # small-batch decode: the first 8 sequences of the same Engine caches, all 30 layers, outside
+    # the timed region
+    small = None
+    if not args.no_small_batch:
+        Bs = 8
+        log(f"small-batch decode (first {Bs} sequences) ...")
+        reps = max(args.steps, 5)
+        on_s = on[:Bs]
+        qs = [qn[l][:Bs] for l in range(E.n_layer)]
+        ks = [kcache[l][:Bs] for l in range(E.n_layer)]
+        vs = [vcache[l][:Bs] for l in range(E.n_layer)]
+        lens_s = len_tab[0][:Bs]
+
+        def small_call(l):
+            return lambda i: sw.attn_decode(qs[l], ks[l], vs[l], lens_s, o=on_s,
+                                            window=E.window(l), ws=ws_d)
+
+        t_s = queued_pass_time([small_call(l) for l in range(E.n_layer)], reps)
+        s_bytes = decode_bytes(0, Bs)
+        small = {"B": Bs, "launches": sw.attn_decode_launches(Bs, E.H, E.Lcap, E.D),
+                 "us_per_layer_step": round(t_s / E.n_layer * 1e6, 2),
+                 "GB/s": round(s_bytes / t_s / 1e9, 1),
+                 "frac_of_hbm_peak": round(s_bytes / t_s / 1e9 / PEAK_HBM, 4)}
+
+    # long-context decode: 2 sequences x 15 heads, each attending to all of its 16384 cached rows,
+    # four layers' caches in rotation (1 GB, beyond the last-level cache).  With 30 (sequence, head)
+    # pairs each reading more than 2048 rows, the decode splits every pair's keys across
+    # workgroups and merges the chunks in a second kernel; outside the timed region
+    longctx = None
+    if not args.no_long_context:
+        Bl, Ll, nll = 2, 16384, 4
+        log(f"long-context decode ({Bl} sequences x {Ll} rows) ...")
+        gl = torch.Generator(device=dev).manual_seed(E.seed + 1)
+        kl = [torch.randn((Bl, Ll, E.H, E.D), device=dev, dtype=torch.bfloat16, generator=gl)
+              for _ in range(nll)]
+        vl = [torch.randn((Bl, Ll, E.H, E.D), device=dev, dtype=torch.bfloat16, generator=gl)
+              for _ in range(nll)]
+        ql = torch.randn((Bl, E.H, E.D), device=dev, dtype=torch.bfloat16, generator=gl)
+        ol = torch.empty_like(ql)
+        lens_l = torch.full((Bl,), Ll, dtype=torch.int32, device=dev)
+        ws_l = torch.empty(sw.attn_decode_workspace_bytes(Bl, E.H, Ll, E.D), device=dev,
+                           dtype=torch.uint8)
+
+        def long_call(l):
+            return lambda i: sw.attn_decode(ql, kl[l], vl[l], lens_l, o=ol, ws=ws_l)
+
+        t_l = queued_pass_time([long_call(l) for l in range(nll)], max(args.steps, 5)) / nll
+        l_bytes = Bl * E.H * Ll * E.D * 2 * 2 + 2 * Bl * E.H * E.D * 2
+        longctx = {"B": Bl, "H": E.H, "L": Ll, "launches": sw.attn_decode_launches(Bl, E.H, Ll, E.D),
+                   "us_per_call": round(t_l * 1e6, 2), "GB/s": round(l_bytes / t_l / 1e9, 1),
+                   "frac_of_hbm_peak": round(l_bytes / t_l / 1e9 / PEAK_HBM, 4)}
+        del kl, vl, ql, ol, ws_l
+    del busy
+
     # streaming-read reference: a plain read of the decode step's byte count, rotating over the
     # 30 layers' key caches (each larger than the last-level cache), outside the timed region
     stream_ref = None
@@ -423,7 +501,8 @@ def main() -> int:
                    "bytes_per_layer_step": round(dec_bytes / E.n_layer),
                    "stream_read_ref_GB/s": stream_ref and round(stream_ref, 1),
                    "frac_of_stream_read_ref": stream_ref and round(dec_gbs / stream_ref, 4),
-                   "step_graph": step_graph},
+                   "step_graph": step_graph, "small_batch": small,
+                   "long_context": longctx},
         "prefill": {"TFLOP/s": round(pre_flops / t_pre / 1e12, 2), "ms_per_layer": round(t_pre * 1e3, 4)},
         "varlen": varlen,
         "qknorm": qknorm,

@@ -20,7 +20,7 @@ __all__ = [
     "attn_abi_version", "attn_last_error", "attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv",
     "attn_bwd_workspace_bytes",
     "attn_prefill", "attn_kv_append", "attn_decode", "attn_decode_step",
-    "attn_decode_workspace_bytes", "attn_fwd_varlen", "attn_bwd_varlen", "attn_fwd_qknorm",
+    "attn_decode_workspace_bytes", "attn_decode_launches", "attn_fwd_varlen", "attn_bwd_varlen", "attn_fwd_qknorm",
     "attn_bwd_qknorm", "attention", "attention_varlen", "attention_qknorm", "KVCache",
     "DecodeStepGraph", "FULL", "QKNORM_EPS",
 ]
@@ -74,6 +74,15 @@ def attn_bwd_workspace_bytes(B: int, H: int, T: int, D: int) -> int:
 
 def attn_decode_workspace_bytes(B: int, H: int, Lcap: int, D: int) -> int:
     return load().attn_decode_workspace_bytes(B, H, Lcap, D)
+
+
+def attn_decode_launches(B: int, H: int, Lcap: int, D: int, window=None) -> int:
+    """Kernel launches of attn_decode / attn_decode_step at these sizes: 1 (one workgroup per
+    (sequence, head)) or 2 (split-K across workgroups, then a merge kernel)."""
+    rc = load().attn_decode_launches(B, H, Lcap, D, _win(window, Lcap))
+    if rc < 0:
+        check(rc, "attn_decode_launches")
+    return rc
 
 
 def attn_fwd(q, k, v, o=None, lse=None, window=None, want_lse=True):

@@ -35,6 +35,7 @@ SIGNATURES = {
     "attn_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "attn_kv_append": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "attn_decode_launches": (_i, [_i, _i, _i, _i, _i]),
     "attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "attn_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz,
                               _vp]),

@@ -263,6 +263,12 @@ size_t attn_decode_workspace_bytes(int B, int H, int Lcap, int D) {
   return align256(slots * D * sizeof(float)) + align256(slots * 2 * sizeof(float));
 }
 
+int attn_decode_launches(int B, int H, int Lcap, int D, int window) {
+  TRY(check_dims("attn_decode_launches", B, H, Lcap, "Lcap", D, window));
+  ok();
+  return swattn::decode_uses_fused(B, H, Lcap, window) ? 1 : 2;
+}
+
 int attn_decode(const void* q, const void* kcache, const void* vcache, const int* lens, void* o,
                 float* lse, int B, int H, int Lcap, int D, int window, void* ws, size_t ws_bytes,
                 void* stream) {

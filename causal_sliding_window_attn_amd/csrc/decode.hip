@@ -9,10 +9,11 @@
 // cache -- so it is HBM-bound and uses VALU dot products, not MFMA.  The visible key range is
 // split into 64-key chunks; a wave issues all of one chunk's K and V loads (16-byte, D/8 lanes per
 // key row) before using any of them and reduces q.k over the row's lanes with DPP.  Two schedules:
-//   many (sequence, head) pairs: one workgroup per pair, chunks dealt to its 4 waves, partial
-//   results merged in LDS (decode_fused_kernel, one launch, no workspace);
-//   few pairs (long contexts, small batch): one wave per (head, chunk, sequence) writes its chunk's
-//   (max, sum, unnormalised output) to the workspace and a second kernel merges the chunks.
+//   one workgroup per (sequence, head), chunks dealt to its 8 waves, partial results merged in
+//   LDS (decode_fused_kernel, one launch, no workspace) -- the usual case;
+//   few pairs over long caches (decode_uses_fused): one wave per (head, chunk, sequence) writes
+//   its chunk's (max, sum, unnormalised output) to the workspace and a second kernel merges the
+//   chunks.
 // Both merge with the log-sum-exp rule and write O (bf16) and LSE.
 //
 // Decode step (STEP): the same kernels also append the step's new key / value row at pos[b] and
@@ -217,42 +218,79 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecArgs p) {
   }
 }
 
+// Merge of the split schedule, one workgroup per (sequence, head).  A long cache leaves hundreds
+// of partial results per pair, so the threads share them out: D / 4 threads cover one chunk's
+// features (a float4 each) and the workgroup's rows of threads take every R-th chunk, with the
+// rows' sums meeting in LDS.
+constexpr int kCombineThreads = 256;
+
 template <int D, bool STEP>
-__global__ __launch_bounds__(64) void decode_combine_kernel(DecArgs p) {
-  constexpr int DPL = D / 64;  // features per lane
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecArgs p) {
+  constexpr int F4 = D / 4;                // threads per chunk row
+  constexpr int R = kCombineThreads / F4;  // chunk rows
+  constexpr int NWV = kCombineThreads / 64;
+  __shared__ float s_max[NWV];
+  __shared__ float4 s_o[R][F4];
+  __shared__ float s_l[R];
   const int bh = blockIdx.x;
   const int b = bh / p.H;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int L = dec_len<STEP>(p, b);
-  uint16_t* ob = p.o + (int64_t)bh * D + lane * DPL;
+  uint16_t* ob = p.o + (int64_t)bh * D;
   if (L == 0) {
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) ob[e] = 0;
-    if (p.lse && lane == 0) p.lse[bh] = -INFINITY;
+    if (tid < D) ob[tid] = 0;
+    if (p.lse && tid == 0) p.lse[bh] = -INFINITY;
     return;
   }
   const int nvis = min(p.window, L);
   const int nc = (nvis + kDecodeChunk - 1) / kDecodeChunk;
   const int64_t slot0 = (int64_t)bh * p.nc_max;
-  float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, p.ws_ml[2 * (slot0 + c)]);
-  float Ls = 0.f, acc[DPL];
+  // M: the largest chunk maximum (every chunk holds a visible key, so M is finite)
+  float m = -INFINITY;
+  for (int c = tid; c < nc; c += kCombineThreads) m = fmaxf(m, p.ws_ml[2 * (slot0 + c)]);
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-  for (int c = 0; c < nc; ++c) {
-    const float sc = __builtin_amdgcn_exp2f(p.ws_ml[2 * (slot0 + c)] - M);
-    Ls = fmaf(p.ws_ml[2 * (slot0 + c) + 1], sc, Ls);
-    const float* src = p.ws_o + (slot0 + c) * D + lane * DPL;
+  for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+  m = max_with_partner(m);
+  if (lane == 0) s_max[wave] = m;
+  __syncthreads();
+  float M = s_max[0];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] = fmaf(src[e], sc, acc[e]);
+  for (int w = 1; w < NWV; ++w) M = fmaxf(M, s_max[w]);
+  // this thread's four features summed over its row's chunks, each weighted by 2^(m_c - M)
+  const int f = tid % F4, row = tid / F4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float ls = 0.f;
+  for (int c = row; c < nc; c += R) {
+    const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + 2 * (slot0 + c));
+    const float wgt = __builtin_amdgcn_exp2f(ml.x - M);
+    ls = fmaf(ml.y, wgt, ls);
+    const float4 o4 = *reinterpret_cast<const float4*>(p.ws_o + (slot0 + c) * D + 4 * f);
+    acc.x = fmaf(o4.x, wgt, acc.x);
+    acc.y = fmaf(o4.y, wgt, acc.y);
+    acc.z = fmaf(o4.z, wgt, acc.z);
+    acc.w = fmaf(o4.w, wgt, acc.w);
+  }
+  s_o[row][f] = acc;
+  if (f == 0) s_l[row] = ls;
+  __syncthreads();
+  if (tid >= F4) return;
+  float4 a = s_o[0][tid];
+  float Ls = s_l[0];
+#pragma unroll
+  for (int r = 1; r < R; ++r) {
+    const float4 o4 = s_o[r][tid];
+    a.x += o4.x;
+    a.y += o4.y;
+    a.z += o4.z;
+    a.w += o4.w;
+    Ls += s_l[r];
   }
   const float inv = 1.f / Ls;
-  if constexpr (DPL == 2) {
-    *reinterpret_cast<uint32_t*>(ob) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-  } else {
-    ob[0] = __builtin_bit_cast(uint16_t, (__bf16)(acc[0] * inv));
-  }
-  if (p.lse && lane == 0) p.lse[bh] = (M + __log2f(Ls)) * kLn2;
+  uint2 st;
+  st.x = pack_bf16x2(a.x * inv, a.y * inv);
+  st.y = pack_bf16x2(a.z * inv, a.w * inv);
+  *reinterpret_cast<uint2*>(ob + 4 * tid) = st;
+  if (p.lse && tid == 0) p.lse[bh] = (M + __log2f(Ls)) * kLn2;
 }
 
 // One workgroup of NW waves per (sequence, head): the visible key range is split into 64-key chunks
@@ -408,7 +446,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs p) {
 
 template <int D, bool STEP>
 static hipError_t launch_decode_d(const DecArgs& a, hipStream_t s) {
-  if (decode_uses_fused(a.B, a.H)) {
+  if (decode_uses_fused(a.B, a.H, a.Lcap, a.window)) {
     hipLaunchKernelGGL((decode_fused_kernel<D, 8, STEP>), dim3(a.B * a.H), dim3(512), 0, s, a);
     return hipGetLastError();
   }
@@ -417,7 +455,8 @@ static hipError_t launch_decode_d(const DecArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((decode_split_kernel<D, STEP>), dim3(a.H, nc, a.B), dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D, STEP>), dim3(a.B * a.H), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((decode_combine_kernel<D, STEP>), dim3(a.B * a.H), dim3(kCombineThreads), 0,
+                     s, a);
   return hipGetLastError();
 }
 

@@ -95,9 +95,18 @@ struct AppendArgs {
 
 constexpr int kDecodeChunk = 64;  // keys per split of the decode
 
-// Decode schedule: one workgroup per (sequence, head) when the pairs alone fill the GPU's CUs
-// several times over, else split each pair's keys across workgroups and merge in a second kernel.
-inline bool decode_uses_fused(int B, int H) { return (long long)B * H >= 512; }
+// Decode schedule: one workgroup of 8 waves per (sequence, head), its chunks merged in LDS, in one
+// launch; or one wave per (head, chunk, sequence) and a merge kernel.  Measured on MI355X (H = 15,
+// D = 128, ragged and full-length caches of 512 to 16384 rows): with at most 2048 visible rows the
+// one-launch schedule is at most 30% slower at 1-4 sequences over full caches and up to 25% faster
+// over ragged ones; over longer caches the split schedule is 1.1-4.3x faster below 128 (sequence,
+// head) pairs (one workgroup per pair leaves most CUs idle there), and 7-12% slower from 240 up.
+constexpr int kDecodeFusedMinPairs = 128;
+constexpr int kDecodeFusedMaxRows = 2048;
+inline bool decode_uses_fused(int B, int H, int Lcap, int window) {
+  const int visible = window < Lcap ? window : Lcap;
+  return (long long)B * H >= kDecodeFusedMinPairs || visible <= kDecodeFusedMaxRows;
+}
 
 hipError_t launch_fwd(const FwdArgs& a, bool f32, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s);

@@ -45,7 +45,8 @@
 extern "C" {
 #endif
 
-#define SWATTN_ABI_VERSION 4  /* 2: attn_decode_step; 3: *_varlen; 4: *_qknorm */
+#define SWATTN_ABI_VERSION 5  /* 2: attn_decode_step; 3: *_varlen; 4: *_qknorm;
+                                 5: attn_decode_launches */
 
 typedef enum { SWATTN_BF16 = 0, SWATTN_F32 = 1 } swattn_dtype;
 
@@ -123,12 +124,20 @@ int attn_prefill(const void* q, const void* kcache, const void* vcache, const in
 int attn_kv_append(void* kcache, void* vcache, const void* knew, const void* vnew, const int* pos,
                    int B, int H, int Lcap, int D, void* stream);
 
-/* Bytes of device workspace attn_decode needs (split-K partial results, float32). */
+/* Bytes of device workspace attn_decode needs (split-K partial results, float32; only the
+ * two-kernel schedule writes it, but every call checks its size). */
 size_t attn_decode_workspace_bytes(int B, int H, int Lcap, int D);
+
+/* Kernel launches that attn_decode and attn_decode_step make for these sizes: 1 (split-K inside a
+ * workgroup per (sequence, head), merged in LDS) or 2 (split across workgroups into the workspace,
+ * then a merge kernel).  Negative status for invalid sizes, as attn_decode. */
+int attn_decode_launches(int B, int H, int Lcap, int D, int window);
 
 /*
  * Engine decode: one new query per sequence attends to its cache (split-K over the cache length,
- * then a log-sum-exp merge of the partial results).
+ * then a log-sum-exp merge of the partial results).  One launch, with the split inside a
+ * workgroup per (sequence, head); two (split across workgroups, then a merge kernel) when fewer
+ * than 128 (sequence, head) pairs each see more than 2048 rows (min(window, Lcap) > 2048).
  *   q      [B, H, D] bf16 (read); kcache, vcache [B, Lcap, H, D] bf16 (read).
  *   lens   device int32 [B]: cached tokens including the new one (append first, then decode);
  *          the query sits at position L_b - 1.  Values are clamped to [0, Lcap]; L_b = 0 gives
@@ -145,8 +154,9 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
  * One Engine decode step, KV append and decode together: for each sequence b with
  * 0 <= pos[b] < Lcap, writes knew[b] / vnew[b] to cache row pos[b], then the query (at position
  * pos[b]) attends to rows max(0, pos[b] - window + 1) .. pos[b] of the updated cache.  The same
- * operation as attn_kv_append(pos) followed by attn_decode(lens = pos + 1), in one launch when
- * B * H >= 512 (two otherwise); no launch reads a cache row written in the same launch.  It makes
+ * operation as attn_kv_append(pos) followed by attn_decode(lens = pos + 1), in one launch (two
+ * when fewer than 128 (sequence, head) pairs each see more than 2048 rows, min(window, Lcap) >
+ * 2048); no launch reads a cache row written in the same launch.  It makes
  * no host synchronisation and issues no memset, so a model's whole decode step (one call per
  * layer) can be captured in one HIP graph and replayed per generated token.
  * (Operation: walkthrough, section "Pretraining", Engine paragraph -- the decode phase over the

@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
     assert {"attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_decode", "attn_prefill",
             "attn_kv_append", "attn_decode_step", "attn_fwd_varlen", "attn_bwd_varlen",
             "attn_fwd_qknorm", "attn_bwd_qknorm", "attn_bwd_workspace_bytes",
-            "attn_decode_workspace_bytes", "attn_last_error", "attn_abi_version"} == names
+            "attn_decode_workspace_bytes", "attn_decode_launches", "attn_last_error",
+            "attn_abi_version"} == names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -55,7 +56,7 @@ def test_nm_lists_only_c_symbols(lib):
 
 
 def test_abi_version(lib):
-    assert lib.attn_abi_version() == 4
+    assert lib.attn_abi_version() == 5
 
 
 P = 4096  # an aligned, non-null stand-in pointer: validation must fail before it is ever used
@@ -121,6 +122,19 @@ def test_prefill_append_decode_validation(lib):
     assert lib.attn_decode(P, P, P, P, P, None, 2, 2, 100, 128, 8, None, need, None) == -3
     assert lib.attn_decode(P, P, P, P, P, None, 2, 2, 100, 128, 0, P, need, None) == -1
     assert lib.attn_decode(P, P, P, None, P, None, 2, 2, 100, 128, 8, P, need, None) == -1
+
+
+def test_decode_schedule_rule(lib):
+    # one launch unless fewer than 128 (sequence, head) pairs each see more than 2048 rows
+    assert lib.attn_decode_launches(64, 15, 2048, 128, 1 << 30) == 1
+    assert lib.attn_decode_launches(1, 15, 2048, 128, 1 << 30) == 1
+    assert lib.attn_decode_launches(1, 15, 2049, 128, 1 << 30) == 2
+    assert lib.attn_decode_launches(1, 15, 16384, 128, 2048) == 1
+    assert lib.attn_decode_launches(8, 15, 16384, 64, 2049) == 2
+    assert lib.attn_decode_launches(8, 16, 16384, 128, 1 << 30) == 1
+    assert lib.attn_decode_launches(1, 15, 2049, 80, 1 << 30) == -2
+    assert lib.attn_decode_launches(0, 15, 2049, 128, 1 << 30) == -1
+    assert lib.attn_decode_launches(1, 15, 2049, 128, 0) == -1
 
 
 def test_decode_step_validation(lib):

@@ -245,18 +245,29 @@ def test_multi_batch_head_strides(sw):
 
 
 # --------------------------------------------------------------------------- Engine edge cases
+# Decode cases: (B, H, Lcap, cache lengths, windows, launches).  Few or many (sequence, head)
+# pairs over short caches take the one-launch schedule; few pairs that may each see more than 2048
+# rows take split-K across workgroups plus the merge kernel (the windows keep more than 2048 rows
+# visible there).
+DECODE_CASES = {
+    "one-launch-few": (8, 3, 200, [0, 1, 63, 64, 65, 128, 199, 200], (None, 1, 2, 64, 65, 100, 10 ** 6), 1),
+    "one-launch-many": (64, 8, 200, [0, 1, 63, 64, 65, 128, 199, 200], (None, 1, 2, 64, 65, 100, 10 ** 6), 1),
+    "split-merge": (8, 3, 2112, [0, 1, 65, 2047, 2048, 2049, 2111, 2112], (None, 2049, 2100, 10 ** 6), 2),
+}
+
+
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("B,H", [(8, 3), (64, 8)])  # split-K across workgroups / within one
-def test_decode_edge_lengths(sw, D, B, H):
-    Lcap = 200
-    edge = [0, 1, 63, 64, 65, 128, 199, 200]
-    lens = torch.tensor([edge[b % 8] for b in range(B)], dtype=torch.int32)
+@pytest.mark.parametrize("case", list(DECODE_CASES))
+def test_decode_edge_lengths(sw, D, case):
+    B, H, Lcap, edge, windows, launches = DECODE_CASES[case]
+    lens = torch.tensor([edge[b % len(edge)] for b in range(B)], dtype=torch.int32)
     g = torch.Generator().manual_seed(5 + D)
     kc = torch.randn(B, Lcap, H, D, generator=g).to(torch.bfloat16)
     vc = torch.randn(B, Lcap, H, D, generator=g).to(torch.bfloat16)
     q = torch.randn(B, H, D, generator=g).to(torch.bfloat16)
     kcd, vcd = kc.to(DEV), vc.to(DEV)
-    for window in (None, 1, 2, 64, 65, 100, 10 ** 6):
+    for window in windows:
+        assert sw.attn_decode_launches(B, H, Lcap, D, window) == launches, (case, window)
         o, lse = sw.attn_decode(q.to(DEV), kcd, vcd, lens.to(DEV), window=window, want_lse=True)
         torch.cuda.synchronize()
         o_r, lse_r = ref.decode(f64(q), f64(kc), f64(vc), lens.numpy(), window)
@@ -332,25 +343,30 @@ def test_determinism_and_full_window_bitwise(sw):
 
 
 def test_decode_deterministic_and_schedule_independent(sw):
-    """Decode repeats bit for bit, and its two schedules agree: the same 8 sequences decoded
-    within a batch of 64 (one workgroup per (sequence, head), B * H >= 512) and alone (64-key
-    chunks across workgroups, then a merge kernel, B * H < 512)."""
-    B, H, D, Lcap = 64, 8, 128, 700
+    """Decode repeats bit for bit, and its two schedules agree: the same 4 sequences decoded
+    within a batch of 64 (one workgroup per (sequence, head)) and alone (32 pairs over caches of
+    more than 2048 rows: 64-key chunks across workgroups, then a merge kernel)."""
+    B, H, D, Lcap, Bs = 64, 8, 128, 2176, 4
     g = torch.Generator().manual_seed(130)
     lens = torch.randint(1, Lcap + 1, (B,), generator=g, dtype=torch.int32)
-    kc, vc = (torch.randn(B, Lcap, H, D, generator=g).to(torch.bfloat16).to(DEV) for _ in range(2))
-    q = torch.randn(B, H, D, generator=g).to(torch.bfloat16).to(DEV)
+    lens[:2] = torch.tensor([Lcap, 2049], dtype=torch.int32)
+    gd = torch.Generator(device=DEV).manual_seed(130)
+    kc, vc = (torch.randn(B, Lcap, H, D, generator=gd, device=DEV).to(torch.bfloat16)
+              for _ in range(2))
+    q = torch.randn(B, H, D, generator=gd, device=DEV).to(torch.bfloat16)
     ld = lens.to(DEV)
-    for window in (None, 100):
+    for window in (None, 2100):
+        assert sw.attn_decode_launches(B, H, Lcap, D, window) == 1
+        assert sw.attn_decode_launches(Bs, H, Lcap, D, window) == 2
         runs = [sw.attn_decode(q, kc, vc, ld, window=window, want_lse=True) for _ in range(3)]
-        small = sw.attn_decode(q[:8].contiguous(), kc[:8].contiguous(), vc[:8].contiguous(),
-                               ld[:8].contiguous(), window=window, want_lse=True)
+        small = sw.attn_decode(q[:Bs].contiguous(), kc[:Bs].contiguous(), vc[:Bs].contiguous(),
+                               ld[:Bs].contiguous(), window=window, want_lse=True)
         torch.cuda.synchronize()
         for o, l in runs[1:]:
             assert torch.equal(o, runs[0][0]) and torch.equal(l, runs[0][1])
         o, l = runs[0]
-        assert (o[:8].float() - small[0].float()).abs().max().item() <= 2 ** -7 * o.abs().max().item()
-        assert (l[:8] - small[1]).abs().max().item() <= 1e-4
+        assert (o[:Bs].float() - small[0].float()).abs().max().item() <= 2 ** -7 * o.abs().max().item()
+        assert (l[:Bs] - small[1]).abs().max().item() <= 1e-4
 
 
 def test_split_passes_equal_attn_bwd(sw):
@@ -422,13 +438,19 @@ def test_autograd_wrapper_and_kvcache(sw):
 
 
 # ------------------------------------------------------------------ decode step (append + decode)
+STEP_CASES = {  # (B, H, Lcap, positions, windows, launches)
+    "one-launch-few": (8, 3, 200, [0, 1, 63, 64, 65, 128, 199, -1, 200], (None, 1, 2, 64, 65, 100), 1),
+    "one-launch-many": (64, 8, 200, [0, 1, 63, 64, 65, 128, 199, -1, 200], (None, 1, 2, 64, 65, 100), 1),
+    "split-merge": (8, 3, 2112, [0, 1, 2047, 2048, 2110, 2111, -1, 2112], (None, 2049, 2100), 2),
+}
+
+
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("B,H", [(8, 3), (64, 8)])  # split-K across workgroups / within one
-def test_decode_step_equals_append_then_decode(sw, D, B, H):
+@pytest.mark.parametrize("case", list(STEP_CASES))
+def test_decode_step_equals_append_then_decode(sw, D, case):
     """attn_decode_step(pos) is attn_kv_append(pos) then attn_decode(lens = pos + 1), bit for bit,
     and matches the oracle; a pos outside [0, Lcap) writes nothing and gives o = 0, lse = -inf."""
-    Lcap = 200
-    edge = [0, 1, 63, 64, 65, 128, 199, -1, 200]
+    B, H, Lcap, edge, windows, launches = STEP_CASES[case]
     pos = torch.tensor([edge[b % len(edge)] for b in range(B)], dtype=torch.int32)
     valid = ((pos >= 0) & (pos < Lcap)).numpy()
     g = torch.Generator().manual_seed(21 + D)
@@ -441,7 +463,8 @@ def test_decode_step_equals_append_then_decode(sw, D, B, H):
     vb = np.nonzero(valid)[0]  # the oracle's append covers in-range rows only
     kc_r[vb], vc_r[vb] = ref.kv_append(kc_r[vb], vc_r[vb], f64(kn)[vb], f64(vn)[vb],
                                        pos.numpy()[vb])
-    for window in (None, 1, 2, 64, 65, 100):
+    for window in windows:
+        assert sw.attn_decode_launches(B, H, Lcap, D, window) == launches, (case, window)
         k1, v1 = kc.to(DEV), vc.to(DEV)
         o1, lse1 = sw.attn_decode_step(qd, knd, vnd, k1, v1, posd, window=window, want_lse=True)
         k2, v2 = kc.to(DEV), vc.to(DEV)
@@ -456,12 +479,15 @@ def test_decode_step_equals_append_then_decode(sw, D, B, H):
         assert np.abs(f64(lse1)[valid] - lse_r[valid]).max() <= LSE_TOL
 
 
-@pytest.mark.parametrize("B,H", [(4, 2), (64, 8)])
-def test_decode_step_graph_replays_match_eager(sw, B, H):
+@pytest.mark.parametrize("B,H,Lcap,windows", [(4, 2, 96, [None, 5, 40]), (64, 8, 96, [None, 5, 40]),
+                                               (4, 2, 2100, [None, 5, 2049])])
+def test_decode_step_graph_replays_match_eager(sw, B, H, Lcap, windows):
     """A captured decode step over every layer, replayed token after token with unrelated eager
-    work and synchronisations in between, equals the same steps run eagerly, bit for bit."""
-    n_layer, Lcap, D = 3, 96, 128
-    windows = [None, 5, 40]
+    work and synchronisations in between, equals the same steps run eagerly, bit for bit.  With
+    Lcap = 2100 the layers with more than 2048 visible rows capture the two-launch schedule."""
+    n_layer, D = 3, 128
+    launches = [sw.attn_decode_launches(B, H, Lcap, D, w) for w in windows]
+    assert launches == ([2, 1, 2] if Lcap > 2048 else [1, 1, 1])
     g = torch.Generator().manual_seed(31 + B)
     lens0 = torch.randint(1, 60, (B,), generator=g, dtype=torch.int32)
     Tq = int(lens0.max())
@@ -491,7 +517,8 @@ def test_decode_step_graph_replays_match_eager(sw, B, H):
         assert torch.equal(graphed.k, eager.k) and torch.equal(graphed.v, eager.v), f"replay {s}"
         # the eager path itself against the oracle, last layer
         lens_now = f64(eager.lens).astype(np.int64)
-        o_r, _ = ref.decode(f64(ins[0][-1]), f64(eager.k[-1]), f64(eager.v[-1]), lens_now, 40)
+        o_r, _ = ref.decode(f64(ins[0][-1]), f64(eager.k[-1]), f64(eager.v[-1]), lens_now,
+                            windows[-1])
         assert np.abs(f64(o_e[-1]) - o_r).max() <= O_TOL, f"replay {s}"
 
 
