@@ -19,7 +19,8 @@ per layer); ``decode.small_batch`` the first 8 sequences alone, and ``decode.lon
 sequences over 16384 cached rows, where the decode takes its two-kernel schedule (split-K partials
 across workgroups, then the merge kernel); ``prefill`` TFLOP/s; ``varlen`` the d20 rows re-read as packed documents that attend
 only to themselves (attn_fwd_varlen / attn_bwd_varlen); ``qknorm`` the d20 layer with RMS-normalised
-q and k (attn_fwd_qknorm / attn_bwd_qknorm).  ``roofline`` describes the
+q and k (attn_fwd_qknorm / attn_bwd_qknorm); ``d26`` the alternating-window d26 layers (window
+512 and full causal, B=16, H=13).  ``roofline`` describes the
 longest-running MFMA kernel; ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
 d20 workload on the host cores.  One JSON line goes to stdout; progress goes to stderr.
 """
@@ -140,6 +141,8 @@ def main() -> int:
                     help="skip the QK-norm (normalised q, k) fwd+bwd measurement")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the packed-document (varlen) fwd+bwd measurement")
+    ap.add_argument("--no-d26", action="store_true",
+                    help="skip the d26 alternating-window layers (w = 512 and full) measurement")
     ap.add_argument("--no-small-batch", action="store_true",
                     help="skip the small-batch decode measurement")
     ap.add_argument("--no-long-context", action="store_true",
@@ -366,6 +369,46 @@ def main() -> int:
                   "note": "fwd includes the norm pass; FLOPs are the attention's only"}
         del gq, oq, lq, qn_, kn_, rq_, rk_
 
+    # d26 alternating-window layers (B 16, T 2048, H 13, D 128; windows 512, full, 512, full):
+    # layer 0 (w = 512) and layer 1 (full causal) of the same seeded stack, forward + backward,
+    # timed with events outside the timed region.  Algorithmic bytes: every input read once, every
+    # output written once.
+    d26 = None
+    if not args.no_d26:
+        log("d26 layers (w = 512 and full): forward + backward ...")
+        d26 = {}
+        for layer in (0, 1):
+            w26 = W.D26_WINDOWS[layer]
+            q6, k6, v6, do6 = (t.to(dev) for t in W.d26_layer_inputs(layer))
+            B6, T6, H6, D6 = q6.shape
+            o6 = torch.empty_like(q6)
+            lse6 = torch.empty((B6, H6, T6), device=dev, dtype=torch.float32)
+            g6 = [torch.empty_like(q6) for _ in range(3)]
+            ws6 = torch.empty(sw.attn_bwd_workspace_bytes(B6, H6, T6, D6), device=dev,
+                              dtype=torch.uint8)
+            reps = max(args.steps, 5)
+            ev6 = [[Ev() for _ in range(3)] for _ in range(reps + 2)]
+            for i in range(reps + 2):
+                ev6[i][0].record()
+                sw.attn_fwd(q6, k6, v6, o=o6, lse=lse6, window=w26)
+                ev6[i][1].record()
+                sw.attn_bwd(q6, k6, v6, o6, lse6, do6, window=w26, dq=g6[0], dk=g6[1], dv=g6[2],
+                            ws=ws6)
+                ev6[i][2].record()
+            torch.cuda.synchronize()
+            t6f = sum(e[0].elapsed_time(e[1]) for e in ev6[2:]) / reps * 1e-3
+            t6b = sum(e[1].elapsed_time(e[2]) for e in ev6[2:]) / reps * 1e-3
+            P6 = pairs(T6, w26) * B6 * H6
+            nb, nst = q6.numel() * 2, B6 * H6 * T6 * 4
+            d26[f"layer{layer}"] = {
+                "window": w26, "TFLOP/s": round(14 * D6 * P6 / (t6f + t6b) / 1e12, 2),
+                "fwd_ms": round(t6f * 1e3, 4), "bwd_ms": round(t6b * 1e3, 4),
+                "fwd_GB/s": round((4 * nb + nst) / t6f / 1e9, 1),
+                "bwd_GB/s": round((8 * nb + nst) / t6b / 1e9, 1)}
+            del q6, k6, v6, do6, o6, lse6, g6, ws6
+        d26["workload"] = ("d26 stack B16 T2048 H13 D128, seed 3: layer 0 (window 512) and "
+                           "layer 1 (full causal), fwd + bwd")
+
     # the whole 30-layer decode step (append + decode per layer, one launch each) captured in one
     # HIP graph and replayed per token; timed per replay with events, outside the timed region
     step_graph = None
@@ -504,6 +547,7 @@ def main() -> int:
                    "step_graph": step_graph, "small_batch": small,
                    "long_context": longctx},
         "prefill": {"TFLOP/s": round(pre_flops / t_pre / 1e12, 2), "ms_per_layer": round(t_pre * 1e3, 4)},
+        "d26": d26,
         "varlen": varlen,
         "qknorm": qknorm,
         "roofline": roofline,
