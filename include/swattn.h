@@ -25,7 +25,8 @@
  *              KV cache [B, Lcap, H, D]; LSE [B, H, T] float32 (natural log).
  *   Types:     bf16 storage with fp32 accumulation; the forward also accepts fp32 (SWATTN_F32).
  *   Pointers:  device memory owned by the caller; the library allocates nothing and keeps no state
- *              besides a read-only per-device property cache.  All pointers must be 16-byte aligned.
+ *              besides the thread-local error text.  Tensor and workspace pointers must be 16-byte
+ *              aligned; int32 length / position arrays and the decode's lse need 4 bytes.
  *   Streams:   `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue and return; the
  *              caller keeps every buffer alive until the stream has passed the kernels.
  *   Errors:    every check below runs on the host before any HIP call.  A failing call returns a
