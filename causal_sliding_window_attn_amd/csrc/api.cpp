@@ -67,6 +67,15 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int decode_chunks(int Lcap) { return (Lcap + swattn::kDecodeChunk - 1) / swattn::kDecodeChunk; }
 
+// The split decode launches one workgroup per (head, chunk, sequence) with the chunk index on the
+// grid's y dimension, at most 65535.
+int check_decode_cap(const char* what, int Lcap) {
+  if (decode_chunks(Lcap) > 65535)
+    return fail(SWATTN_EINVAL, "%s: Lcap = %d exceeds %d rows", what, Lcap,
+                65535 * swattn::kDecodeChunk);
+  return SWATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -265,6 +274,7 @@ size_t attn_decode_workspace_bytes(int B, int H, int Lcap, int D) {
 
 int attn_decode_launches(int B, int H, int Lcap, int D, int window) {
   TRY(check_dims("attn_decode_launches", B, H, Lcap, "Lcap", D, window));
+  TRY(check_decode_cap("attn_decode_launches", Lcap));
   ok();
   return swattn::decode_uses_fused(B, H, Lcap, window) ? 1 : 2;
 }
@@ -273,6 +283,7 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
                 float* lse, int B, int H, int Lcap, int D, int window, void* ws, size_t ws_bytes,
                 void* stream) {
   TRY(check_dims("attn_decode", B, H, Lcap, "Lcap", D, window));
+  TRY(check_decode_cap("attn_decode", Lcap));
   TRY(check_ptr(q, "q"));
   TRY(check_ptr(kcache, "kcache"));
   TRY(check_ptr(vcache, "vcache"));
@@ -314,6 +325,7 @@ int attn_decode_step(const void* q, const void* knew, const void* vnew, void* kc
                      const int* pos, void* o, float* lse, int B, int H, int Lcap, int D,
                      int window, void* ws, size_t ws_bytes, void* stream) {
   TRY(check_dims("attn_decode_step", B, H, Lcap, "Lcap", D, window));
+  TRY(check_decode_cap("attn_decode_step", Lcap));
   TRY(check_ptr(q, "q"));
   TRY(check_ptr(knew, "knew"));
   TRY(check_ptr(vnew, "vnew"));

@@ -146,6 +146,7 @@ int attn_decode_launches(int B, int H, int Lcap, int D, int window);
  *   o      [B, H, D] bf16 (written);  lse [B, H] float32 or NULL.
  *   window keys visible to the query, counting itself.
  *   ws / ws_bytes: caller-owned device scratch of at least attn_decode_workspace_bytes().
+ *   Lcap <= 65535 * 64 (the split schedule puts the 64-row chunk index on a grid dimension).
  */
 int attn_decode(const void* q, const void* kcache, const void* vcache, const int* lens, void* o,
                 float* lse, int B, int H, int Lcap, int D, int window, void* ws, size_t ws_bytes,

@@ -135,6 +135,10 @@ def test_decode_schedule_rule(lib):
     assert lib.attn_decode_launches(1, 15, 2049, 80, 1 << 30) == -2
     assert lib.attn_decode_launches(0, 15, 2049, 128, 1 << 30) == -1
     assert lib.attn_decode_launches(1, 15, 2049, 128, 0) == -1
+    assert lib.attn_decode_launches(1, 15, 65535 * 64, 128, 1 << 30) == 2
+    assert lib.attn_decode_launches(1, 15, 65535 * 64 + 1, 128, 1 << 30) == -1
+    need = lib.attn_decode_workspace_bytes(1, 1, 65535 * 64 + 1, 128)
+    assert lib.attn_decode(P, P, P, P, P, None, 1, 1, 65535 * 64 + 1, 128, 8, P, need, None) == -1
 
 
 def test_decode_step_validation(lib):
