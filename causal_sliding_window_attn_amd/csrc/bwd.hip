@@ -96,10 +96,11 @@ __device__ __forceinline__ BwdRows bwd_rows(const BwdArgs& p, int b, int h, int 
 }
 
 // ------------------------------------------------------------------------------------------ dQ
-// dS^T = P^T (dP^T - Delta) for one 32-key block, in place in the S^T accumulator.
+// dS^T = P^T (dP^T - Delta) for one 32-key block, in place in the S^T accumulator; `dp` already
+// holds dP^T - Delta (its MFMA chain starts from -Delta).
 template <bool MASK>
 __device__ __forceinline__ void dq_ds(f32x16& s, const f32x16& dp, int d0, int w, float sl2,
-                                      float lse2, float delta) {
+                                      float lse2) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse2));
@@ -108,7 +109,7 @@ __device__ __forceinline__ void dq_ds(f32x16& s, const f32x16& dp, int d0, int w
       const unsigned dist = (unsigned)(d0 - (8 * (r >> 2) + (r & 3)));
       pr = dist < (unsigned)w ? pr : 0.f;
     }
-    s[r] = pr * (dp[r] - delta);
+    s[r] = pr * dp[r];
   }
 }
 
@@ -117,7 +118,7 @@ __device__ __forceinline__ void dq_ds(f32x16& s, const f32x16& dp, int d0, int w
 template <int D>
 __device__ __forceinline__ void dq_tile(const uint16_t* __restrict__ sK,
                                         const uint16_t* __restrict__ sV, bool mask, int k_lo,
-                                        int qi, int w, float sl2, float lse2, float delta,
+                                        int qi, int w, float sl2, float lse2, const f32x16& ndelta,
                                         const uint4 (&qf)[D / 16], const uint4 (&df)[D / 16],
                                         const LdsOffsets<D>& lo, f32x16 (&dqacc)[D / 32],
                                         int lane) {
@@ -125,7 +126,8 @@ __device__ __forceinline__ void dq_tile(const uint16_t* __restrict__ sK,
   const int half = lane >> 5;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    f32x16 s = zero16(), dp = zero16();
+    // the dP^T chain takes -Delta (the lane's query) as its first C operand: no subtraction later
+    f32x16 s = zero16(), dp = ndelta;
 #pragma unroll
     for (int t = 0; t < DK; ++t) {
       s = mfma32(rc_frag<D>(sK, lo, nb, t), qf[t], s);
@@ -134,9 +136,9 @@ __device__ __forceinline__ void dq_tile(const uint16_t* __restrict__ sK,
     sched_mfma_chain<2 * DK, 1, 8>();
     const int d0 = qi - (k_lo + nb * 32) - 4 * half;
     if (mask)
-      dq_ds<true>(s, dp, d0, w, sl2, lse2, delta);
+      dq_ds<true>(s, dp, d0, w, sl2, lse2);
     else
-      dq_ds<false>(s, dp, d0, w, sl2, lse2, delta);
+      dq_ds<false>(s, dp, d0, w, sl2, lse2);
     const uint4 dsf[2] = {pack_frag(s, 0), pack_frag(s, 1)};
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -153,7 +155,7 @@ __device__ __forceinline__ void dq_step(const uint16_t* __restrict__ cur,
                                         uint16_t* __restrict__ nxt, bool issue_next,
                                         const uint16_t* kb, const uint16_t* vb, int rs, int T,
                                         int kt, int qa, int qi, int w, float sl2, float lse2,
-                                        float delta, const uint4 (&qf)[D / 16],
+                                        const f32x16& ndelta, const uint4 (&qf)[D / 16],
                                         const uint4 (&df)[D / 16], const LdsOffsets<D>& lo,
                                         f32x16 (&dqacc)[D / 32], int wave, int lane) {
   constexpr int BC = kBwdBC, TILE = BC * D;
@@ -164,7 +166,7 @@ __device__ __forceinline__ void dq_step(const uint16_t* __restrict__ cur,
   const int k_lo = kt * BC, k_hi = k_lo + BC - 1, qz = qa + 31;
   if ((qa >= T) || (k_lo > qz) || (qa - k_hi >= w)) return;
   const bool mask = !(k_hi <= qa && qz - k_lo < w);
-  dq_tile<D>(cur, cur + TILE, mask, k_lo, qi, w, sl2, lse2, delta, qf, df, lo, dqacc, lane);
+  dq_tile<D>(cur, cur + TILE, mask, k_lo, qi, w, sl2, lse2, ndelta, qf, df, lo, dqacc, lane);
 }
 
 // One job: query tile qt (NW waves x 32 queries) of head bh.  Returns with every wave past its
@@ -231,6 +233,9 @@ __device__ __forceinline__ void dq_job(const BwdArgs& p, int bh, int qt, uint16_
     p.lse2[rw.stat + qi] = lse_raw * kLog2e;  // the dK/dV pass reads LSE in base 2
   }
   const float lse2 = qvalid ? lse_raw * kLog2e : 0.f;
+  f32x16 ndelta;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndelta[r] = -delta;
 
   f32x16 dqacc[MB];
 #pragma unroll
@@ -245,17 +250,17 @@ __device__ __forceinline__ void dq_job(const BwdArgs& p, int bh, int qt, uint16_
   for (; kt < kt_end; kt += 2) {
     wait_vmcnt<0>();
     __syncthreads();
-    dq_step<D, NW>(stage0, stage1, true, kb, vb, rs, T, kt, qa, qi, w, p.scale_log2, lse2, delta,
+    dq_step<D, NW>(stage0, stage1, true, kb, vb, rs, T, kt, qa, qi, w, p.scale_log2, lse2, ndelta,
                    qf, df, lo, dqacc, wave, lane);
     wait_vmcnt<0>();
     __syncthreads();
     dq_step<D, NW>(stage1, stage0, kt + 1 < kt_end, kb, vb, rs, T, kt + 1, qa, qi, w,
-                   p.scale_log2, lse2, delta, qf, df, lo, dqacc, wave, lane);
+                   p.scale_log2, lse2, ndelta, qf, df, lo, dqacc, wave, lane);
   }
   if (kt == kt_end) {
     wait_vmcnt<0>();
     __syncthreads();
-    dq_step<D, NW>(stage0, stage1, false, kb, vb, rs, T, kt, qa, qi, w, p.scale_log2, lse2, delta,
+    dq_step<D, NW>(stage0, stage1, false, kb, vb, rs, T, kt, qa, qi, w, p.scale_log2, lse2, ndelta,
                    qf, df, lo, dqacc, wave, lane);
   }
 
