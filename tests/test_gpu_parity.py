@@ -342,6 +342,25 @@ def test_determinism_and_full_window_bitwise(sw):
         assert torch.equal(a, b)
 
 
+def test_decode_long_cache_split_merge(sw):
+    """Few sequences over a 16384-row cache: up to 256 chunks per (sequence, head) meet in the
+    merge kernel (four chunks in flight per thread, plus the remainder), against the oracle."""
+    B, H, D, Lcap = 2, 3, 128, 16384
+    g = torch.Generator().manual_seed(140)
+    kc = torch.randn(B, Lcap, H, D, generator=g).to(torch.bfloat16)
+    vc = torch.randn(B, Lcap, H, D, generator=g).to(torch.bfloat16)
+    q = torch.randn(B, H, D, generator=g).to(torch.bfloat16)
+    lens = torch.tensor([Lcap, 9001], dtype=torch.int32)
+    kcd, vcd = kc.to(DEV), vc.to(DEV)
+    for window in (None, 5000):
+        assert sw.attn_decode_launches(B, H, Lcap, D, window) == 2
+        o, lse = sw.attn_decode(q.to(DEV), kcd, vcd, lens.to(DEV), window=window, want_lse=True)
+        torch.cuda.synchronize()
+        o_r, lse_r = ref.decode(f64(q), f64(kc), f64(vc), lens.numpy(), window)
+        assert np.abs(f64(o) - o_r).max() <= O_TOL, f"window {window}"
+        assert np.abs(f64(lse) - lse_r).max() <= LSE_TOL, f"window {window}"
+
+
 def test_decode_deterministic_and_schedule_independent(sw):
     """Decode repeats bit for bit, and its two schedules agree: the same 4 sequences decoded
     within a batch of 64 (one workgroup per (sequence, head)) and alone (32 pairs over caches of
