@@ -21,7 +21,8 @@ sequences over 16384 cached rows, where the decode takes its two-kernel schedule
 across workgroups, then the merge kernel); ``prefill`` TFLOP/s; ``varlen`` the d20 rows re-read as packed documents that attend
 only to themselves (attn_fwd_varlen / attn_bwd_varlen); ``qknorm`` the d20 layer with RMS-normalised
 q and k (attn_fwd_qknorm / attn_bwd_qknorm); ``d26`` the alternating-window d26 layers (window
-512 and full causal, B=16, H=13).  ``roofline`` describes the
+512 and full causal, B=16, H=13); ``small_configs`` the tiny fp32 forward and the small bf16
+fwd + bwd (launch-latency bound).  ``roofline`` describes the
 longest-running MFMA kernel; ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
 d20 workload on the host cores.  One JSON line goes to stdout; progress goes to stderr.
 """
@@ -144,6 +145,8 @@ def main() -> int:
                     help="skip the packed-document (varlen) fwd+bwd measurement")
     ap.add_argument("--no-d26", action="store_true",
                     help="skip the d26 alternating-window layers (w = 512 and full) measurement")
+    ap.add_argument("--no-small-configs", action="store_true",
+                    help="skip the tiny fp32 and small bf16 configuration measurements")
     ap.add_argument("--no-small-batch", action="store_true",
                     help="skip the small-batch decode measurement")
     ap.add_argument("--no-long-context", action="store_true",
@@ -453,6 +456,39 @@ def main() -> int:
         torch.cuda.synchronize()
         return sum(a.elapsed_time(b) for a, b in evs[2:]) / reps * 1e-3
 
+    # the two small training configurations (fp32 tiny forward, B 1 T 128 H 2 D 64 full causal;
+    # bf16 small fwd + bwd, B 2 T 512 H 4 D 128 window 128), 50 back-to-back calls per pass:
+    # launch-latency bound, reported for completeness
+    small_cfg = None
+    if not args.no_small_configs:
+        log("small configurations (tiny fp32 forward, small bf16 fwd + bwd) ...")
+        small_cfg = {}
+        tc = W.TINY_F32
+        qt_, kt_, vt_ = (t.to(dev) for t in W.attn_inputs(tc)[:3])
+        ot_ = torch.empty_like(qt_)
+        lt_ = torch.empty((tc.B, tc.H, tc.T), device=dev, dtype=torch.float32)
+        n_rep = 50
+        t_t = queued_pass_time([lambda i: sw.attn_fwd(qt_, kt_, vt_, o=ot_, lse=lt_, window=tc.window)]
+                               * n_rep, 5) / n_rep
+        small_cfg["tiny_fp32_fwd"] = {"us_per_call": round(t_t * 1e6, 2),
+                                      "TFLOP/s": round(4 * tc.D * pairs(tc.T, tc.window) * tc.B
+                                                       * tc.H / t_t / 1e12, 4)}
+        sc_ = W.SMALL_W128
+        qs_, ks_, vs_, dos_ = (t.to(dev) for t in W.attn_inputs(sc_))
+        os_ = torch.empty_like(qs_)
+        ls_ = torch.empty((sc_.B, sc_.H, sc_.T), device=dev, dtype=torch.float32)
+        gs_ = [torch.empty_like(qs_) for _ in range(3)]
+        wss_ = torch.empty(sw.attn_bwd_workspace_bytes(sc_.B, sc_.H, sc_.T, sc_.D), device=dev,
+                           dtype=torch.uint8)
+        t_sf = queued_pass_time([lambda i: sw.attn_fwd(qs_, ks_, vs_, o=os_, lse=ls_,
+                                                       window=sc_.window)] * n_rep, 5) / n_rep
+        t_sb = queued_pass_time([lambda i: sw.attn_bwd(qs_, ks_, vs_, os_, ls_, dos_,
+                                                       window=sc_.window, dq=gs_[0], dk=gs_[1],
+                                                       dv=gs_[2], ws=wss_)] * n_rep, 5) / n_rep
+        ps_ = pairs(sc_.T, sc_.window) * sc_.B * sc_.H
+        small_cfg["small_bf16_w128"] = {"fwd_us": round(t_sf * 1e6, 2), "bwd_us": round(t_sb * 1e6, 2),
+                                        "TFLOP/s": round(14 * sc_.D * ps_ / (t_sf + t_sb) / 1e12, 3)}
+
     # small-batch decode: the first 8 sequences of the same Engine caches, all 30 layers, outside
     # the timed region
     small = None
@@ -552,6 +588,7 @@ def main() -> int:
                    "long_context": longctx},
         "prefill": {"TFLOP/s": round(pre_flops / t_pre / 1e12, 2), "ms_per_layer": round(t_pre * 1e3, 4)},
         "d26": d26,
+        "small_configs": small_cfg,
         "varlen": varlen,
         "qknorm": qknorm,
         "roofline": roofline,

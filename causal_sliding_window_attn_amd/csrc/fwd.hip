@@ -351,7 +351,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs p) {
   constexpr int NW = 4, BR = 32 * NW, BC = 32, NT = 64 * NW, MB = D / 32;
   constexpr int SK = D + 1;  // padded row stride (floats) against bank conflicts
   __shared__ float sK[BC * SK];
-  __shared__ float sV[BC * D];
+  __shared__ __attribute__((aligned(16))) float sV[BC * D];
 
   const float* qg = reinterpret_cast<const float*>(p.q);
   const float* kg = reinterpret_cast<const float*>(p.k);
@@ -391,12 +391,25 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs p) {
 
   for (int kt = kt_begin; kt <= kt_end; ++kt) {
     __syncthreads();
-    for (int idx = tid; idx < BC * D; idx += NT) {
-      const int r = idx / D, d = idx % D;
+    // 16-byte loads, all of a thread's issued before any store (rows are 16-byte aligned)
+    constexpr int C4 = D / 4;
+    static_assert((BC * C4) % NT == 0, "whole float4 loads per thread");
+#pragma unroll
+    for (int it = 0; it < BC * C4 / NT; ++it) {
+      const int idx = tid + it * NT;
+      const int r = idx / C4, c4 = idx % C4;
       const int j = kt * BC + r;
-      const bool ok = j < L;
-      sK[r * SK + d] = ok ? kb[(int64_t)j * rs + d] : 0.f;
-      sV[r * D + d] = ok ? vb[(int64_t)j * rs + d] : 0.f;
+      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+      if (j < L) {
+        kv = *reinterpret_cast<const float4*>(kb + (int64_t)j * rs + 4 * c4);
+        vv = *reinterpret_cast<const float4*>(vb + (int64_t)j * rs + 4 * c4);
+      }
+      float* dk = sK + r * SK + 4 * c4;  // padded rows: four scalar stores
+      dk[0] = kv.x;
+      dk[1] = kv.y;
+      dk[2] = kv.z;
+      dk[3] = kv.w;
+      *reinterpret_cast<float4*>(sV + r * D + 4 * c4) = vv;
     }
     __syncthreads();
     const int k_lo = kt * BC, k_hi = k_lo + BC - 1, qz = qa + 31;
