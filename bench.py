@@ -2,38 +2,42 @@
 """Benchmark of the windowed causal attention hot path on one MI355X.
 
 One step is one pass over every part of the path, on synthetic data of the pages' shapes:
-  * the d20 training layer (B=32, T=2048, H=10, D=128, bf16, full causal): forward, dQ pass,
-    dK/dV pass;
+  * the d20 training layer (B=32, T=2048, H=10, D=128, bf16, full causal): forward and backward
+    (each backward entry point timed on its own);
   * one Engine decode step of the d30-style model (30 layers, B=64, H=15, D=128, cache 2048,
     prompts U[32,1024], window 1024 on odd layers): every layer's KV append, then every
-    layer's decode (split-K inside each workgroup at this batch), the 30 decodes between one
-    pair of events;
+    layer's decode, the 30 decodes between one pair of events;
   * one Engine prefill layer (the same prompts, layer step % 30).
-Every part is bracketed by HIP events on the stream the kernels run on.
+
+Timing protocol: every part of a step is bracketed by HIP events on the stream the kernels run on,
+and a 512 MiB scratch buffer is written just before each part (outside its events), so that no part
+finds its inputs in the 4 MB L2s or the 256 MB last-level cache.  Each figure is the median over the
+timed steps (the minimum and mean are reported next to it).  The GPU's clocks and power are sampled
+with amd-smi during the timed region.
 
 The headline ``value`` is the d20 fwd+bwd rate in TFLOP/s counting unmasked FLOPs only (4D per
-visible (query, key) pair forward, 10D backward).  ``decode`` reports algorithmic HBM GB/s (every
-visible cache row read once, plus q and o), next to a plain streaming read of the same byte count
-(the rate this GPU sustains at that size), and ``decode.step_graph`` the same decode step for all
-30 layers as one replay of a captured HIP graph (attn_decode_step: append and decode in one launch
-per layer); ``decode.small_batch`` the first 8 sequences alone, and ``decode.long_context`` 2
-sequences over 16384 cached rows, where the decode takes its two-kernel schedule (split-K partials
-across workgroups, then the merge kernel); ``prefill`` TFLOP/s; ``varlen`` the d20 rows re-read as packed documents that attend
-only to themselves (attn_fwd_varlen / attn_bwd_varlen); ``qknorm`` the d20 layer with RMS-normalised
-q and k (attn_fwd_qknorm / attn_bwd_qknorm); ``d26`` the alternating-window d26 layers (window
-512 and full causal, B=16, H=13); ``small_configs`` the tiny fp32 forward and the small bf16
-fwd + bwd (launch-latency bound).  ``roofline`` describes the
-longest-running MFMA kernel; ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
-d20 workload on the host cores.  One JSON line goes to stdout; progress goes to stderr.
+visible (query, key) pair forward, 10D backward), from the median times.  ``decode`` reports
+algorithmic HBM GB/s (every visible cache row read once, plus q and o), next to a plain streaming
+read of the same byte count; ``decode.reading_b`` the same decode over cache lengths drawn
+uniformly from 1..2048 (where the 1024 window bites); ``decode.step_graph`` the whole 30-layer
+decode step as one HIP-graph replay; ``decode.small_batch`` and ``decode.long_context`` two more
+batch shapes; ``prefill`` TFLOP/s; ``varlen`` the d20 rows as packed documents; ``qknorm`` the
+d20 layer with RMS-normalised q and k; ``d26`` the alternating-window d26 layers; ``small_configs``
+the tiny fp32 forward and the small bf16 fwd + bwd.  ``roofline`` describes the longest-running MFMA
+kernel, ``roofline_decode`` the decode kernel; ``cpu_baseline`` times the fp64 oracle on the same
+d20 inputs on the host cores.  One JSON line goes to stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import os
+import re
+import statistics
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -43,6 +47,7 @@ METRIC = "attn fwd+bwd TFLOP/s (unmasked FLOPs) & % bf16 MFMA peak; decode HBM G
 PEAK_MFMA_BF16 = 2500.0  # TFLOP/s, MI355X dense bf16 (published)
 PEAK_HBM = 8000.0        # GB/s, MI355X HBM3E (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+FLUSH_BYTES = 512 << 20  # > 256 MB last-level cache + 8 x 4 MB L2
 
 
 def log(*a):
@@ -56,10 +61,148 @@ def pairs(T: int, w) -> int:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the sources libswattn.so is built from (the HBM-traffic figures recorded in
+    profiles/ stand for these sources only)."""
+    from causal_sliding_window_attn_amd import build as bld
+
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "causal_sliding_window_attn_amd", "csrc", "*"))):
+    files = [os.path.join(bld.CSRC, s) for s in bld.SOURCES]
+    files += [os.path.join(bld.CSRC, s) for s in bld.HEADERS]
+    files.append(os.path.join(ROOT, "include", "swattn.h"))
+    for f in sorted(files):
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
+
+
+def stats_us(xs):
+    """Median, minimum and mean of a list of seconds, in microseconds."""
+    return {"median_us": round(statistics.median(xs) * 1e6, 2), "min_us": round(min(xs) * 1e6, 2),
+            "mean_us": round(sum(xs) / len(xs) * 1e6, 2), "n": len(xs)}
+
+
+# ------------------------------------------------------------------------------ clocks and power
+class SmiSampler:
+    """Samples the GPU's clocks and power with amd-smi in a background thread."""
+
+    def __init__(self):
+        self.samples, self.errors = [], []
+        self._stop = threading.Event()
+        self._t = None
+
+    @staticmethod
+    def _numbers(obj, path=""):
+        if isinstance(obj, dict):
+            for k, v in obj.items():
+                yield from SmiSampler._numbers(v, f"{path}/{k}")
+        elif isinstance(obj, list):
+            for i, v in enumerate(obj):
+                yield from SmiSampler._numbers(v, f"{path}/{i}")
+        else:
+            try:
+                yield path.lower(), float(obj)
+            except (TypeError, ValueError):
+                pass
+
+    def _once(self):
+        try:
+            r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--power", "--json"],
+                               capture_output=True, text=True, timeout=10)
+            if r.returncode != 0:
+                self.errors.append(r.stderr.strip()[-200:])
+                return
+            s = r.stdout[r.stdout.find("[") if r.stdout.lstrip().startswith("[") else
+                         r.stdout.find("{"):]
+            data = json.loads(s)
+            # gpu_data/0/clock/gfx_<n>/clk/value (MHz, one per XCD) and
+            # gpu_data/0/power/socket_power/value (W)
+            gfx, power = [], []
+            for path, val in self._numbers(data):
+                if re.search(r"/clock/gfx_\d+/clk/value$", path):
+                    gfx.append(val)
+                elif re.search(r"/power/socket_power/value$", path):
+                    power.append(val)
+            self.samples.append({"gfx_mhz": max(gfx) if gfx else None,
+                                 "power_w": max(power) if power else None})
+        except Exception as e:  # noqa: BLE001 -- a missing tool must not stop the measurement
+            self.errors.append(repr(e)[-200:])
+
+    def _run(self):
+        while not self._stop.is_set():
+            self._once()
+            self._stop.wait(0.05)
+
+    def start(self):
+        self._t = threading.Thread(target=self._run, daemon=True)
+        self._t.start()
+
+    def stop(self):
+        self._stop.set()
+        if self._t is not None:
+            self._t.join(timeout=15)
+        g = [s["gfx_mhz"] for s in self.samples if s["gfx_mhz"] is not None]
+        p = [s["power_w"] for s in self.samples if s["power_w"] is not None]
+        out = {"tool": "amd-smi metric -g 0 --clock --power --json", "samples": len(self.samples)}
+        if g:
+            out["gfx_clock_mhz"] = {"median": statistics.median(g), "min": min(g), "max": max(g)}
+        if p:
+            out["power_w"] = {"median": statistics.median(p), "min": min(p), "max": max(p)}
+        if not self.samples and self.errors:
+            out["error"] = self.errors[-1]
+        return out
+
+
+# ------------------------------------------------------------------------------ cpu baseline
+def host_info():
+    import numpy as np
+
+    info = {"affinity_cpus": len(os.sched_getaffinity(0)), "os_cpu_count": os.cpu_count()}
+    try:
+        model = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
+                 if l.startswith("model name")]
+        info["cpu_model"] = model[0] if model else None
+    except OSError:
+        info["cpu_model"] = None
+    try:
+        deps = np.show_config(mode="dicts").get("Build Dependencies", {})
+        blas = deps.get("blas", {})
+        info["numpy_blas"] = (f"{blas.get('name')} {blas.get('version')} "
+                              f"({blas.get('openblas configuration', '').strip()})")
+    except Exception as e:  # noqa: BLE001
+        info["numpy_blas"] = f"unknown ({e!r})"
+    return info
+
+
+def cpu_baseline(case, q, k, v, do, n_heads: int):
+    """The fp64 oracle, as it stands, on n_heads (b, h) heads of the d20 layer, fwd + bwd."""
+    import torch
+
+    from oracle import attention as ref
+
+    B, H = case.B, case.H
+    n_heads = min(n_heads, B * H)
+    if n_heads == B * H:  # the whole layer
+        heads = [(b, h) for b in range(B) for h in range(H)]
+    else:  # a spread of distinct heads
+        heads = sorted({((i * 13) % B, (i * 7) % H) for i in range(4 * n_heads)})[:n_heads]
+    pick = lambda t: torch.stack([t[b, :, h] for b, h in heads])[:, :, None, :].double().numpy()  # noqa: E731
+    Q, K, V, DO = pick(q), pick(k), pick(v), pick(do)
+    host = host_info()
+    threads = min(16, host["affinity_cpus"])
+    t0 = time.perf_counter()
+    ref.forward(Q, K, V, case.window, threads=threads)
+    ref.backward(Q, K, V, DO, case.window, threads=threads)
+    dt = time.perf_counter() - t0
+    flops = 14 * case.D * pairs(case.T, case.window) * len(heads)
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"fp64 oracle fwd+bwd on {len(heads)} of the {B * H} (b,h) heads of the d20 "
+                  f"layer (T={case.T}, D={case.D}, full causal), same seeded inputs; {dt:.2f} s "
+                  f"wall on {threads} worker threads (one single-threaded BLAS call each)",
+        "host": host,
+    }
 
 
 def stream_read_gbs(bufs, nbytes: int, reps: int = 3) -> float:
@@ -97,35 +240,15 @@ def stream_read_gbs(bufs, nbytes: int, reps: int = 3) -> float:
     return nbytes / t / 1e9
 
 
-def cpu_baseline(case, q, k, v, do, n_heads: int):
-    """The fp64 oracle, as it stands, on n_heads (b, h) heads of the d20 layer, fwd + bwd."""
-    import torch
-
-    from oracle import attention as ref
-
-    B, H = case.B, case.H
-    n_heads = min(n_heads, B * H)
-    if n_heads == B * H:  # the whole layer
-        heads = [(b, h) for b in range(B) for h in range(H)]
-    else:  # a spread of distinct heads
-        heads = sorted({((i * 13) % B, (i * 7) % H) for i in range(4 * n_heads)})[:n_heads]
-    pick = lambda t: torch.stack([t[b, :, h] for b, h in heads])[:, :, None, :].double().numpy()  # noqa: E731
-    Q, K, V, DO = pick(q), pick(k), pick(v), pick(do)
-    threads = min(16, len(os.sched_getaffinity(0)))
-    t0 = time.perf_counter()
-    ref.forward(Q, K, V, case.window, threads=threads)
-    ref.backward(Q, K, V, DO, case.window, threads=threads)
-    dt = time.perf_counter() - t0
-    flops = 14 * case.D * pairs(case.T, case.window) * len(heads)
-    return {
-        "value": round(flops / dt / 1e12, 6),
-        "unit": "TFLOP/s",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": f"fp64 oracle fwd+bwd on {len(heads)} of the {B * H} (b,h) heads of the d20 "
-                  f"layer (T={case.T}, D={case.D}, full causal), same seeded inputs; {dt:.2f} s "
-                  f"wall on {threads} threads",
-    }
+def traffic_entry(key: str, src_hash: str):
+    """HBM bytes per launch recorded in profiles/traffic.json for one (kernel, launch grid) entry,
+    or None when absent or recorded for other kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    tr = json.load(open(TRAFFIC_FILE))
+    if tr.get("source_hash") != src_hash:
+        return None
+    return tr.get("entries", {}).get(key)
 
 
 def main() -> int:
@@ -135,6 +258,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-heads", type=int, default=320)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the 512 MiB cache flush before each timed part")
+    ap.add_argument("--no-smi", action="store_true", help="do not sample clocks with amd-smi")
     ap.add_argument("--no-stream-ref", action="store_true",
                     help="skip the streaming-read reference of the decode roofline")
     ap.add_argument("--no-step-graph", action="store_true",
@@ -152,6 +278,8 @@ def main() -> int:
     ap.add_argument("--no-long-context", action="store_true",
                     help="skip the long-context decode (split-K across workgroups + merge kernel) "
                          "measurement")
+    ap.add_argument("--no-reading-b", action="store_true",
+                    help="skip the decode over cache lengths U[1, 2048]")
     ap.add_argument("--calib-copy-mib", type=int, default=1024,
                     help="after the timed region, one plain device copy of this size (the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -174,6 +302,34 @@ def main() -> int:
     props = torch.cuda.get_device_properties(dev)
     log(f"device: {props.name}, {props.multi_processor_count} CUs")
 
+    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush_n = [0]
+
+    def flush():
+        """Write 512 MiB so that the next part starts with cold L2 and last-level caches."""
+        if not args.no_flush:
+            flush_n[0] += 1
+            scratch.fill_(flush_n[0] & 0xFF)
+
+    Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def timed_parts(parts, reps, warm=2):
+        """Runs the named parts `warm + reps` times, each preceded by a flush and bracketed by its
+        own events; returns {name: [seconds per rep]} over the last reps."""
+        evs = [[(Ev(), Ev()) for _ in parts] for _ in range(warm + reps)]
+        for i in range(warm + reps):
+            for j, (_, fn) in enumerate(parts):
+                flush()
+                evs[i][j][0].record()
+                fn(i)
+                evs[i][j][1].record()
+        torch.cuda.synchronize()
+        return {name: [evs[i][j][0].elapsed_time(evs[i][j][1]) * 1e-3
+                       for i in range(warm, warm + reps)]
+                for j, (name, _) in enumerate(parts)}
+
+    med = statistics.median
+
     # ------------------------------------------------------------------ d20 training layer
     case = W.D20_LAYER
     log("drawing d20 inputs ...")
@@ -186,8 +342,8 @@ def main() -> int:
     ws_b = torch.empty(sw.attn_bwd_workspace_bytes(B, H, T, D), device=dev, dtype=torch.uint8)
     P20 = pairs(T, case.window) * B * H
     F_fwd = 4 * D * P20
-    F_dq = 2 * D * P20
-    F_dkdv = 8 * D * P20
+    F_bwd = 10 * D * P20
+    win = case.window
 
     # ------------------------------------------------------------------ d30 Engine
     E = W.D30_ENGINE
@@ -218,15 +374,18 @@ def main() -> int:
     ws_d = torch.empty(sw.attn_decode_workspace_bytes(E.B, E.H, E.Lcap, E.D), device=dev,
                        dtype=torch.uint8)
 
-    def decode_bytes(s: int, nb: int = E.B) -> int:
+    def decode_bytes_for(lens_list, nb: int = E.B) -> int:
         tot = 0
         for l in range(E.n_layer):
             w = E.window(l)
             for b in range(nb):
-                L = int(lens0[b]) + s + 1
+                L = int(lens_list[b])
                 tot += E.H * (min(L, w) if w else L) * E.D * 2 * 2
             tot += 2 * nb * E.H * E.D * 2  # q read, o written
         return tot
+
+    def decode_bytes(s: int, nb: int = E.B) -> int:
+        return decode_bytes_for([int(lens0[b]) + s + 1 for b in range(nb)], nb)
 
     def prefill_flops(layer: int) -> int:
         w = E.window(layer)
@@ -234,78 +393,102 @@ def main() -> int:
 
     # ------------------------------------------------------------------ timed loop
     n_total = args.warmup + args.steps
-    Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    ev = [[Ev() for _ in range(7)] for _ in range(n_total)]
-    win = case.window
+    part_names = ["fwd", "bwd_dq", "bwd_dkdv", "append", "decode", "prefill"]
+    ev = [[(Ev(), Ev()) for _ in part_names] for _ in range(n_total)]
 
     def step(i: int):
         e = ev[i]
         s = i % E.steps
-        e[0].record()
-        sw.attn_fwd(q, k, v, o=o, lse=lse, window=win)
-        e[1].record()
-        sw.attn_bwd_dq(q, k, v, o, lse, do, ws_b, window=win, dq=dq)
-        e[2].record()
-        sw.attn_bwd_dkdv(q, k, v, lse, do, ws_b, window=win, dk=dk, dv=dv)
-        e[3].record()
+
+        def part(j, fn):
+            flush()
+            e[j][0].record()
+            fn()
+            e[j][1].record()
+
+        part(0, lambda: sw.attn_fwd(q, k, v, o=o, lse=lse, window=win))
+        part(1, lambda: sw.attn_bwd_dq(q, k, v, o, lse, do, ws_b, window=win, dq=dq))
+        part(2, lambda: sw.attn_bwd_dkdv(q, k, v, lse, do, ws_b, window=win, dk=dk, dv=dv))
+
         # the Engine step: every layer's KV append, then every layer's decode back to back (the
         # layers' caches are distinct, so the order is free), so that the decode events bracket
         # the 30 decode launches and no event falls between two of them
-        for l in range(E.n_layer):
-            sw.attn_kv_append(kcache[l], vcache[l], kn[l], vn[l], pos_tab[s])
-        e[4].record()
-        for l in range(E.n_layer):
-            sw.attn_decode(qn[l], kcache[l], vcache[l], len_tab[s], o=on, window=E.window(l),
-                           ws=ws_d)
-        e[5].record()
+        def appends():
+            for l in range(E.n_layer):
+                sw.attn_kv_append(kcache[l], vcache[l], kn[l], vn[l], pos_tab[s])
+
+        def decodes():
+            for l in range(E.n_layer):
+                sw.attn_decode(qn[l], kcache[l], vcache[l], len_tab[s], o=on, window=E.window(l),
+                               ws=ws_d)
+
+        part(3, appends)
+        part(4, decodes)
         pl = i % E.n_layer
-        sw.attn_prefill(qp, kcache[pl], vcache[pl], lens0_d, o=op, window=E.window(pl))
-        e[6].record()
+        part(5, lambda: sw.attn_prefill(qp, kcache[pl], vcache[pl], lens0_d, o=op,
+                                        window=E.window(pl)))
 
     log(f"warmup {args.warmup} steps ...")
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    smi = SmiSampler()
+    if not args.no_smi:
+        smi.start()
     log(f"timing {args.steps} steps ...")
     t0 = time.perf_counter()
     for i in range(args.warmup, n_total):
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clocks = smi.stop() if not args.no_smi else None
     log("timed region done")
 
     K = args.steps
-    timed = range(args.warmup, n_total)
-    t_fwd = sum(ev[i][0].elapsed_time(ev[i][1]) for i in timed) / K * 1e-3
-    t_dq = sum(ev[i][1].elapsed_time(ev[i][2]) for i in timed) / K * 1e-3
-    t_dkdv = sum(ev[i][2].elapsed_time(ev[i][3]) for i in timed) / K * 1e-3
-    t_app = sum(ev[i][3].elapsed_time(ev[i][4]) for i in timed) / K * 1e-3
-    t_dec = sum(ev[i][4].elapsed_time(ev[i][5]) for i in timed) / K * 1e-3
-    t_pre = sum(ev[i][5].elapsed_time(ev[i][6]) for i in timed) / K * 1e-3
-    dec_bytes = sum(decode_bytes(i % E.steps) for i in timed) / K
-    pre_flops = sum(prefill_flops(i % E.n_layer) for i in timed) / K
+    timed = list(range(args.warmup, n_total))
+    per = {name: [ev[i][j][0].elapsed_time(ev[i][j][1]) * 1e-3 for i in timed]
+           for j, name in enumerate(part_names)}
+    t_fwd, t_dq, t_dkdv = med(per["fwd"]), med(per["bwd_dq"]), med(per["bwd_dkdv"])
+    t_app, t_dec, t_pre = med(per["append"]), med(per["decode"]), med(per["prefill"])
+    dec_bytes_s = [decode_bytes(i % E.steps) for i in timed]
+    dec_gbs_s = [b / t / 1e9 for b, t in zip(dec_bytes_s, per["decode"])]
+    dec_bytes = sum(dec_bytes_s) / K
+    pre_flops_s = [prefill_flops(i % E.n_layer) for i in timed]
+    pre_tf_s = [f / t / 1e12 for f, t in zip(pre_flops_s, per["prefill"])]
     t_fb = t_fwd + t_dq + t_dkdv
-    value = (F_fwd + F_dq + F_dkdv) / t_fb / 1e12
-
-    kernels = {
-        "fwd_bf16_kernel": (F_fwd, t_fwd),
-        "bwd_dq_kernel": (F_dq, t_dq),
-        "bwd_dkdv_kernel": (F_dkdv, t_dkdv),
-    }
-    dom = max(kernels, key=lambda n: kernels[n][1])
-    f_dom, t_dom = kernels[dom]
-    achieved = f_dom / t_dom / 1e12
-    traffic = None
+    value = (F_fwd + F_bwd) / t_fb / 1e12
+    fb_min = min(a + b + c for a, b, c in zip(per["fwd"], per["bwd_dq"], per["bwd_dkdv"]))
     src_hash = kernel_source_hash()
-    if os.path.exists(TRAFFIC_FILE):
-        tr = json.load(open(TRAFFIC_FILE))
-        ent = tr.get("kernels", {}).get(dom)
-        if ent and tr.get("source_hash") == src_hash:
-            traffic = ent["hbm_bytes_per_launch"]
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
-                "peak": PEAK_MFMA_BF16, "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_BF16, 4),
-                "traffic": traffic, "avg_launch_us": round(t_dom * 1e6, 2),
-                "algorithmic_flops_per_launch": f_dom}
+
+    # the longest-running MFMA kernel of the d20 layer, with the FLOPs the algorithm credits it
+    # (each backward entry point launches one kernel on this workload)
+    F_dq_credit, F_dkdv_credit = 2 * D * P20, 8 * D * P20
+    kernels = {
+        "fwd_bf16_kernel": ("d20 forward", F_fwd, t_fwd),
+        "bwd_dq_kernel": ("d20 dQ pass", F_dq_credit, t_dq),
+        "bwd_dkdv_kernel": ("d20 dK/dV pass", F_dkdv_credit, t_dkdv),
+    }
+    dom = max(kernels, key=lambda n: kernels[n][2])
+    dom_label, f_dom, t_dom = kernels[dom]
+    achieved = f_dom / t_dom / 1e12
+    tr_dom = traffic_entry(dom_label, src_hash)
+    roofline = {"bound": "mfma", "kernel": dom, "workload": dom_label,
+                "achieved": round(achieved, 2), "peak": PEAK_MFMA_BF16, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_MFMA_BF16, 4),
+                "traffic": tr_dom and tr_dom["hbm_bytes_per_launch"],
+                "traffic_grid": tr_dom and tr_dom["grid"],
+                "avg_launch_us": round(t_dom * 1e6, 2),
+                "algorithmic_flops_per_launch": f_dom,
+                "algorithmic_flops_per_pair": f_dom // P20, "pairs_per_launch": P20}
+    dec_achieved = dec_bytes / E.n_layer / (t_dec / E.n_layer) / 1e9
+    tr_dec = traffic_entry("d30 decode", src_hash)
+    roofline_decode = {"bound": "hbm", "kernel": "decode_fused_kernel", "workload": "d30 decode",
+                       "achieved": round(dec_achieved, 1), "peak": PEAK_HBM, "unit": "GB/s",
+                       "frac": round(dec_achieved / PEAK_HBM, 4),
+                       "traffic": tr_dec and tr_dec["hbm_bytes_per_launch"],
+                       "traffic_grid": tr_dec and tr_dec["grid"],
+                       "avg_launch_us": round(t_dec / E.n_layer * 1e6, 2),
+                       "algorithmic_bytes_per_launch": round(dec_bytes / E.n_layer)}
 
     # plain copy kernel of known size (rocprofv3 counter calibration); outside the timed region
     if args.calib_copy_mib > 0:
@@ -316,9 +499,10 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    reps = max(args.steps, 5)
+
     # packed documents in the same d20 rows (each document attends only to itself; the sequence
-    # offsets come from workloads.d20_packed_cu): the same q, k, v, dO viewed as [B*T, H, D],
-    # forward + backward timed with events, outside the timed region
+    # offsets come from workloads.d20_packed_cu): the same q, k, v, dO viewed as [B*T, H, D]
     varlen = None
     if not args.no_varlen:
         log("packed-document d20 rows: forward + backward ...")
@@ -332,18 +516,11 @@ def main() -> int:
         gv = [torch.empty_like(qv) for _ in range(3)]
         wsv = torch.empty(sw.attn_bwd_workspace_bytes(1, H, B * T, D), device=dev,
                           dtype=torch.uint8)
-        reps = max(args.steps, 5)
-        ev_v = [[Ev() for _ in range(3)] for _ in range(reps + 2)]
-        for i in range(reps + 2):
-            ev_v[i][0].record()
-            sw.attn_fwd_varlen(qv, kv, vv, cu_d, ms, o=ov, lse=lsev, window=win)
-            ev_v[i][1].record()
-            sw.attn_bwd_varlen(qv, kv, vv, ov, lsev, dov, cu_d, ms, window=win, dq=gv[0], dk=gv[1],
-                               dv=gv[2], ws=wsv)
-            ev_v[i][2].record()
-        torch.cuda.synchronize()
-        tv_f = sum(e[0].elapsed_time(e[1]) for e in ev_v[2:]) / reps * 1e-3
-        tv_b = sum(e[1].elapsed_time(e[2]) for e in ev_v[2:]) / reps * 1e-3
+        tv = timed_parts([
+            ("fwd", lambda i: sw.attn_fwd_varlen(qv, kv, vv, cu_d, ms, o=ov, lse=lsev, window=win)),
+            ("bwd", lambda i: sw.attn_bwd_varlen(qv, kv, vv, ov, lsev, dov, cu_d, ms, window=win,
+                                                 dq=gv[0], dk=gv[1], dv=gv[2], ws=wsv))], reps)
+        tv_f, tv_b = med(tv["fwd"]), med(tv["bwd"])
         pv = sum(pairs(L, win) for L in lens_d) * H
         varlen = {"TFLOP/s": round(14 * D * pv / (tv_f + tv_b) / 1e12, 2),
                   "fwd_ms": round(tv_f * 1e3, 4), "bwd_ms": round(tv_b * 1e3, 4),
@@ -352,33 +529,33 @@ def main() -> int:
                               "lengths, median 600, cut at row ends), same q, k, v, dO"}
         del ov, lsev, gv, wsv
 
-    # QK-norm on the d20 layer: the same q, k, v, dO; forward = norm pass + attention on the
+    # QK-norm on the d20 layer: the same q, k, v, dO; forward = norm + attention on the
     # normalised rows, backward = both passes with the norm's backward in their epilogues
     qknorm = None
     if not args.no_qknorm:
         log("QK-norm d20 layer: forward + backward ...")
-        reps = max(args.steps, 5)
-        ev_q = [[Ev() for _ in range(3)] for _ in range(reps + 2)]
         gq = [torch.empty_like(q) for _ in range(3)]
-        for i in range(reps + 2):
-            ev_q[i][0].record()
-            oq, lq, qn_, kn_, rq_, rk_ = sw.attn_fwd_qknorm(q, k, v, window=win)
-            ev_q[i][1].record()
+        fq = {}
+
+        def qk_fwd(i):
+            fq["r"] = sw.attn_fwd_qknorm(q, k, v, window=win)
+
+        def qk_bwd(i):
+            oq, lq, qn_, kn_, rq_, rk_ = fq["r"]
             sw.attn_bwd_qknorm(qn_, kn_, v, oq, lq, do, rq_, rk_, window=win, dq=gq[0], dk=gq[1],
                                dv=gq[2], ws=ws_b)
-            ev_q[i][2].record()
-        torch.cuda.synchronize()
-        tq_f = sum(e[0].elapsed_time(e[1]) for e in ev_q[2:]) / reps * 1e-3
-        tq_b = sum(e[1].elapsed_time(e[2]) for e in ev_q[2:]) / reps * 1e-3
-        qknorm = {"TFLOP/s": round((F_fwd + F_dq + F_dkdv) / (tq_f + tq_b) / 1e12, 2),
+
+        tq = timed_parts([("fwd", qk_fwd), ("bwd", qk_bwd)], reps)
+        tq_f, tq_b = med(tq["fwd"]), med(tq["bwd"])
+        qknorm = {"TFLOP/s": round((F_fwd + F_bwd) / (tq_f + tq_b) / 1e12, 2),
                   "fwd_ms": round(tq_f * 1e3, 4), "bwd_ms": round(tq_b * 1e3, 4),
-                  "note": "fwd includes the norm pass; FLOPs are the attention's only"}
-        del gq, oq, lq, qn_, kn_, rq_, rk_
+                  "overhead_vs_plain_ms": round((tq_f + tq_b - t_fb) * 1e3, 4),
+                  "note": "fwd includes the norm of q and k; FLOPs are the attention's only"}
+        del gq, fq
 
     # d26 alternating-window layers (B 16, T 2048, H 13, D 128; windows 512, full, 512, full):
-    # layer 0 (w = 512) and layer 1 (full causal) of the same seeded stack, forward + backward,
-    # timed with events outside the timed region.  Algorithmic bytes: every input read once, every
-    # output written once.
+    # layer 0 (w = 512) and layer 1 (full causal) of the same seeded stack, forward + backward.
+    # Algorithmic bytes: every input read once, every output written once.
     d26 = None
     if not args.no_d26:
         log("d26 layers (w = 512 and full): forward + backward ...")
@@ -392,18 +569,11 @@ def main() -> int:
             g6 = [torch.empty_like(q6) for _ in range(3)]
             ws6 = torch.empty(sw.attn_bwd_workspace_bytes(B6, H6, T6, D6), device=dev,
                               dtype=torch.uint8)
-            reps = max(args.steps, 5)
-            ev6 = [[Ev() for _ in range(3)] for _ in range(reps + 2)]
-            for i in range(reps + 2):
-                ev6[i][0].record()
-                sw.attn_fwd(q6, k6, v6, o=o6, lse=lse6, window=w26)
-                ev6[i][1].record()
-                sw.attn_bwd(q6, k6, v6, o6, lse6, do6, window=w26, dq=g6[0], dk=g6[1], dv=g6[2],
-                            ws=ws6)
-                ev6[i][2].record()
-            torch.cuda.synchronize()
-            t6f = sum(e[0].elapsed_time(e[1]) for e in ev6[2:]) / reps * 1e-3
-            t6b = sum(e[1].elapsed_time(e[2]) for e in ev6[2:]) / reps * 1e-3
+            t6 = timed_parts([
+                ("fwd", lambda i: sw.attn_fwd(q6, k6, v6, o=o6, lse=lse6, window=w26)),
+                ("bwd", lambda i: sw.attn_bwd(q6, k6, v6, o6, lse6, do6, window=w26, dq=g6[0],
+                                              dk=g6[1], dv=g6[2], ws=ws6))], reps)
+            t6f, t6b = med(t6["fwd"]), med(t6["bwd"])
             P6 = pairs(T6, w26) * B6 * H6
             nb, nst = q6.numel() * 2, B6 * H6 * T6 * 4
             d26[f"layer{layer}"] = {
@@ -416,7 +586,7 @@ def main() -> int:
                            "layer 1 (full causal), fwd + bwd")
 
     # the whole 30-layer decode step (append + decode per layer, one launch each) captured in one
-    # HIP graph and replayed per token; timed per replay with events, outside the timed region
+    # HIP graph and replayed per token
     step_graph = None
     if not args.no_step_graph:
         log("decode step graph: capture and replay ...")
@@ -424,41 +594,58 @@ def main() -> int:
         sg.q.copy_(qn)
         sg.k_new.copy_(kn)
         sg.v_new.copy_(vn)
-        reps = max(args.steps, 5)
-        ev_g = [(Ev(), Ev()) for _ in range(reps + 2)]
-        for i in range(reps + 2):
-            eng.lens.copy_(pos_tab[i % E.steps])
-            ev_g[i][0].record()
-            sg.replay()
-            ev_g[i][1].record()
-        torch.cuda.synchronize()
-        t_g = sum(a.elapsed_time(b) for a, b in ev_g[2:]) / reps * 1e-3
+        lmax0 = int(lens0.max())
+        tg = timed_parts([("replay", lambda i: (
+            eng.set_lens(pos_tab[i % E.steps], max_len=lmax0 + i % E.steps), sg.replay()))], reps)
+        t_g = med(tg["replay"])
         g_bytes = sum(decode_bytes(i % E.steps) for i in range(2, reps + 2)) / reps
         step_graph = {"us_per_layer_step": round(t_g / E.n_layer * 1e6, 2),
                       "GB/s": round(g_bytes / t_g / 1e9, 1),
                       "frac_of_hbm_peak": round(g_bytes / t_g / 1e9 / PEAK_HBM, 4),
-                      "us_per_token_all_layers": round(t_g * 1e6, 1), "replays": reps}
+                      "us_per_token_all_layers": round(t_g * 1e6, 1), "replays": reps,
+                      "note": "includes the lens reset copy before each replay"}
         del sg
 
-    # Short decode calls take less GPU time than the host needs to launch them, so the two figures
-    # below time whole passes of calls queued behind ~1 ms of unrelated GPU work (a bf16 matmul):
-    # by the time the first call runs, the host has queued them all.
+    # decode over cache lengths drawn uniformly from 1..2048 (the 1024 window of the odd layers
+    # then limits most rows), same caches and queries, all 30 layers
+    reading_b = None
+    if not args.no_reading_b:
+        log("decode over cache lengths U[1, 2048] ...")
+        gb = torch.Generator("cpu").manual_seed(E.seed + 2)
+        lens_b = torch.randint(1, E.Lcap + 1, (E.B,), generator=gb, dtype=torch.int32)
+        lens_bd = lens_b.to(dev)
+
+        def decodes_b(i):
+            for l in range(E.n_layer):
+                sw.attn_decode(qn[l], kcache[l], vcache[l], lens_bd, o=on, window=E.window(l),
+                               ws=ws_d)
+
+        tb = timed_parts([("decode", decodes_b)], reps)
+        t_b = med(tb["decode"])
+        b_bytes = decode_bytes_for(lens_b.tolist())
+        reading_b = {"us_per_layer_step": round(t_b / E.n_layer * 1e6, 2),
+                     "GB/s": round(b_bytes / t_b / 1e9, 1),
+                     "frac_of_hbm_peak": round(b_bytes / t_b / 1e9 / PEAK_HBM, 4),
+                     "bytes_per_layer_step": round(b_bytes / E.n_layer),
+                     "lens": "U[1, 2048], seed 6, the Engine's 64 sequences"}
+
+    # Short calls take less GPU time than the host needs to launch them, so the figures below time
+    # whole passes of calls queued behind ~1 ms of unrelated GPU work (a bf16 matmul): by the time
+    # the first call runs, the host has queued them all.
     busy = torch.randn((8192, 8192), device=dev, dtype=torch.bfloat16)
 
-    def queued_pass_time(calls, reps):
-        evs = [(Ev(), Ev()) for _ in range(reps + 2)]
-        for i in range(reps + 2):
+    def queued_pass_times(calls, n):
+        evs = [(Ev(), Ev()) for _ in range(n + 2)]
+        for i in range(n + 2):
+            flush()
             torch.matmul(busy, busy)
             evs[i][0].record()
             for c in calls:
                 c(i)
             evs[i][1].record()
         torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in evs[2:]) / reps * 1e-3
+        return [a.elapsed_time(b) * 1e-3 for a, b in evs[2:]]
 
-    # the two small training configurations (fp32 tiny forward, B 1 T 128 H 2 D 64 full causal;
-    # bf16 small fwd + bwd, B 2 T 512 H 4 D 128 window 128), 50 back-to-back calls per pass:
-    # launch-latency bound, reported for completeness
     small_cfg = None
     if not args.no_small_configs:
         log("small configurations (tiny fp32 forward, small bf16 fwd + bwd) ...")
@@ -468,8 +655,9 @@ def main() -> int:
         ot_ = torch.empty_like(qt_)
         lt_ = torch.empty((tc.B, tc.H, tc.T), device=dev, dtype=torch.float32)
         n_rep = 50
-        t_t = queued_pass_time([lambda i: sw.attn_fwd(qt_, kt_, vt_, o=ot_, lse=lt_, window=tc.window)]
-                               * n_rep, 5) / n_rep
+        t_t = med(queued_pass_times(
+            [lambda i: sw.attn_fwd(qt_, kt_, vt_, o=ot_, lse=lt_, window=tc.window)] * n_rep,
+            5)) / n_rep
         small_cfg["tiny_fp32_fwd"] = {"us_per_call": round(t_t * 1e6, 2),
                                       "TFLOP/s": round(4 * tc.D * pairs(tc.T, tc.window) * tc.B
                                                        * tc.H / t_t / 1e12, 4)}
@@ -480,22 +668,19 @@ def main() -> int:
         gs_ = [torch.empty_like(qs_) for _ in range(3)]
         wss_ = torch.empty(sw.attn_bwd_workspace_bytes(sc_.B, sc_.H, sc_.T, sc_.D), device=dev,
                            dtype=torch.uint8)
-        t_sf = queued_pass_time([lambda i: sw.attn_fwd(qs_, ks_, vs_, o=os_, lse=ls_,
-                                                       window=sc_.window)] * n_rep, 5) / n_rep
-        t_sb = queued_pass_time([lambda i: sw.attn_bwd(qs_, ks_, vs_, os_, ls_, dos_,
-                                                       window=sc_.window, dq=gs_[0], dk=gs_[1],
-                                                       dv=gs_[2], ws=wss_)] * n_rep, 5) / n_rep
+        t_sf = med(queued_pass_times([lambda i: sw.attn_fwd(qs_, ks_, vs_, o=os_, lse=ls_,
+                                                            window=sc_.window)] * n_rep, 5)) / n_rep
+        t_sb = med(queued_pass_times([lambda i: sw.attn_bwd(qs_, ks_, vs_, os_, ls_, dos_,
+                                                            window=sc_.window, dq=gs_[0], dk=gs_[1],
+                                                            dv=gs_[2], ws=wss_)] * n_rep, 5)) / n_rep
         ps_ = pairs(sc_.T, sc_.window) * sc_.B * sc_.H
         small_cfg["small_bf16_w128"] = {"fwd_us": round(t_sf * 1e6, 2), "bwd_us": round(t_sb * 1e6, 2),
                                         "TFLOP/s": round(14 * sc_.D * ps_ / (t_sf + t_sb) / 1e12, 3)}
 
-    # small-batch decode: the first 8 sequences of the same Engine caches, all 30 layers, outside
-    # the timed region
     small = None
     if not args.no_small_batch:
         Bs = 8
         log(f"small-batch decode (first {Bs} sequences) ...")
-        reps = max(args.steps, 5)
         on_s = on[:Bs]
         qs = [qn[l][:Bs] for l in range(E.n_layer)]
         ks = [kcache[l][:Bs] for l in range(E.n_layer)]
@@ -506,7 +691,7 @@ def main() -> int:
             return lambda i: sw.attn_decode(qs[l], ks[l], vs[l], lens_s, o=on_s,
                                             window=E.window(l), ws=ws_d)
 
-        t_s = queued_pass_time([small_call(l) for l in range(E.n_layer)], reps)
+        t_s = med(queued_pass_times([small_call(l) for l in range(E.n_layer)], reps))
         s_bytes = decode_bytes(0, Bs)
         small = {"B": Bs, "launches": sw.attn_decode_launches(Bs, E.H, E.Lcap, E.D),
                  "us_per_layer_step": round(t_s / E.n_layer * 1e6, 2),
@@ -514,9 +699,8 @@ def main() -> int:
                  "frac_of_hbm_peak": round(s_bytes / t_s / 1e9 / PEAK_HBM, 4)}
 
     # long-context decode: 2 sequences x 15 heads, each attending to all of its 16384 cached rows,
-    # four layers' caches in rotation (1 GB, beyond the last-level cache).  With 30 (sequence, head)
-    # pairs each reading more than 2048 rows, the decode splits every pair's keys across
-    # workgroups and merges the chunks in a second kernel; outside the timed region
+    # four layers' caches in rotation; the decode splits every pair's keys across workgroups and
+    # merges the chunks in a second kernel
     longctx = None
     if not args.no_long_context:
         Bl, Ll, nll = 2, 16384, 4
@@ -535,7 +719,7 @@ def main() -> int:
         def long_call(l):
             return lambda i: sw.attn_decode(ql, kl[l], vl[l], lens_l, o=ol, ws=ws_l)
 
-        t_l = queued_pass_time([long_call(l) for l in range(nll)], max(args.steps, 5)) / nll
+        t_l = med(queued_pass_times([long_call(l) for l in range(nll)], reps)) / nll
         l_bytes = Bl * E.H * Ll * E.D * 2 * 2 + 2 * Bl * E.H * E.D * 2
         longctx = {"B": Bl, "H": E.H, "L": Ll, "launches": sw.attn_decode_launches(Bl, E.H, Ll, E.D),
                    "us_per_call": round(t_l * 1e6, 2), "GB/s": round(l_bytes / t_l / 1e9, 1),
@@ -544,7 +728,7 @@ def main() -> int:
     del busy
 
     # streaming-read reference: a plain read of the decode step's byte count, rotating over the
-    # 30 layers' key caches (each larger than the last-level cache), outside the timed region
+    # 30 layers' key caches (each larger than the last-level cache)
     stream_ref = None
     if not args.no_stream_ref:
         stream_ref = stream_read_gbs(kcache, int(dec_bytes / E.n_layer))
@@ -574,25 +758,34 @@ def main() -> int:
                         "1024 on odd layers: one decode step + one prefill layer per step",
             "B": B, "T": T, "H": H, "D": D, "window": None,
         },
+        "timing": ("median over the timed steps of HIP-event intervals per part, each part "
+                   "preceded by a 512 MiB scratch write" if not args.no_flush else
+                   "median over the timed steps of HIP-event intervals per part, no flush"),
         "frac_of_peak": round(value / PEAK_MFMA_BF16, 4),
-        "fwd": {"TFLOP/s": round(F_fwd / t_fwd / 1e12, 2), "ms": round(t_fwd * 1e3, 4)},
-        "bwd": {"TFLOP/s": round((F_dq + F_dkdv) / (t_dq + t_dkdv) / 1e12, 2),
-                "ms_dq": round(t_dq * 1e3, 4), "ms_dkdv": round(t_dkdv * 1e3, 4)},
+        "value_from_min": round((F_fwd + F_bwd) / fb_min / 1e12, 3),
+        "fwd": {"TFLOP/s": round(F_fwd / t_fwd / 1e12, 2), "ms": round(t_fwd * 1e3, 4),
+                **stats_us(per["fwd"])},
+        "bwd": {"TFLOP/s": round(F_bwd / (t_dq + t_dkdv) / 1e12, 2),
+                "ms_dq": round(t_dq * 1e3, 4), "ms_dkdv": round(t_dkdv * 1e3, 4),
+                "dq": stats_us(per["bwd_dq"]), "dkdv": stats_us(per["bwd_dkdv"])},
         "decode": {"GB/s": round(dec_gbs, 1), "frac_of_hbm_peak": round(dec_gbs / PEAK_HBM, 4),
+                   "GB/s_min_max": [round(min(dec_gbs_s), 1), round(max(dec_gbs_s), 1)],
                    "us_per_layer_step": round(t_dec / E.n_layer * 1e6, 2),
                    "append_us_per_layer": round(t_app / E.n_layer * 1e6, 2),
                    "bytes_per_layer_step": round(dec_bytes / E.n_layer),
                    "stream_read_ref_GB/s": stream_ref and round(stream_ref, 1),
                    "frac_of_stream_read_ref": stream_ref and round(dec_gbs / stream_ref, 4),
-                   "step_graph": step_graph, "small_batch": small,
+                   "reading_b": reading_b, "step_graph": step_graph, "small_batch": small,
                    "long_context": longctx},
-        "prefill": {"TFLOP/s": round(pre_flops / t_pre / 1e12, 2), "ms_per_layer": round(t_pre * 1e3, 4)},
+        "prefill": {"TFLOP/s": round(med(pre_tf_s), 2), "ms_per_layer": round(t_pre * 1e3, 4)},
         "d26": d26,
         "small_configs": small_cfg,
         "varlen": varlen,
         "qknorm": qknorm,
         "roofline": roofline,
+        "roofline_decode": roofline_decode,
         "cpu_baseline": cpu,
+        "clocks": clocks,
         "device": props.name,
         "kernel_source_hash": src_hash,
     }

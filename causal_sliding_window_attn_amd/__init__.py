@@ -433,6 +433,10 @@ class KVCache:
     ``lens`` (device int32 [B]) counts the cached tokens; ``decode`` appends the new token at row
     ``lens`` and then attends with ``lens + 1`` keys.  The same ``lens`` serves every layer, so
     advance it with ``step()`` once per generated token after the last layer.
+
+    ``max_len`` is a host-side upper bound of ``lens`` (set by ``prefill`` / ``set_lens``, advanced
+    by ``step``): ``decode`` raises instead of letting a sequence run past the capacity, where the
+    kernels would append nothing and return o = 0.
     """
 
     def __init__(self, n_layer, B, Lcap, H, D, device="cuda", windows=None):
@@ -441,9 +445,18 @@ class KVCache:
         self.k = torch.zeros(shape, device=device, dtype=torch.bfloat16)
         self.v = torch.zeros(shape, device=device, dtype=torch.bfloat16)
         self.lens = torch.zeros(B, device=device, dtype=torch.int32)
+        self.max_len = 0
         self.windows = list(windows) if windows is not None else [None] * n_layer
         self._ws = torch.empty(attn_decode_workspace_bytes(B, H, Lcap, D), device=device,
                                dtype=torch.uint8)
+
+    def set_lens(self, lens, max_len=None):
+        """Set the cached-token counts (int32 [B]); ``max_len`` (host int) is their maximum, read
+        from the device when not given."""
+        self.lens.copy_(lens)
+        self.max_len = int(lens.max()) if max_len is None else int(max_len)
+        if self.max_len > self.Lcap:
+            raise ValueError(f"a length of {self.max_len} exceeds the cache capacity {self.Lcap}")
 
     def prefill(self, layer, q, k, v, lens):
         """Write prompts (padded [B, Tq, H, D]) into the cache and attend causally."""
@@ -452,19 +465,27 @@ class KVCache:
             raise ValueError("prompt longer than the cache")
         self.k[layer, :, :Tq].copy_(k)
         self.v[layer, :, :Tq].copy_(v)
-        self.lens.copy_(lens)
+        self.set_lens(lens)
         o, _ = attn_prefill(q, self.k[layer], self.v[layer], self.lens,
                             window=self.windows[layer])
         return o
 
+    def _check_room(self):
+        if self.max_len >= self.Lcap:
+            raise RuntimeError(f"KV cache full: a sequence holds up to {self.max_len} of "
+                               f"{self.Lcap} rows, so the next token has no row to go to")
+
     def decode(self, layer, q, k_new, v_new, o=None):
         """Append the new token's key / value at row ``lens`` and attend (one call)."""
+        self._check_room()
         o, _ = attn_decode_step(q, k_new, v_new, self.k[layer], self.v[layer], self.lens, o=o,
                                 window=self.windows[layer], ws=self._ws)
         return o
 
     def step(self):
+        self._check_room()
         self.lens.add_(1)
+        self.max_len += 1
 
 
 class DecodeStepGraph:
@@ -475,6 +496,7 @@ class DecodeStepGraph:
     ([n_layer, B, H, D] bf16) and writes ``o`` ([n_layer, B, H, D]); it appends to the cache,
     attends, and finally advances ``cache.lens`` by one.  Fill the inputs, call ``replay()``, read
     ``o``.  Only library kernels and one elementwise add are captured (no memset nodes).
+    ``replay`` raises, as ``KVCache.decode`` does, once the cache has no room for another token.
     """
 
     def __init__(self, cache: KVCache):
@@ -491,15 +513,23 @@ class DecodeStepGraph:
             attn_decode_step(self.q[layer], self.k_new[layer], self.v_new[layer], cache.k[layer],
                              cache.v[layer], idle, o=self.o[layer], window=cache.windows[layer],
                              ws=cache._ws)
-        idle.add_(1)
         torch.cuda.synchronize(dev)
+        # capture records the launches without running them: the host-side length bound must not
+        # advance for it
+        max_len = cache.max_len
+        cache.max_len = 0
         self.graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(self.graph):
-            for layer in range(cache.n_layer):
-                cache.decode(layer, self.q[layer], self.k_new[layer], self.v_new[layer],
-                             o=self.o[layer])
-            cache.step()
+        try:
+            with torch.cuda.graph(self.graph):
+                for layer in range(cache.n_layer):
+                    cache.decode(layer, self.q[layer], self.k_new[layer], self.v_new[layer],
+                                 o=self.o[layer])
+                cache.step()
+        finally:
+            cache.max_len = max_len
 
     def replay(self):
+        self.cache._check_room()
         self.graph.replay()
+        self.cache.max_len += 1
         return self.o

@@ -11,7 +11,10 @@ import os
 
 import torch  # noqa: F401  (must precede the CDLL load, see above)
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswattn.so")
+# SWATTN_LIBRARY names another build of the same library (the CPU ABI tests use it to load the
+# host-side AddressSanitizer build); by default the in-tree libswattn.so is loaded.
+LIB_PATH = os.environ.get("SWATTN_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libswattn.so")
 
 SWATTN_BF16 = 0
 SWATTN_F32 = 1

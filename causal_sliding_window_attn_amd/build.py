@@ -13,6 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libswattn.so")
 SOURCES = ["api.cpp", "fwd.hip", "bwd.hip", "decode.hip", "norm.hip"]
+HEADERS = ["common.h", "launch.h"]
 # measurement helper used by bench.py only (streaming-read reference for the decode roofline)
 PROBE_LIB = os.path.join(PKG, "libswattn_probe.so")
 PROBE_SOURCES = ["stream_probe.hip"]
@@ -73,5 +74,47 @@ def build(extra: list[str] | None = None) -> str:
     return LIB
 
 
+# Host-side AddressSanitizer build of the library, for the CPU tests of the C ABI (argument
+# validation, error text): api.cpp's host code is instrumented (-Xarch_host puts the sanitizer on
+# the host compilation only; device code is built as usual), and the result is a separate file.
+ASAN_LIB = os.path.join(PKG, "libswattn_asan.so")
+
+
+def asan_runtime() -> str:
+    """Path of the clang ASan runtime that a process loading ASAN_LIB must preload."""
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the clang AddressSanitizer runtime was not found")
+    return path
+
+
+def build_asan() -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    asan = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+    def one(src):
+        if src != "api.cpp":
+            return _compile(src, [])
+        obj = _compile(src, asan)
+        tagged = obj[:-2] + "_asan.o"
+        os.replace(obj, tagged)
+        return tagged
+
+    with ThreadPoolExecutor(len(SOURCES)) as ex:
+        objs = list(ex.map(one, SOURCES))
+    tmp = ASAN_LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host",
+           "-fsanitize=address", "-shared-libasan", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, ASAN_LIB)
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(sys.argv[1:]))
+    if sys.argv[1:2] == ["--asan"]:
+        print(build_asan())
+    else:
+        print(build(sys.argv[1:]))

@@ -1,9 +1,11 @@
 """GPU parity: the HIP path through the C ABI against the fp64 CPU oracle on the same seeded inputs.
 
 Bars (bf16 in, fp32 accumulate): O max-abs <= 1e-2 over valid elements; dQ, dK, dV relative
-Frobenius error <= 2e-2 each; LSE max-abs <= 1e-3 (reported bar).  Full-size workloads compare
-every element of sampled (batch, head) pairs; the oracle computes those heads exactly.
+Frobenius error <= 2e-2 each, over the whole tensor; LSE max-abs <= 1e-3 (reported bar).  The
+full-size workloads (the d20 layer, the four d26 layers, the packed-document d20 rows, the QK-norm
+d20 layer) compare every head against the oracle run on the whole tensor.
 """
+import math
 import os
 
 import numpy as np
@@ -58,8 +60,24 @@ def check_fwd(o, lse, o_r, lse_r, heads=None, tag=""):
         assert el <= LSE_TOL, f"{tag} LSE max-abs {el}"
 
 
-def check_grads(gs, rs, heads=None, tag=""):
-    for name, g, r in zip(("dQ", "dK", "dV"), gs, rs):
+def zero_grad_bounds(Q, K, V, DO):
+    """Rounding residue allowed where the exact dQ and dK vanish (window 1: P = I, O = V, so
+    dS_ii = P_ii (dO_i . v_i - dO_i . O_i) = 0 exactly).  The kernels form the two dot products
+    in fp32 in different orders; each is a sum of D rounded terms, whose rounding errors behave as
+    a random walk of about sqrt(D) unit roundoffs u = 2^-24 times the sum of |terms|.  The bound
+    allows 8 such steps on each side, then the gradient's factors: dQ_i = dS_ii k_i / sqrt(D),
+    dK_i = dS_ii q_i / sqrt(D)."""
+    D = Q.shape[-1]
+    u = 2.0 ** -24
+    dot_abs = np.abs(DO * V).sum(-1)  # [B, T, H]
+    ds = 2 * 8 * math.sqrt(D) * u * dot_abs
+    b_dq = float((ds * np.abs(K).max(-1)).max()) / math.sqrt(D)
+    b_dk = float((ds * np.abs(Q).max(-1)).max()) / math.sqrt(D)
+    return b_dq, b_dk
+
+
+def check_grads(gs, rs, heads=None, tag="", zero_bounds=None):
+    for i, (name, g, r) in enumerate(zip(("dQ", "dK", "dV"), gs, rs)):
         g = f64(g)
         if heads is not None:
             g = np.stack([g[b, :, h] for b, h in heads])
@@ -67,8 +85,9 @@ def check_grads(gs, rs, heads=None, tag=""):
         if not np.any(r):
             # closed-form zero gradient (window 1 gives dQ = dK = 0 exactly): relative error is
             # undefined, so bound the rounding residue absolutely instead
+            assert zero_bounds is not None, f"{tag} {name}: exact zero needs a residue bound"
             e = float(np.abs(g).max())
-            assert e <= 1e-3, f"{tag} {name} should be 0, max-abs {e}"
+            assert e <= zero_bounds[i], f"{tag} {name} should be 0, max-abs {e} > {zero_bounds[i]}"
             continue
         e = rel_fro(g, r)
         assert e <= G_TOL, f"{tag} {name} rel-Frobenius {e}"
@@ -109,37 +128,32 @@ def test_small_bf16_window128(sw):
     check_grads(g, ref.backward(Q, K, V, DO, c.window), tag=c.name)
 
 
-D20_HEADS = [(0, 0), (7, 3), (19, 9), (31, 5)]
-
-
 @pytest.mark.slow
-def test_d20_layer_sampled_heads(sw):
+def test_d20_layer_every_head(sw):
+    """The d20 layer in the bench's launch configuration, every head against the oracle: O and
+    LSE max-abs over all elements, dQ / dK / dV relative Frobenius over the whole tensors."""
     c = W.D20_LAYER
     q, k, v, do = W.attn_inputs(c)
     o, lse, g = run_fwd_bwd(sw, q, k, v, do, c.window)
     Q, K, V, DO = (f64(t) for t in (q, k, v, do))
-    o_r, lse_r = ref.forward(Q, K, V, c.window, heads=D20_HEADS)
-    check_fwd(o, lse, o_r, lse_r, heads=D20_HEADS, tag=c.name)
-    check_grads(g, ref.backward(Q, K, V, DO, c.window, heads=D20_HEADS), heads=D20_HEADS,
-                tag=c.name)
-    # properties that hold for every head at any size
-    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
-    for t in g:
-        assert torch.isfinite(t).all()
+    o_r, lse_r = ref.forward(Q, K, V, c.window)
+    check_fwd(o, lse, o_r, lse_r, tag=c.name)
+    del o_r, lse_r
+    check_grads(g, ref.backward(Q, K, V, DO, c.window), tag=c.name)
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("layer", [0, 1, 2, 3])
 def test_d26_alternating_layer(sw, layer):
+    """Each layer of the d26 stack (windows 512, full, 512, full), every head."""
     window = W.D26_WINDOWS[layer]
     q, k, v, do = W.d26_layer_inputs(layer)
     o, lse, g = run_fwd_bwd(sw, q, k, v, do, window)
-    heads = [(0, 0), (5, 12), (15, 6)]
     Q, K, V, DO = (f64(t) for t in (q, k, v, do))
-    o_r, lse_r = ref.forward(Q, K, V, window, heads=heads)
-    check_fwd(o, lse, o_r, lse_r, heads=heads, tag=f"d26 layer {layer}")
-    check_grads(g, ref.backward(Q, K, V, DO, window, heads=heads), heads=heads,
-                tag=f"d26 layer {layer}")
+    o_r, lse_r = ref.forward(Q, K, V, window)
+    check_fwd(o, lse, o_r, lse_r, tag=f"d26 layer {layer}")
+    del o_r, lse_r
+    check_grads(g, ref.backward(Q, K, V, DO, window), tag=f"d26 layer {layer}")
 
 
 @pytest.mark.slow
@@ -221,7 +235,8 @@ def test_edge_sweep_bf16(sw, T, D):
         torch.cuda.synchronize()
         o_r, lse_r = ref.forward(Q, K, V, w, threads=1)
         check_fwd(o, lse, o_r, lse_r, tag=f"T={T} D={D} w={w}")
-        check_grads(g, ref.backward(Q, K, V, DO, w, threads=1), tag=f"T={T} D={D} w={w}")
+        check_grads(g, ref.backward(Q, K, V, DO, w, threads=1), tag=f"T={T} D={D} w={w}",
+                    zero_bounds=zero_grad_bounds(Q, K, V, DO) + (0.0,))
 
 
 @pytest.mark.parametrize("T,w,D", [(1, 1, 64), (65, 7, 64), (129, 129, 128), (300, 64, 128),
@@ -566,7 +581,8 @@ def test_varlen_matches_oracle(sw, D):
         assert np.abs(f64(o) - o_r).max() <= O_TOL, f"window {window}"
         assert np.abs(f64(lse) - lse_r).max() <= LSE_TOL, f"window {window}"
         g_r = ref.backward_varlen(f64(q), f64(k), f64(v), f64(do), cu.numpy(), window)
-        check_grads(g, g_r, tag=f"varlen D{D} window {window}")
+        check_grads(g, g_r, tag=f"varlen D{D} window {window}",
+                    zero_bounds=zero_grad_bounds(f64(q), f64(k), f64(v), f64(do)) + (0.0,))
 
 
 def test_varlen_is_each_document_alone_bit_for_bit(sw):
@@ -671,12 +687,12 @@ def test_qknorm_autograd_wrapper(sw):
     check_grads((qd.grad, kd.grad, vd.grad), g_r, tag="qknorm autograd")
 
 
-# ------------------------------------------------- full-size NEXT workloads, sampled outputs
+# ------------------------------------------------- full-size NEXT workloads, every head
 @pytest.mark.slow
-def test_d20_packed_documents_sampled(sw):
+def test_d20_packed_documents_every_head(sw):
     """The bench's packed-document d20 rows (same q, k, v, dO as the d20 layer), forward and
-    backward in the bench's launch configuration; the shortest, a median and the longest document
-    checked on two heads against the oracle run on each document alone."""
+    backward in the bench's launch configuration, every document and head against the oracle:
+    O and LSE max-abs over all rows, dQ / dK / dV relative Frobenius over the whole tensors."""
     c = W.D20_LAYER
     q, k, v, do = W.attn_inputs(c)
     B, T, H, D = q.shape
@@ -688,35 +704,27 @@ def test_d20_packed_documents_sampled(sw):
     o, lse = sw.attn_fwd_varlen(qd, kd, vd, cu.to(DEV), ms, window=c.window)
     g = sw.attn_bwd_varlen(qd, kd, vd, o, lse, dod, cu.to(DEV), ms, window=c.window)
     torch.cuda.synchronize()
-    order = sorted(range(len(lens)), key=lambda i: lens[i])
-    heads = [0, H - 1]
-    for s in (order[0], order[len(order) // 2], order[-1]):
-        a, e = int(cu[s]), int(cu[s + 1])
-        one = [f64(t[a:e]).reshape(1, e - a, H, D) for t in (qp, kp, vp, dop)]
-        hh = [(0, h) for h in heads]
-        o_r, lse_r = ref.forward(one[0], one[1], one[2], c.window, heads=hh)
-        g_r = ref.backward(*one, c.window, heads=hh)
-        for h in heads:
-            assert np.abs(f64(o[a:e, h]) - o_r[0, :, h]).max() <= O_TOL, (s, h)
-            assert np.abs(f64(lse[h, a:e]) - lse_r[0, h]).max() <= LSE_TOL, (s, h)
-            for gg, rr in zip(g, g_r):
-                assert rel_fro(f64(gg[a:e, h]), rr[0, :, h]) <= G_TOL, (s, h, e - a)
-    for t in (o, lse) + tuple(g):
-        assert torch.isfinite(t).all()
+    Q, K, V, DO = (f64(t) for t in (qp, kp, vp, dop))
+    o_r, lse_r = ref.forward_varlen(Q, K, V, cu.numpy(), c.window)
+    e = float(np.abs(f64(o) - o_r).max())
+    assert e <= O_TOL, f"packed d20 O max-abs {e}"
+    el = float(np.abs(f64(lse) - lse_r).max())
+    assert el <= LSE_TOL, f"packed d20 LSE max-abs {el}"
+    del o_r, lse_r
+    check_grads(g, ref.backward_varlen(Q, K, V, DO, cu.numpy(), c.window), tag="packed d20")
 
 
 @pytest.mark.slow
-def test_d20_qknorm_sampled_heads(sw):
-    """QK-norm on the d20 layer in the bench's configuration, sampled heads against the oracle."""
+def test_d20_qknorm_every_head(sw):
+    """QK-norm on the d20 layer in the bench's configuration, every head against the oracle."""
     c = W.D20_LAYER
     q, k, v, do = W.attn_inputs(c)
     qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
     o, lse, qn, kn, rq, rk = sw.attn_fwd_qknorm(qd, kd, vd, window=c.window)
     g = sw.attn_bwd_qknorm(qn, kn, vd, o, lse, dod, rq, rk, window=c.window)
     torch.cuda.synchronize()
-    heads = [(0, 0), (31, 9)]
     Q, K, V, DO = (f64(t) for t in (q, k, v, do))
-    o_r, lse_r, _, _ = ref.forward_qknorm(Q, K, V, c.window, heads=heads)
-    check_fwd(o, lse, o_r, lse_r, heads=heads, tag="d20 qknorm")
-    check_grads(g, ref.backward_qknorm(Q, K, V, DO, c.window, heads=heads), heads=heads,
-                tag="d20 qknorm")
+    o_r, lse_r, _, _ = ref.forward_qknorm(Q, K, V, c.window)
+    check_fwd(o, lse, o_r, lse_r, tag="d20 qknorm")
+    del o_r, lse_r
+    check_grads(g, ref.backward_qknorm(Q, K, V, DO, c.window), tag="d20 qknorm")

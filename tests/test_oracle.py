@@ -502,3 +502,40 @@ def test_qknorm_gradient_is_orthogonal_to_the_row():
     dq, dk, _ = A.backward_qknorm(q, k, v, g, None, 0.0, round_bf16=False)
     assert np.abs((dq * q).sum(-1)).max() < 1e-12
     assert np.abs((dk * k).sum(-1)).max() < 1e-12
+
+
+@pytest.mark.parametrize("w", [3, 100])
+def test_qknorm_rounded_rows_match_straight_through_autograd(w):
+    """round_bf16=True (the setting the GPU tests use): fp64 autograd through torch's rms_norm, a
+    bf16 cast of the normalised rows with a straight-through gradient (the cast's value, identity
+    derivative), and the masked softmax attention.  Inputs are far from unit RMS so the norm and the
+    rounding both matter."""
+    rng = np.random.default_rng(95 + w)
+    B, T, H, D, eps = 1, 21, 2, 16, 1e-6
+    q, k, v, g = (rng.standard_normal((B, T, H, D)) * s for s in (3.0, 0.5, 1.0, 1.0))
+    o, lse, qn, kn = A.forward_qknorm(q, k, v, w, eps, round_bf16=True)
+    dq, dk, dv = A.backward_qknorm(q, k, v, g, w, eps, round_bf16=True)
+    m = torch.tensor(brute.mask(T, w))
+
+    def st_bf16(x):  # value of the bf16 cast, gradient of the identity
+        return x + (x.to(torch.bfloat16).to(torch.float64) - x).detach()
+
+    for h in range(H):
+        tq, tk, tv = (torch.tensor(x[0, :, h], requires_grad=True) for x in (q, k, v))
+        nq = st_bf16(torch.nn.functional.rms_norm(tq, (D,), eps=eps))
+        nk = st_bf16(torch.nn.functional.rms_norm(tk, (D,), eps=eps))
+        # the rows the attention saw are exactly bf16 values
+        np.testing.assert_array_equal(qn[0, :, h], nq.detach().numpy())
+        np.testing.assert_array_equal(kn[0, :, h], nk.detach().numpy())
+        s = ((nq @ nk.T) / math.sqrt(D)).masked_fill(~m, float("-inf"))
+        to = torch.softmax(s, dim=1) @ tv
+        np.testing.assert_allclose(o[0, :, h], to.detach().numpy(), atol=1e-12)
+        np.testing.assert_allclose(lse[0, h], torch.logsumexp(s, dim=1).detach().numpy(),
+                                   atol=1e-12)
+        to.backward(torch.tensor(g[0, :, h]))
+        np.testing.assert_allclose(dq[0, :, h], tq.grad.numpy(), atol=1e-10)
+        np.testing.assert_allclose(dk[0, :, h], tk.grad.numpy(), atol=1e-10)
+        np.testing.assert_allclose(dv[0, :, h], tv.grad.numpy(), atol=1e-10)
+    # rounding changes the result: the unrounded oracle differs by far more than the tolerance above
+    o_u, _, _, _ = A.forward_qknorm(q, k, v, w, eps, round_bf16=False)
+    assert np.abs(o_u - o).max() > 1e-6
