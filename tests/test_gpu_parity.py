@@ -1,6 +1,8 @@
 """GPU parity: the HIP path through the C ABI against the fp64 CPU oracle on the same seeded inputs.
 
-Bars (bf16 in, fp32 accumulate): O max-abs <= 1e-2 over valid elements; dQ, dK, dV relative
+Bars (bf16 in, fp32 accumulate): O max-abs <= 1e-2 over valid elements, except where storing the
+exact value in the output format alone can miss it by more (a bf16 output with |O| >= 4, whose
+half ulp is 2^-6 > 1e-2): there one bf16 ulp of the exact value (see o_bar); dQ, dK, dV relative
 Frobenius error <= 2e-2 each, over the whole tensor; LSE max-abs <= 1e-3 (reported bar).  The
 full-size workloads (the d20 layer, the four d26 layers, the packed-document d20 rows, the QK-norm
 d20 layer) compare every head against the oracle run on the whole tensor.
@@ -39,22 +41,48 @@ def f64(t):
     return t.detach().double().cpu().numpy()
 
 
+def o_bar(o_r, fp32=False):
+    """Per-element bar on O: 1e-2, or for bf16 outputs with |O| >= 4 one bf16 ulp of the exact
+    value.  A bf16 value near |O| in [4, 8) is only representable to 2^-5, so the nearest one can
+    sit 2^-6 > 1e-2 from the exact result: there the bar is the format's own resolution."""
+    if fp32:
+        return np.full(np.shape(o_r), O_TOL)
+    a = np.abs(o_r)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(a, 1e-300))) - 7)
+    return np.where(a < 4.0, O_TOL, ulp)
+
+
+def o_excess(o, o_r, fp32=False):
+    """max |o - o_r| / bar over valid (finite-reference) elements; the check is <= 1."""
+    o, o_r = np.asarray(o, np.float64), np.asarray(o_r, np.float64)
+    m = np.isfinite(o_r)
+    if not m.any():
+        return 0.0
+    return float((np.abs(o[m] - o_r[m]) / o_bar(o_r[m], fp32)).max())
+
+
+def assert_o(o, o_r, tag="", fp32=False):
+    x = o_excess(o, o_r, fp32)
+    e = float(np.abs(np.asarray(o, np.float64) - np.asarray(o_r, np.float64))[np.isfinite(o_r)].max()) \
+        if np.isfinite(o_r).any() else 0.0
+    assert x <= 1.0, f"{tag} O error {x:.3f} x its bar (max-abs {e:.4g})"
+
+
 def rel_fro(a, b):
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
 
 
 def check_fwd(o, lse, o_r, lse_r, heads=None, tag=""):
+    fp32 = o.dtype == torch.float32
     o, lse = f64(o), f64(lse) if lse is not None else None
     if heads is not None:
         for b, h in heads:
-            e = np.abs(o[b, :, h] - o_r[b, :, h]).max()
-            assert e <= O_TOL, f"{tag} O max-abs {e} at head {(b, h)}"
+            assert_o(o[b, :, h], o_r[b, :, h], f"{tag} head {(b, h)}", fp32)
             if lse is not None:
                 el = np.abs(lse[b, h] - lse_r[b, h]).max()
                 assert el <= LSE_TOL, f"{tag} LSE max-abs {el} at head {(b, h)}"
         return
-    e = np.abs(o - o_r).max()
-    assert e <= O_TOL, f"{tag} O max-abs {e}"
+    assert_o(o, o_r, tag, fp32)
     if lse is not None:
         el = np.abs(lse - lse_r).max()
         assert el <= LSE_TOL, f"{tag} LSE max-abs {el}"
@@ -176,8 +204,7 @@ def test_d30_engine_prefill_and_decode(sw, layer):
     of, lf = f64(o), f64(lse)
     for b in range(E.B):
         L = int(lens[b])
-        e = np.abs(of[b, :L] - o_r[b, :L]).max()
-        assert e <= O_TOL, f"prefill b={b} max-abs {e}"
+        assert_o(of[b, :L], o_r[b, :L], f"prefill b={b}")
         assert np.abs(lf[b, :, :L] - lse_r[b, :, :L]).max() <= LSE_TOL
         assert np.all(of[b, L:] == 7.0), "rows past the prompt must stay untouched"
     # decode steps: append, then attend with lens + 1
@@ -205,9 +232,9 @@ def test_d30_engine_prefill_and_decode(sw, layer):
             kc_bf[b, int(cur[b])] = kn[b]
             vc_bf[b, int(cur[b])] = vn[b]
         od_r, lse_dr = ref.decode(f64(qn), kc_ref, vc_ref, (cur + 1).numpy(), window)
-        e = float(np.abs(f64(od) - od_r).max())
+        e = o_excess(f64(od), od_r)
         worst = max(worst, e)
-        assert e <= O_TOL, f"decode step {s} max-abs {e}"
+        assert e <= 1.0, f"decode step {s}: O error {e:.3f} x its bar"
         assert np.abs(f64(lsed) - lse_dr).max() <= LSE_TOL
         cur += 1
     # the device cache holds exactly what the reference appended
@@ -286,7 +313,7 @@ def test_decode_edge_lengths(sw, D, case):
         o, lse = sw.attn_decode(q.to(DEV), kcd, vcd, lens.to(DEV), window=window, want_lse=True)
         torch.cuda.synchronize()
         o_r, lse_r = ref.decode(f64(q), f64(kc), f64(vc), lens.numpy(), window)
-        assert np.abs(f64(o) - o_r).max() <= O_TOL, f"window {window}"
+        assert_o(f64(o), o_r, f"window {window}")
         lf = f64(lse)
         zero = (lens == 0).numpy()
         assert np.all(f64(o)[zero] == 0) and np.all(np.isneginf(lf[zero]))
@@ -311,7 +338,7 @@ def test_prefill_ragged_and_window_noop(sw):
         for b in range(B):
             L = int(lens[b])
             if L:
-                assert np.abs(of[b, :L] - o_r[b, :L]).max() <= O_TOL, (window, b)
+                assert_o(of[b, :L], o_r[b, :L], f"window {window} b {b}")
                 assert np.abs(f64(lse)[b, :, :L] - lse_r[b, :, :L]).max() <= LSE_TOL
             assert np.all(of[b, L:] == -3.0)
     # every prompt is <= 130 keys: window 130 equals full causal bit for bit
@@ -372,7 +399,7 @@ def test_decode_long_cache_split_merge(sw):
         o, lse = sw.attn_decode(q.to(DEV), kcd, vcd, lens.to(DEV), window=window, want_lse=True)
         torch.cuda.synchronize()
         o_r, lse_r = ref.decode(f64(q), f64(kc), f64(vc), lens.numpy(), window)
-        assert np.abs(f64(o) - o_r).max() <= O_TOL, f"window {window}"
+        assert_o(f64(o), o_r, f"window {window}")
         assert np.abs(f64(lse) - lse_r).max() <= LSE_TOL, f"window {window}"
 
 
@@ -444,8 +471,8 @@ def test_decode_matches_prefill_last_row(sw):
         od, _ = sw.attn_decode(qlast.contiguous(), kcd, vcd, ld, window=window)
         torch.cuda.synchronize()
         for b in range(B):
-            a = o[b, int(lens[b]) - 1].float()
-            assert (a - od[b].float()).abs().max().item() <= 1e-2
+            a = f64(o[b, int(lens[b]) - 1])
+            assert_o(f64(od[b]), a, f"decode vs prefill row, b {b}")
 
 
 def test_autograd_wrapper_and_kvcache(sw):
@@ -468,7 +495,7 @@ def test_autograd_wrapper_and_kvcache(sw):
     torch.cuda.synchronize()
     kc, vc = f64(cache.k[1]), f64(cache.v[1])
     od_r, _ = ref.decode(f64(qn), kc, vc, np.array([4, 11]), 8)
-    assert np.abs(f64(od) - od_r).max() <= O_TOL
+    assert_o(f64(od), od_r, "kvcache decode")
 
 
 # ------------------------------------------------------------------ decode step (append + decode)
@@ -509,7 +536,7 @@ def test_decode_step_equals_append_then_decode(sw, D, case):
         assert torch.equal(o1[valid], o2[valid]) and torch.equal(lse1[valid], lse2[valid]), window
         assert torch.all(o1[~valid] == 0) and torch.all(torch.isneginf(lse1[~valid]))
         o_r, lse_r = ref.decode(f64(q), kc_r, vc_r, np.where(valid, pos.numpy() + 1, 0), window)
-        assert np.abs(f64(o1) - o_r).max() <= O_TOL, f"window {window}"
+        assert_o(f64(o1), o_r, f"window {window}")
         assert np.abs(f64(lse1)[valid] - lse_r[valid]).max() <= LSE_TOL
 
 
@@ -553,7 +580,7 @@ def test_decode_step_graph_replays_match_eager(sw, B, H, Lcap, windows):
         lens_now = f64(eager.lens).astype(np.int64)
         o_r, _ = ref.decode(f64(ins[0][-1]), f64(eager.k[-1]), f64(eager.v[-1]), lens_now,
                             windows[-1])
-        assert np.abs(f64(o_e[-1]) - o_r).max() <= O_TOL, f"replay {s}"
+        assert_o(f64(o_e[-1]), o_r, f"replay {s}")
 
 
 # ------------------------------------------------------------- packed documents (varlen)
@@ -578,7 +605,7 @@ def test_varlen_matches_oracle(sw, D):
         g = sw.attn_bwd_varlen(qd, kd, vd, o, lse, dod, cud, max(lengths), window=window)
         torch.cuda.synchronize()
         o_r, lse_r = ref.forward_varlen(f64(q), f64(k), f64(v), cu.numpy(), window)
-        assert np.abs(f64(o) - o_r).max() <= O_TOL, f"window {window}"
+        assert_o(f64(o), o_r, f"window {window}")
         assert np.abs(f64(lse) - lse_r).max() <= LSE_TOL, f"window {window}"
         g_r = ref.backward_varlen(f64(q), f64(k), f64(v), f64(do), cu.numpy(), window)
         check_grads(g, g_r, tag=f"varlen D{D} window {window}",
@@ -626,8 +653,8 @@ def test_varlen_autograd_and_rows_past_max_seqlen(sw):
     o_r, _ = ref.forward_varlen(f64(q), f64(k), f64(v), cu.numpy(), 25)
     a = int(cu[1])
     assert torch.all(o2[a + 64:a + 90] == 7.0)
-    assert np.abs(f64(o2[a:a + 64]) - o_r[a:a + 64]).max() <= O_TOL
-    assert np.abs(f64(o2[:a]) - o_r[:a]).max() <= O_TOL
+    assert_o(f64(o2[a:a + 64]), o_r[a:a + 64], "rows before max_seqlen")
+    assert_o(f64(o2[:a]), o_r[:a], "first document")
 
 
 # ------------------------------------------------------------------------------ QK-norm
@@ -651,7 +678,7 @@ def test_qknorm_matches_oracle(sw, D):
             assert np.abs(f64(a) - b).max() <= 2 ** -7 * np.abs(b).max()
         _, r_q = ref.rmsnorm(f64(q), eps)
         assert np.abs(f64(rq) - r_q.transpose(0, 2, 1)).max() <= 1e-5 * np.abs(r_q).max()
-        assert np.abs(f64(o) - o_r).max() <= O_TOL, f"window {window}"
+        assert_o(f64(o), o_r, f"window {window}")
         assert np.abs(f64(lse) - lse_r).max() <= LSE_TOL, f"window {window}"
         g_r = ref.backward_qknorm(f64(q), f64(k), f64(v), f64(do), window, eps)
         check_grads(g3, g_r, tag=f"qknorm D{D} window {window}")
@@ -706,8 +733,7 @@ def test_d20_packed_documents_every_head(sw):
     torch.cuda.synchronize()
     Q, K, V, DO = (f64(t) for t in (qp, kp, vp, dop))
     o_r, lse_r = ref.forward_varlen(Q, K, V, cu.numpy(), c.window)
-    e = float(np.abs(f64(o) - o_r).max())
-    assert e <= O_TOL, f"packed d20 O max-abs {e}"
+    assert_o(f64(o), o_r, "packed d20")
     el = float(np.abs(f64(lse) - lse_r).max())
     assert el <= LSE_TOL, f"packed d20 LSE max-abs {el}"
     del o_r, lse_r
