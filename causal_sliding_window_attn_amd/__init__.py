@@ -20,6 +20,7 @@ __all__ = [
     "attn_abi_version", "attn_last_error", "attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv",
     "attn_bwd_workspace_bytes",
     "attn_prefill", "attn_kv_append", "attn_decode", "attn_decode_step",
+    "attn_decode_step_noalloc",
     "attn_decode_workspace_bytes", "attn_decode_launches", "attn_fwd_varlen", "attn_bwd_varlen", "attn_fwd_qknorm",
     "attn_bwd_qknorm", "attention", "attention_varlen", "attention_qknorm", "KVCache",
     "DecodeStepGraph", "FULL", "QKNORM_EPS",
@@ -260,6 +261,30 @@ def attn_decode_step(q, knew, vnew, kcache, vcache, pos, o=None, lse=None, windo
                                  Lcap, D, _win(window, Lcap), ws.data_ptr(),
                                  ws.numel() * ws.element_size(), _stream(q))
     check(rc, "attn_decode_step")
+    return o, lse
+
+
+def attn_decode_step_noalloc(q, knew, vnew, kcache, vcache, pos, o, lse=None, window=None):
+    """attn_decode_step with no workspace: the library keeps the split schedule's partial results
+    in a static device array (32 MiB per GPU), so the call allocates nothing.  The output ``o``
+    ([B, H, D] bf16) and the optional ``lse`` ([B, H] float32) must be given.  Calls on one GPU
+    share that array and must not run concurrently."""
+    B, H, D = q.shape
+    Lcap = kcache.shape[1]
+    _need(q, "q", None, torch.bfloat16)
+    _need(knew, "knew", (B, H, D), torch.bfloat16)
+    _need(vnew, "vnew", (B, H, D), torch.bfloat16)
+    _need(kcache, "kcache", (B, Lcap, H, D), torch.bfloat16)
+    _need(vcache, "vcache", (B, Lcap, H, D), torch.bfloat16)
+    _need(pos, "pos", (B,), torch.int32)
+    _need(o, "o", (B, H, D), torch.bfloat16)
+    if lse is not None:
+        _need(lse, "lse", (B, H), torch.float32)
+    rc = load().attn_decode_step_noalloc(q.data_ptr(), knew.data_ptr(), vnew.data_ptr(),
+                                         kcache.data_ptr(), vcache.data_ptr(), pos.data_ptr(),
+                                         o.data_ptr(), _ptr(lse), B, H, Lcap, D,
+                                         _win(window, Lcap), _stream(q))
+    check(rc, "attn_decode_step_noalloc")
     return o, lse
 
 

@@ -371,6 +371,61 @@ int attn_decode_step(const void* q, const void* knew, const void* vnew, void* kc
                     "attn_decode_step launch");
 }
 
+int attn_decode_step_noalloc(const void* q, const void* knew, const void* vnew, void* kcache,
+                             void* vcache, const int* pos, void* o, float* lse, int B, int H,
+                             int Lcap, int D, int window, void* stream) {
+  const char* what = "attn_decode_step_noalloc";
+  TRY(check_dims(what, B, H, Lcap, "Lcap", D, window));
+  TRY(check_decode_cap(what, Lcap));
+  TRY(check_ptr(q, "q"));
+  TRY(check_ptr(knew, "knew"));
+  TRY(check_ptr(vnew, "vnew"));
+  TRY(check_ptr(kcache, "kcache"));
+  TRY(check_ptr(vcache, "vcache"));
+  if (!pos) return fail(SWATTN_EINVAL, "pos is NULL");
+  if (reinterpret_cast<uintptr_t>(pos) & 3u) return fail(SWATTN_EINVAL, "pos is not 4-byte aligned");
+  TRY(check_ptr(o, "o"));
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(SWATTN_EINVAL, "lse is not 4-byte aligned");
+  // only the split schedule keeps partial results; the one-launch schedule needs no scratch
+  const bool split = !swattn::decode_uses_fused(B, H, Lcap, window);
+  const int nc_max = decode_chunks(Lcap);
+  const size_t slots = (size_t)B * H * nc_max;
+  const size_t need = split ? attn_decode_workspace_bytes(B, H, Lcap, D) : 0;
+  if (need > swattn::kNoAllocScratchBytes)
+    return fail(SWATTN_EWORKSPACE,
+                "%s: these sizes take the split schedule, whose partial results need %zu bytes, "
+                "more than the %zu-byte static scratch (use attn_decode_step with a workspace)",
+                what, need, swattn::kNoAllocScratchBytes);
+  void* ws = nullptr;
+  (void)hipGetLastError();
+  if (split) TRY(hip_status(swattn::decode_noalloc_scratch(&ws), "attn_decode_step_noalloc scratch"));
+  swattn::DecArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kc = static_cast<const uint16_t*>(kcache);
+  a.vc = static_cast<const uint16_t*>(vcache);
+  a.pos = pos;
+  a.kn = static_cast<const uint16_t*>(knew);
+  a.vn = static_cast<const uint16_t*>(vnew);
+  a.kcw = static_cast<uint16_t*>(kcache);
+  a.vcw = static_cast<uint16_t*>(vcache);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.ws_o = static_cast<float*>(ws);
+  a.ws_ml = split ? reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                             align256(slots * D * sizeof(float)))
+                  : nullptr;
+  a.B = B;
+  a.H = H;
+  a.D = D;
+  a.Lcap = Lcap;
+  a.window = window;
+  a.nc_max = nc_max;
+  a.scale_log2 = scale_log2_for(D);
+  return hip_status(swattn::launch_decode(a, static_cast<hipStream_t>(stream)),
+                    "attn_decode_step_noalloc launch");
+}
+
 // Packed sequences (documents): shared argument checks of attn_fwd_varlen / attn_bwd_varlen.
 static int check_varlen(const char* what, const int* cu, int nseq, int total, int max_seqlen,
                         int H, int D, int window) {

@@ -20,10 +20,40 @@
 // attend over rows .. pos[b].  The chunk ending at the new row takes that row's key / value from
 // the new-row inputs instead of the cache, and one wave copies the row into the cache after its
 // own loads, so no launch reads a cache row written in the same launch.
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
 namespace swattn {
+
+// Scratch of the allocation-free decode step.  In host code `scratch` names a host-side stand-in,
+// not device memory: only the address that hipGetSymbolAddress returns for the current device is
+// ever passed to a kernel.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {

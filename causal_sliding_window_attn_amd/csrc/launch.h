@@ -108,6 +108,14 @@ inline bool decode_uses_fused(int B, int H, int Lcap, int window) {
   return (long long)B * H >= kDecodeFusedMinPairs || visible <= kDecodeFusedMaxRows;
 }
 
+// Static scratch of the allocation-free decode step (attn_decode_step_noalloc): the split
+// schedule's partial results, in a file-scope device array of decode.hip (one copy per GPU, held
+// until the process ends).
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+// Device address of this GPU's copy of the scratch array (the current device's), looked up with
+// hipGetSymbolAddress on the first call on each device and kept.
+hipError_t decode_noalloc_scratch(void** ptr);
+
 hipError_t launch_fwd(const FwdArgs& a, bool f32, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t s);

@@ -25,8 +25,9 @@
  *              KV cache [B, Lcap, H, D]; LSE [B, H, T] float32 (natural log).
  *   Types:     bf16 storage with fp32 accumulation; the forward also accepts fp32 (SWATTN_F32).
  *   Pointers:  device memory owned by the caller; the library allocates nothing and keeps no state
- *              besides the thread-local error text.  Tensor and workspace pointers must be 16-byte
- *              aligned; int32 length / position arrays and the decode's lse need 4 bytes.
+ *              besides the thread-local error text and the static scratch array of
+ *              attn_decode_step_noalloc.  Tensor and workspace pointers must be 16-byte aligned;
+ *              int32 length / position arrays and the decode's lse need 4 bytes.
  *   Streams:   `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue and return; the
  *              caller keeps every buffer alive until the stream has passed the kernels.
  *   Errors:    every check below runs on the host before any HIP call.  A failing call returns a
@@ -35,7 +36,8 @@
  *              caller's next synchronisation.  No entry point throws.
  *   Window:    window >= 1; any window >= the sequence length means full causal attention.
  *   Head dim:  D in {64, 128}.
- *   Threads:   entry points are re-entrant; concurrent calls may share nothing they write.
+ *   Threads:   entry points are re-entrant; concurrent calls may share nothing they write (calls
+ *              of attn_decode_step_noalloc on one GPU share its scratch, see there).
  */
 #ifndef SWATTN_H
 #define SWATTN_H
@@ -46,8 +48,8 @@
 extern "C" {
 #endif
 
-#define SWATTN_ABI_VERSION 5  /* 2: attn_decode_step; 3: *_varlen; 4: *_qknorm;
-                                 5: attn_decode_launches */
+#define SWATTN_ABI_VERSION 6  /* 2: attn_decode_step; 3: *_varlen; 4: *_qknorm;
+                                 5: attn_decode_launches; 6: attn_decode_step_noalloc */
 
 typedef enum { SWATTN_BF16 = 0, SWATTN_F32 = 1 } swattn_dtype;
 
@@ -174,6 +176,23 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
 int attn_decode_step(const void* q, const void* knew, const void* vnew, void* kcache, void* vcache,
                      const int* pos, void* o, float* lse, int B, int H, int Lcap, int D,
                      int window, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * attn_decode_step without a workspace argument, for callers that cannot allocate device memory:
+ * code being captured into a HIP graph, tight serving loops, harnesses that forbid hipMalloc.
+ * Same operation, arguments (minus ws / ws_bytes), kernels and results as attn_decode_step; it
+ * calls no hipMalloc / hipFree and allocates nothing.  The split schedule's partial results go
+ * to a static device array of 32 MiB inside the library (one per GPU, kept until the process
+ * ends; its address is looked up once per device, on the first call made with that device
+ * current).  Sizes whose split schedule would need more than 32 MiB (attn_decode_workspace_bytes
+ * above 32 MiB when attn_decode_launches returns 2) return SWATTN_EWORKSPACE; the one-launch
+ * schedule needs no scratch at any size.  All calls on one GPU share that array: calls that may
+ * run at the same time on one GPU (different streams, different host threads) race on it and
+ * must be ordered by the caller.  Errors otherwise as attn_decode_step.
+ */
+int attn_decode_step_noalloc(const void* q, const void* knew, const void* vnew, void* kcache,
+                             void* vcache, const int* pos, void* o, float* lse, int B, int H,
+                             int Lcap, int D, int window, void* stream);
 
 /*
  * Packed variable-length sequences (documents), for training and packed prefill.  A row of

@@ -29,7 +29,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = set(declared_functions())
     assert {"attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_decode", "attn_prefill",
-            "attn_kv_append", "attn_decode_step", "attn_fwd_varlen", "attn_bwd_varlen",
+            "attn_kv_append", "attn_decode_step", "attn_decode_step_noalloc", "attn_fwd_varlen", "attn_bwd_varlen",
             "attn_fwd_qknorm", "attn_bwd_qknorm", "attn_bwd_workspace_bytes",
             "attn_decode_workspace_bytes", "attn_decode_launches", "attn_last_error",
             "attn_abi_version"} == names
@@ -56,7 +56,7 @@ def test_nm_lists_only_c_symbols(lib):
 
 
 def test_abi_version(lib):
-    assert lib.attn_abi_version() == 5
+    assert lib.attn_abi_version() == 6
 
 
 P = 4096  # an aligned, non-null stand-in pointer: validation must fail before it is ever used
@@ -163,6 +163,33 @@ def test_decode_step_validation(lib):
     assert call(a7=P + 2) == -1  # lse alignment
     assert call(a11=80) == -2  # head dimension
     assert call(a10=0) == -1  # Lcap
+
+
+def test_decode_step_noalloc_validation(lib):
+    # q, knew, vnew, kcache, vcache, pos, o, lse, B, H, Lcap, D, window, stream
+    ok = [P, P, P, P, P, P, P, None, 2, 2, 100, 128, 8, None]
+
+    def call(**change):
+        a = list(ok)
+        for i, val in change.items():
+            a[int(i[1:])] = val
+        return lib.attn_decode_step_noalloc(*a)
+
+    assert call(a12=0) == -1  # window
+    assert call(a5=None) == -1 and "pos" in err(lib)
+    assert call(a5=P + 2) == -1  # pos alignment
+    assert call(a0=None) == -1 and "q" in err(lib)
+    assert call(a6=None) == -1 and "o" in err(lib)
+    assert call(a7=P + 2) == -1  # lse alignment
+    assert call(a11=80) == -2  # head dimension
+    assert call(a10=0) == -1  # Lcap
+    assert call(a10=65535 * 64 + 1) == -1  # the split schedule's grid limit
+    # the split schedule (few pairs, more than 2048 visible rows) whose partial results would
+    # exceed the 32 MiB static scratch is refused before any HIP call
+    assert lib.attn_decode_launches(4, 30, 70000, 128, 70000) == 2
+    assert lib.attn_decode_workspace_bytes(4, 30, 70000, 128) > 32 << 20
+    assert call(a8=4, a9=30, a10=70000, a12=70000) == -3
+    assert "static scratch" in err(lib)
 
 
 def test_varlen_validation(lib):
