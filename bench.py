@@ -10,8 +10,9 @@ One step is one pass over every part of the path, on synthetic data of the pages
   * one Engine prefill layer (the same prompts, layer step % 30).
 
 Timing protocol: every part of a step is bracketed by HIP events on the stream the kernels run on,
-and a 512 MiB scratch buffer is written just before each part (outside its events), so that no part
-finds its inputs in the 4 MB L2s or the 256 MB last-level cache.  Each figure is the median over the
+and a 512 MiB scratch buffer is written, then another 512 MiB read, just before each part (outside
+its events), so that no part finds its inputs in the 4 MB L2s or the 256 MB last-level cache, nor
+pays for writing back lines the flush left dirty.  Each figure is the median over the
 timed steps (the minimum and mean are reported next to it).  The GPU's clocks and power are sampled
 with amd-smi during the timed region.
 
@@ -303,13 +304,17 @@ def main() -> int:
     log(f"device: {props.name}, {props.multi_processor_count} CUs")
 
     scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    scratch_rd = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev).fill_(1)
     flush_n = [0]
 
     def flush():
-        """Write 512 MiB so that the next part starts with cold L2 and last-level caches."""
+        """Write 512 MiB, then read another 512 MiB, so that the next part starts with cold L2 and
+        last-level caches holding no dirty lines (left dirty by the write alone, their write-back
+        would be charged to the next part: measured ~45 us on the row-sized passes)."""
         if not args.no_flush:
             flush_n[0] += 1
             scratch.fill_(flush_n[0] & 0xFF)
+            scratch_rd.sum()
 
     Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
@@ -432,17 +437,30 @@ def main() -> int:
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    smi = SmiSampler()
-    if not args.no_smi:
-        smi.start()
     log(f"timing {args.steps} steps ...")
     t0 = time.perf_counter()
     for i in range(args.warmup, n_total):
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    clocks = smi.stop() if not args.no_smi else None
     log("timed region done")
+
+    # clocks and power under the same load: amd-smi reports the current clock, and one call takes
+    # longer than the timed region, so the d20 layer's passes run back to back for a few seconds
+    # while it samples (outside the timed region)
+    clocks = None
+    if not args.no_smi:
+        log("sampling clocks and power under load ...")
+        smi = SmiSampler()
+        smi.start()
+        t_end = time.perf_counter() + 4.0
+        while time.perf_counter() < t_end:
+            for _ in range(20):
+                sw.attn_fwd(q, k, v, o=o, lse=lse, window=win)
+                sw.attn_bwd(q, k, v, o, lse, do, window=win, dq=dq, dk=dk, dv=dv, ws=ws_b)
+            torch.cuda.synchronize()
+        clocks = smi.stop()
+        clocks["load"] = "d20 layer fwd + bwd back to back"
 
     K = args.steps
     timed = list(range(args.warmup, n_total))
@@ -759,7 +777,7 @@ def main() -> int:
             "B": B, "T": T, "H": H, "D": D, "window": None,
         },
         "timing": ("median over the timed steps of HIP-event intervals per part, each part "
-                   "preceded by a 512 MiB scratch write" if not args.no_flush else
+                   "preceded by a 512 MiB scratch write and a 512 MiB read" if not args.no_flush else
                    "median over the timed steps of HIP-event intervals per part, no flush"),
         "frac_of_peak": round(value / PEAK_MFMA_BF16, 4),
         "value_from_min": round((F_fwd + F_bwd) / fb_min / 1e12, 3),

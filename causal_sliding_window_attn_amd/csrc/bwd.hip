@@ -511,8 +511,10 @@ __device__ __forceinline__ void dkdv_loop(uint16_t* smem, uint16_t* myP, int qt_
   const int n = qt_hi - qt_lo + 1;
   int s0 = 0, s1 = 2 * SE, s2 = SE;  // element offsets of stages i % 3, (i - 1) % 3, (i + 1) % 3
   for (int i = 0; i <= n; ++i) {
-    wait_vmcnt<0>();  // tile i (the only DMA in flight) has landed
-    __syncthreads();  // ... for all waves; P of tile i - 1 is complete; stage (i + 1) % 3 is free
+    // tile i (the only DMA in flight) has landed: the P waves issued it and wait for it; then an
+    // LDS-only barrier (no release fence: nothing here hands data through global memory)
+    if (PW) wait_vmcnt<0>();
+    lds_barrier();  // ... for all waves; P of tile i - 1 is complete; stage (i + 1) % 3 is free
     const int pb = (i & 1) * PE;
     const int qt = qt_hi - i;
     dkdv_step<D, NW, PW>(smem + s0, smem + s1, smem + s2, myP + pb, myP + (PE - pb), i + 1 < n,
