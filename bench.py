@@ -304,7 +304,7 @@ def main() -> int:
     log(f"device: {props.name}, {props.multi_processor_count} CUs")
 
     scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
-    scratch_rd = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev).fill_(1)
+    scratch_rd = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)  # read by a sum
     flush_n = [0]
 
     def flush():

@@ -150,19 +150,27 @@ __device__ __forceinline__ void dq_tile(const uint16_t* __restrict__ sK,
   }
 }
 
+// Streams key tile kt of K and of V into one ring stage.
+template <int D, int NW>
+__device__ __forceinline__ void dq_issue(const RowDma<D, NW, kBwdBC>& dma, const uint16_t* kb,
+                                         const uint16_t* vb, int rs, int T, int kt,
+                                         uint16_t* stage, int wave, int lane) {
+  const int64_t row0 = (int64_t)kt * kBwdBC * rs;
+  dma.issue(kb + row0, T - kt * kBwdBC, stage, wave, lane);
+  dma.issue(vb + row0, T - kt * kBwdBC, stage + kBwdBC * D, wave, lane);
+}
+
 template <int D, int NW>
 __device__ __forceinline__ void dq_step(const uint16_t* __restrict__ cur,
                                         uint16_t* __restrict__ nxt, bool issue_next,
-                                        const uint16_t* kb, const uint16_t* vb, int rs, int T,
-                                        int kt, int qa, int qi, int w, float sl2, float lse2,
-                                        const f32x16& ndelta, const uint4 (&qf)[D / 16],
-                                        const uint4 (&df)[D / 16], const LdsOffsets<D>& lo,
-                                        f32x16 (&dqacc)[D / 32], int wave, int lane) {
+                                        const RowDma<D, NW, kBwdBC>& dma, const uint16_t* kb,
+                                        const uint16_t* vb, int rs, int T, int kt, int qa, int qi,
+                                        int w, float sl2, float lse2, const f32x16& ndelta,
+                                        const uint4 (&qf)[D / 16], const uint4 (&df)[D / 16],
+                                        const LdsOffsets<D>& lo, f32x16 (&dqacc)[D / 32],
+                                        int wave, int lane) {
   constexpr int BC = kBwdBC, TILE = BC * D;
-  if (issue_next) {
-    issue_rows<D, NW, BC>(kb, rs, (kt + 1) * BC, T - 1, nxt, wave, lane);
-    issue_rows<D, NW, BC>(vb, rs, (kt + 1) * BC, T - 1, nxt + TILE, wave, lane);
-  }
+  if (issue_next) dq_issue<D, NW>(dma, kb, vb, rs, T, kt + 1, nxt, wave, lane);
   const int k_lo = kt * BC, k_hi = k_lo + BC - 1, qz = qa + 31;
   if ((qa >= T) || (k_lo > qz) || (qa - k_hi >= w)) return;
   const bool mask = !(k_hi <= qa && qz - k_lo < w);
@@ -192,8 +200,8 @@ __device__ __forceinline__ void dq_job(const BwdArgs& p, int bh, int qt, uint16_
   const uint16_t* kb = p.k + base;
   const uint16_t* vb = p.v + base;
 
-  issue_rows<D, NW, BC>(kb, rs, kt_begin * BC, T - 1, smem, wave, lane);
-  issue_rows<D, NW, BC>(vb, rs, kt_begin * BC, T - 1, smem + TILE, wave, lane);
+  const RowDma<D, NW, BC> dma(rs, wave, lane);
+  dq_issue<D, NW>(dma, kb, vb, rs, T, kt_begin, smem, wave, lane);
 
   const int qa = q0 + 32 * wave;
   const int qi = qa + l32;
@@ -250,17 +258,17 @@ __device__ __forceinline__ void dq_job(const BwdArgs& p, int bh, int qt, uint16_
   for (; kt < kt_end; kt += 2) {
     wait_vmcnt<0>();
     __syncthreads();
-    dq_step<D, NW>(stage0, stage1, true, kb, vb, rs, T, kt, qa, qi, w, p.scale_log2, lse2, ndelta,
+    dq_step<D, NW>(stage0, stage1, true, dma, kb, vb, rs, T, kt, qa, qi, w, p.scale_log2, lse2, ndelta,
                    qf, df, lo, dqacc, wave, lane);
     wait_vmcnt<0>();
     __syncthreads();
-    dq_step<D, NW>(stage1, stage0, kt + 1 < kt_end, kb, vb, rs, T, kt + 1, qa, qi, w,
+    dq_step<D, NW>(stage1, stage0, kt + 1 < kt_end, dma, kb, vb, rs, T, kt + 1, qa, qi, w,
                    p.scale_log2, lse2, ndelta, qf, df, lo, dqacc, wave, lane);
   }
   if (kt == kt_end) {
     wait_vmcnt<0>();
     __syncthreads();
-    dq_step<D, NW>(stage0, stage1, false, kb, vb, rs, T, kt, qa, qi, w, p.scale_log2, lse2, ndelta,
+    dq_step<D, NW>(stage0, stage1, false, dma, kb, vb, rs, T, kt, qa, qi, w, p.scale_log2, lse2, ndelta,
                    qf, df, lo, dqacc, wave, lane);
   }
 
@@ -334,7 +342,7 @@ struct DkdvStage {
 };
 
 template <int D, int NW>
-__device__ __forceinline__ void dkdv_issue(const RowDma<D, NW, kBwdBQ>& dma, const uint16_t* qb,
+__device__ __forceinline__ void dkdv_issue(const RowDmaFlat<D, NW, kBwdBQ>& dma, const uint16_t* qb,
                                            const uint16_t* db, const float* lseb,
                                            const float* delb, int rs, int qt, int T,
                                            uint16_t* stage, int wave, int lane) {
@@ -483,7 +491,7 @@ __device__ __forceinline__ void dkdv_step(const uint16_t* __restrict__ curp,
                                           float sl2, const uint4 (&frag)[D / 16],
                                           f32x16 (&acc)[D / 32], f32x16 (&acc2)[D / 32],
                                           const LdsOffsets<D>& lo,
-                                          const RowDma<D, kDkdvDmaWaves, kBwdBQ>& dma, int wave,
+                                          const RowDmaFlat<D, kDkdvDmaWaves, kBwdBQ>& dma, int wave,
                                           int lane) {
   if (issue_next)
     dkdv_issue<D, kDkdvDmaWaves>(dma, qb, db, lseb, delb, rs, qt_next, T, nxt, wave, lane);
@@ -505,7 +513,7 @@ __device__ __forceinline__ void dkdv_loop(uint16_t* smem, uint16_t* myP, int qt_
                                           int kj, int T, int w, float sl2,
                                           const uint4 (&frag)[D / 16], f32x16 (&acc)[D / 32],
                                           f32x16 (&acc2)[D / 32], const LdsOffsets<D>& lo,
-                                          const RowDma<D, kDkdvDmaWaves, kBwdBQ>& dma, int wave,
+                                          const RowDmaFlat<D, kDkdvDmaWaves, kBwdBQ>& dma, int wave,
                                           int lane) {
   constexpr int SE = DkdvStage<D>::ELEMS, PE = DkdvStage<D>::PELEMS;
   const int n = qt_hi - qt_lo + 1;
@@ -554,7 +562,7 @@ __device__ __forceinline__ void dkdv_job(const BwdArgs& p, int bh, int kt, uint1
   const float* lseb = p.lse2 + rw.stat;  // LSE * log2(e), from the dQ pass
   const float* delb = p.delta + rw.stat;
 
-  const RowDma<D, kDkdvDmaWaves, BQ> dma(rs, wave, lane);  // used by the issuing waves only
+  const RowDmaFlat<D, kDkdvDmaWaves, BQ> dma(rs, wave, lane);  // used by the issuing waves only
   dkdv_issue<D, kDkdvDmaWaves>(dma, qb, db, lseb, delb, rs, qt_hi, T, smem, wave, lane);
 
   const int ka = k0 + 32 * kblk;

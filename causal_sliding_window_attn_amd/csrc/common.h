@@ -144,31 +144,63 @@ __device__ __forceinline__ int swz(int r, int c) {
                   : (c ^ (4 * ((r >> 1) & 1) + ((r >> 2) & 3)));
 }
 
-// Streams `rows` consecutive rows (row0 .. row0 + rows - 1 of a [*, rs]-strided bf16 tensor, clamped
-// to row `last`) into a row-major swizzled LDS tile with global_load_lds, NW waves sharing the work.
-// Clamped rows hold a copy of a valid row: callers mask them, and no load leaves the tensor.
-template <int D, int NW, int ROWS>
-__device__ __forceinline__ void issue_rows(const uint16_t* base, int rs, int row0, int last,
-                                           uint16_t* tile, int wave, int lane) {
-  constexpr int CPR = D / 8;     // 16-byte chunks per row
-  constexpr int RPI = 64 / CPR;  // rows per load instruction (1 KB per wave)
-  constexpr int INSTS = ROWS / RPI;
-  const int cp = lane % CPR;
-#pragma unroll
-  for (int i = wave; i < INSTS; i += NW) {
-    const int r = i * RPI + lane / CPR;
-    const int j = min(row0 + r, last);
-    g2lds16(base + (int64_t)j * rs + 8 * swz<D>(r, cp), tile + i * 512);
-  }
-}
+// Word 3 of a raw buffer resource on gfx950: 32-bit data format, byte offsets, and loads at or past
+// num_records bytes return zero.
+constexpr int kRawBufferWord3 = 0x00020000;
 
 // Plan for streaming ROWS consecutive rows of a [*, rs]-strided bf16 tensor into a row-major
-// swizzled LDS tile with global_load_lds, NW waves sharing the work (one 1 KB instruction per
-// wave each).  Each lane's byte offset inside a tile is the same for every tile, so it is computed
-// once; a full tile then costs one scalar base plus one VGPR per load.  Rows past `nvalid` re-read
-// the last valid row: callers mask them, and no load leaves the tensor.
+// swizzled LDS tile with buffer_load_dwordx4 ... lds, NW waves sharing the work (one 1 KB
+// instruction per wave each).  Each lane's byte offset inside a tile is the same for every tile, so
+// the offsets are computed once; a tile then costs a scalar resource (its first row and its valid
+// byte count) and no vector arithmetic.  Rows at or past `nvalid` fall outside the resource's range
+// and land as zeros; every load stays inside the valid rows, whatever the row stride (>= D).
 template <int D, int NW, int ROWS>
 struct RowDma {
+  static constexpr int CPR = D / 8;     // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;  // rows per load instruction
+  static constexpr int INSTS = ROWS / RPI;
+  static constexpr int PER = INSTS / NW;  // instructions per wave
+  static_assert(INSTS % NW == 0, "every wave issues the same number of loads");
+  uint32_t voff[PER];  // this lane's byte offset inside the tile, per load of the wave
+  uint32_t rs2;        // row stride in bytes
+  __device__ __forceinline__ RowDma(int rs, int wave, int lane) : rs2(2u * (uint32_t)rs) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int r = (wave + k * NW) * RPI + lane / CPR;
+      voff[k] = (uint32_t)r * rs2 + 16u * (uint32_t)swz<D>(r, lane % CPR);
+    }
+  }
+  // Tile whose first row is `tile_row0` (pointer to that row's features of this head); rows at or
+  // past nvalid read as zero.
+  __device__ __forceinline__ void issue(const uint16_t* tile_row0, int nvalid, uint16_t* lds,
+                                        int wave, int lane) const {
+    (void)lane;
+#if defined(__HIP_DEVICE_COMPILE__)  // the buffer resource type exists in the device pass only
+    // the tile's base and size are wave-uniform; readfirstlane states it, so the resource lives
+    // in scalar registers and each load is a single instruction
+    const uint64_t a = reinterpret_cast<uint64_t>(tile_row0);
+    const uint64_t au = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const int rows = min(max(nvalid, 0), ROWS);
+    const int nrec = __builtin_amdgcn_readfirstlane((int)((uint32_t)rows * rs2));
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(au), (short)0, nrec, kRawBufferWord3);
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (SWATTN_AS3 void*)(lds + (wave + k * NW) * 512),
+                                               16, voff[k], 0, 0, 0);
+#else
+    (void)tile_row0, (void)nvalid, (void)lds, (void)wave;
+#endif
+  }
+};
+
+// The same plan with global_load_lds and 64-bit per-lane addresses (one add per load per tile).
+// Rows past `nvalid` re-read the last valid row: callers mask them, and no load leaves the tensor.
+// The dK/dV pass keeps this form: with the buffer form its ring measured 2-4% slower, while the
+// forward and the dQ pass gained 3-6% from it.
+template <int D, int NW, int ROWS>
+struct RowDmaFlat {
   static constexpr int CPR = D / 8;     // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;  // rows per load instruction
   static constexpr int INSTS = ROWS / RPI;
@@ -179,7 +211,7 @@ struct RowDma {
   static_assert((NW * RPI) % 16 == 0, "swizzle period");
   uint32_t off0;  // this lane's byte offset inside the tile for the wave's first load
   int rs2;
-  __device__ __forceinline__ RowDma(int rs, int wave, int lane) : rs2(2 * rs) {
+  __device__ __forceinline__ RowDmaFlat(int rs, int wave, int lane) : rs2(2 * rs) {
     const int r = wave * RPI + lane / CPR;
     off0 = (uint32_t)(r * rs2 + 16 * swz<D>(r, lane % CPR));
   }

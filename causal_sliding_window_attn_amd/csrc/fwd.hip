@@ -194,7 +194,33 @@ __device__ __forceinline__ void fwd_step(const uint16_t* __restrict__ cur,
   fwd_tile_pv<D>(cur + TILE, sl2, lo, S, s0, s1);
 }
 
-// Key tiles kt0 .. kt1 - 1 through the NS-stage ring (stage `st` holds tile kt0 on entry).
+// One key tile through the NS-stage ring: wait for tile kt (stage st), refill the stage freed one
+// tile ago with tile kt + NS - 1, consume tile kt.
+template <int D, int NW, int NS, bool MASK>
+__device__ __forceinline__ void fwd_ring_tile(int kt, int kt_end, int st, uint16_t* smem,
+                                              const uint16_t* kb, const uint16_t* vb, int rs,
+                                              int L, int qa, int qi, int w, float sl2,
+                                              const uint4 (&qf)[D / 16], const LdsOffsets<D>& lo,
+                                              const RowDma<D, NW, kFwdBC>& dma, FwdState<D>& S,
+                                              int wave, int lane) {
+  constexpr int TILE = kFwdBC * D;
+  constexpr int LOADS = 2 * (kFwdBC * D / 512) / NW;  // DMA instructions per wave per tile
+  // tile kt has landed once at most the younger tiles' DMA (up to NS - 2 of them) is in flight
+  static_assert(NS >= 2 && NS <= 4, "ring depth");
+  const int younger = min(NS - 2, kt_end - kt);
+  if (NS == 4 && younger >= 2) wait_vmcnt<2 * LOADS>();
+  else if (NS >= 3 && younger >= 1) wait_vmcnt<LOADS>();
+  else wait_vmcnt<0>();
+  lds_barrier();  // ... for every wave (no drain of younger DMA); every wave is done with the
+                  // stage refilled next
+  const int nx = (st + NS - 1) % NS;
+  fwd_step<D, NW, MASK>(smem + st * 2 * TILE, smem + nx * 2 * TILE, kt + NS - 1 <= kt_end,
+                        kt + NS - 1, kb, vb, rs, L, kt, qa, qi, w, sl2, qf, lo, dma, S, wave, lane);
+}
+
+// Key tiles kt0 .. kt1 - 1 through the NS-stage ring (stage `st` holds tile kt0 on entry).  With
+// two stages the loop takes two tiles per trip, so that each stage's LDS base is a compile-time
+// constant and every operand read is the lane's offset plus an immediate.
 template <int D, int NW, int NS, bool MASK>
 __device__ __forceinline__ void fwd_run(int kt0, int kt1, int kt_end, int& st, uint16_t* smem,
                                         const uint16_t* kb, const uint16_t* vb, int rs, int L,
@@ -202,22 +228,31 @@ __device__ __forceinline__ void fwd_run(int kt0, int kt1, int kt_end, int& st, u
                                         const uint4 (&qf)[D / 16], const LdsOffsets<D>& lo,
                                         const RowDma<D, NW, kFwdBC>& dma, FwdState<D>& S,
                                         int wave, int lane) {
-  constexpr int TILE = kFwdBC * D;
-  constexpr int LOADS = 2 * (kFwdBC * D / 512) / NW;  // global_load_lds per wave per tile
-  for (int kt = kt0; kt < kt1; ++kt) {
-    // tile kt has landed once at most the younger tiles' DMA (up to NS - 2 of them) is in flight
-    static_assert(NS >= 2 && NS <= 4, "ring depth");
-    const int younger = min(NS - 2, kt_end - kt);
-    if (NS == 4 && younger >= 2) wait_vmcnt<2 * LOADS>();
-    else if (NS >= 3 && younger >= 1) wait_vmcnt<LOADS>();
-    else wait_vmcnt<0>();
-    lds_barrier();  // ... for every wave (no drain of younger DMA); every wave is done with the
-                    // stage refilled next
-    const int nx = (st + NS - 1) % NS;
-    fwd_step<D, NW, MASK>(smem + st * 2 * TILE, smem + nx * 2 * TILE, kt + NS - 1 <= kt_end,
-                          kt + NS - 1, kb, vb, rs, L, kt, qa, qi, w, sl2, qf, lo, dma, S, wave,
-                          lane);
-    st = (st + 1) % NS;
+  int kt = kt0;
+  if constexpr (NS == 2) {
+    if (st == 1 && kt < kt1) {
+      fwd_ring_tile<D, NW, NS, MASK>(kt, kt_end, 1, smem, kb, vb, rs, L, qa, qi, w, sl2, qf, lo,
+                                     dma, S, wave, lane);
+      ++kt;
+      st = 0;
+    }
+    for (; kt + 1 < kt1; kt += 2) {
+      fwd_ring_tile<D, NW, NS, MASK>(kt, kt_end, 0, smem, kb, vb, rs, L, qa, qi, w, sl2, qf, lo,
+                                     dma, S, wave, lane);
+      fwd_ring_tile<D, NW, NS, MASK>(kt + 1, kt_end, 1, smem, kb, vb, rs, L, qa, qi, w, sl2, qf,
+                                     lo, dma, S, wave, lane);
+    }
+    if (kt < kt1) {
+      fwd_ring_tile<D, NW, NS, MASK>(kt, kt_end, 0, smem, kb, vb, rs, L, qa, qi, w, sl2, qf, lo,
+                                     dma, S, wave, lane);
+      st = 1;
+    }
+  } else {
+    for (; kt < kt1; ++kt) {
+      fwd_ring_tile<D, NW, NS, MASK>(kt, kt_end, st, smem, kb, vb, rs, L, qa, qi, w, sl2, qf, lo,
+                                     dma, S, wave, lane);
+      st = (st + 1) % NS;
+    }
   }
 }
 
@@ -331,10 +366,11 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 1 : 2)) void fwd_bf16_kernel(Fw
   if (PAIRED) {
     const PairJob jb = pair_job(bid, p.BH, (p.n_qtiles + 1) / 2);
     const int qt1 = p.n_qtiles - 1 - jb.j;
-    fwd_job<D, NW, NS, false>(p, jb.bh, jb.j, smem, wave, lane);
-    if (qt1 != jb.j) {
-      __syncthreads();  // every wave is done with the ring before the next job refills it
-      fwd_job<D, NW, NS, false>(p, jb.bh, qt1, smem, wave, lane);
+    const int njobs = qt1 != jb.j ? 2 : 1;
+#pragma unroll 1
+    for (int jx = 0; jx < njobs; ++jx) {  // one copy of the job's code for both tiles
+      if (jx) __syncthreads();  // every wave is done with the ring before the next job refills it
+      fwd_job<D, NW, NS, false>(p, jb.bh, jx ? qt1 : jb.j, smem, wave, lane);
     }
   } else {
     fwd_job<D, NW, NS, VARLEN>(p, bid % p.BH, p.n_qtiles - 1 - bid / p.BH, smem, wave, lane);
