@@ -378,16 +378,23 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 1 : 2)) void fwd_bf16_kernel(Fw
 }
 
 // ---------------------------------------------------------------------------------------------
-// fp32 forward (fp32 in, fp32 out, fp32 MFMA v_mfma_f32_32x32x2f32).  Same structure as above;
-// each MFMA k-step carries one value per lane half, so V is read row-major straight from LDS and
-// P^T feeds the PV product one accumulator slot at a time without rounding.
+// fp32 forward (fp32 in, fp32 out, fp32 MFMA v_mfma_f32_32x32x2f32).  Each MFMA k-step carries one
+// value per lane half, so V is read row-major straight from LDS and P^T feeds the PV product one
+// accumulator slot at a time without rounding.  One workgroup owns 32 queries of one head; its
+// four waves take the query tile's 32-key tiles in turn (tile kt_begin + wave + 4 i), each with
+// its own LDS area, loads for its next tile in flight under the current one and its own online
+// softmax, and merge their (max, sum, O) through LDS at the end.  Small problems (the fp32 case
+// is used at sizes like T = 128) so spread a query tile's keys over four waves instead of
+// walking them in one.
 // ---------------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs p) {
-  constexpr int NW = 4, BR = 32 * NW, BC = 32, NT = 64 * NW, MB = D / 32;
-  constexpr int SK = D + 1;  // padded row stride (floats) against bank conflicts
-  __shared__ float sK[BC * SK];
-  __shared__ __attribute__((aligned(16))) float sV[BC * D];
+  constexpr int NW = 4, BC = 32, MB = D / 32;
+  constexpr int SK = D + 1;                      // padded K row stride (floats) against bank conflicts
+  constexpr int WAREA = BC * SK + BC * D;        // one wave's K and V tiles (floats)
+  constexpr int LPW = BC * D / 4 / 64;           // float4 loads per lane per tile and tensor
+  static_assert(MB * 16 * 64 + 128 <= WAREA, "the merge data fits a wave's tile area");
+  __shared__ __attribute__((aligned(16))) float smem[NW * WAREA];
 
   const float* qg = reinterpret_cast<const float*>(p.q);
   const float* kg = reinterpret_cast<const float*>(p.k);
@@ -403,19 +410,20 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs p) {
   const int b = bh / p.H, h = bh % p.H;
   int L = p.kv_len;
   if (p.lens) L = min(max(p.lens[b], 0), p.kv_len);
-  const int q0 = qt * BR;
+  const int q0 = qt * 32;
   if (q0 >= L) return;
   const int w = min(p.window, L);
   const int kstart = max(0, q0 - w + 1);
-  const int qend = min(q0 + BR, L);
+  const int qend = min(q0 + 32, L);
   const int kt_begin = kstart / BC, kt_end = (qend - 1) / BC;
   const float* qb = qg + (int64_t)b * p.q_bstride + h * D;
   const float* kb = kg + (int64_t)b * p.kv_bstride + h * D;
   const float* vb = vg + (int64_t)b * p.kv_bstride + h * D;
   const int rs = p.row_stride;
-  const int qa = q0 + 32 * wave;
-  const int qi = qa + l32;
+  const int qi = q0 + l32;
   const bool qvalid = qi < L;
+  float* sK = smem + wave * WAREA;
+  float* sV = sK + BC * SK;
 
   float qf[D / 2];
 #pragma unroll
@@ -425,31 +433,41 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs p) {
   for (int m = 0; m < MB; ++m) oacc[m] = zero16();
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int kt = kt_begin; kt <= kt_end; ++kt) {
-    __syncthreads();
-    // 16-byte loads, all of a thread's issued before any store (rows are 16-byte aligned)
-    constexpr int C4 = D / 4;
-    static_assert((BC * C4) % NT == 0, "whole float4 loads per thread");
+  // this wave's tiles; rows past L load as zero (and are masked: they lie past every valid query)
+  float4 kr[LPW], vr[LPW];
+  auto load = [&](int kt) {
 #pragma unroll
-    for (int it = 0; it < BC * C4 / NT; ++it) {
-      const int idx = tid + it * NT;
-      const int r = idx / C4, c4 = idx % C4;
+    for (int it = 0; it < LPW; ++it) {
+      const int idx = lane + 64 * it;
+      const int r = idx / (D / 4), c4 = idx % (D / 4);
       const int j = kt * BC + r;
-      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+      kr[it] = vr[it] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (j < L) {
-        kv = *reinterpret_cast<const float4*>(kb + (int64_t)j * rs + 4 * c4);
-        vv = *reinterpret_cast<const float4*>(vb + (int64_t)j * rs + 4 * c4);
+        kr[it] = *reinterpret_cast<const float4*>(kb + (int64_t)j * rs + 4 * c4);
+        vr[it] = *reinterpret_cast<const float4*>(vb + (int64_t)j * rs + 4 * c4);
       }
-      float* dk = sK + r * SK + 4 * c4;  // padded rows: four scalar stores
-      dk[0] = kv.x;
-      dk[1] = kv.y;
-      dk[2] = kv.z;
-      dk[3] = kv.w;
-      *reinterpret_cast<float4*>(sV + r * D + 4 * c4) = vv;
     }
-    __syncthreads();
-    const int k_lo = kt * BC, k_hi = k_lo + BC - 1, qz = qa + 31;
-    if ((qa >= L) || (k_lo > qz) || (qa - k_hi >= w)) continue;
+  };
+  int kt = kt_begin + wave;
+  if (kt <= kt_end) load(kt);
+  for (; kt <= kt_end; kt += NW) {
+    // this wave's previous tile is fully read before its area is rewritten
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int it = 0; it < LPW; ++it) {
+      const int idx = lane + 64 * it;
+      const int r = idx / (D / 4), c4 = idx % (D / 4);
+      float* dk = sK + r * SK + 4 * c4;  // padded rows: four scalar stores
+      dk[0] = kr[it].x;
+      dk[1] = kr[it].y;
+      dk[2] = kr[it].z;
+      dk[3] = kr[it].w;
+      *reinterpret_cast<float4*>(sV + r * D + 4 * c4) = vr[it];
+    }
+    if (kt + NW <= kt_end) load(kt + NW);  // next tile's loads in flight under this one
+    // the tile's stores land before any lane of the wave reads them
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int k_lo = kt * BC;
 
     f32x16 s = zero16();
 #pragma unroll
@@ -485,19 +503,50 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs p) {
       }
     }
   }
-  const float l_tot = sum_with_partner(l_run);
-  if (!qvalid) return;
+
+  // merge: every wave leaves (max, sum, O) in its own area; wave 0 combines them.  A wave with no
+  // tile leaves max = -inf, sum = 0, O = 0, which the merge weighs by 0.
+  const float l_w = sum_with_partner(l_run);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  float* mo = sK;
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mo[(m * 16 + r) * 64 + lane] = oacc[m][r];
+  mo[MB * 16 * 64 + lane] = m_run;
+  mo[MB * 16 * 64 + 64 + lane] = l_w;
+  __syncthreads();
+  if (wave != 0 || !qvalid) return;
+  float mw[NW], mx = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    mw[v] = smem[v * WAREA + MB * 16 * 64 + lane];
+    mx = fmaxf(mx, mw[v]);
+  }
+  float wt[NW], l_tot = 0.f;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    wt[v] = (mw[v] == -INFINITY) ? 0.f : exp2f(mw[v] - mx);
+    l_tot += wt[v] * smem[v * WAREA + MB * 16 * 64 + 64 + lane];
+  }
   const float inv = 1.f / l_tot;
   float* ob = og + (int64_t)b * p.q_bstride + h * D + (int64_t)qi * rs;
 #pragma unroll
   for (int m = 0; m < MB; ++m)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float4 st = make_float4(oacc[m][4 * j] * inv, oacc[m][4 * j + 1] * inv,
-                              oacc[m][4 * j + 2] * inv, oacc[m][4 * j + 3] * inv);
-      *reinterpret_cast<float4*>(ob + m * 32 + 8 * j + 4 * half) = st;
+      float o4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float acc = 0.f;
+#pragma unroll
+        for (int v = 0; v < NW; ++v) acc += wt[v] * smem[v * WAREA + (m * 16 + 4 * j + i) * 64 + lane];
+        o4[i] = acc * inv;
+      }
+      *reinterpret_cast<float4*>(ob + m * 32 + 8 * j + 4 * half) =
+          make_float4(o4[0], o4[1], o4[2], o4[3]);
     }
-  if (p.lse && half == 0) p.lse[(int64_t)bh * p.lse_T + qi] = (m_run + log2f(l_tot)) * kLn2;
+  if (p.lse && half == 0) p.lse[(int64_t)bh * p.lse_T + qi] = (mx + log2f(l_tot)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -524,7 +573,7 @@ static hipError_t launch_bf16(const FwdArgs& a, hipStream_t s) {
 template <int D>
 static hipError_t launch_f32(const FwdArgs& a, hipStream_t s) {
   FwdArgs p = a;
-  p.n_qtiles = (p.T + 127) / 128;
+  p.n_qtiles = (p.T + 31) / 32;  // 32 queries per workgroup
   const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.BH;
   hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3(grid), dim3(256), 0, s, p);
   return hipGetLastError();
