@@ -89,6 +89,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   TRY(check_dims("attn_fwd", B, H, T, "T", D, window));
   if (dtype != SWATTN_BF16 && dtype != SWATTN_F32)
     return fail(SWATTN_EUNSUPPORTED, "attn_fwd: dtype %d is not supported", dtype);
+  // the fp32 kernel launches one workgroup per 32 queries of each (sequence, head)
+  if (dtype == SWATTN_F32 && (int64_t)(T / 32 + 1) * B * H >= ((int64_t)1 << 31))
+    return fail(SWATTN_EINVAL, "attn_fwd: (T/32 + 1) * B * H exceeds 2^31 for fp32");
   TRY(check_ptr(q, "q"));
   TRY(check_ptr(k, "k"));
   TRY(check_ptr(v, "v"));

@@ -76,6 +76,15 @@ def test_fwd_rejects_bad_dims(lib, B, H, T, D, w, code):
     assert rc == code and err(lib)
 
 
+def test_fwd_fp32_grid_limit(lib):
+    # fp32 launches one workgroup per 32 queries: (T/32 + 1) * B * H must stay below 2^31, a
+    # tighter bound than the bf16 kernels' (T/128 + 1) * B * H
+    T = 1 << 24
+    assert lib.attn_fwd(P, P, P, P, None, 1, 4096, T, 64, T, 1, None) == -1
+    assert "fp32" in err(lib)
+    assert lib.attn_fwd(P, P, P, P, None, 1, 4096, T, 64, T, 7, None) == -2  # dtype first
+
+
 def test_fwd_rejects_bad_pointers_and_dtype(lib):
     assert lib.attn_fwd(None, P, P, P, None, 1, 1, 8, 64, 8, 0, None) == -1
     assert "q" in err(lib)
