@@ -15,9 +15,9 @@
 // first; half of its waves compute S = Q K^T and P, the other half, one tile behind,
 // dP = dO V^T, dS, dV^T += dO^T P and dK^T += Q^T dS, taking P through LDS (lane = key in both).
 // Under the full causal mask both passes give each workgroup a pair of tiles of equal total work
-// (pair_job).  Tiles stream global -> LDS with global_load_lds, one tile ahead with one barrier per
-// tile: a two-stage K/V ring in the dQ pass, a three-stage Q/dO ring in the dK/dV pass (the dS
-// waves still read the tile before).  Every transposed operand (K^T, Q^T, dO^T) comes straight
+// (pair_job).  Tiles stream global -> LDS by DMA (the dQ pass through buffer_load ... lds, the dK/dV
+// pass through global_load_lds), one tile ahead with one barrier per tile: a two-stage K/V ring in
+// the dQ pass, a three-stage Q/dO ring in the dK/dV pass (the dS waves still read the tile before).  Every transposed operand (K^T, Q^T, dO^T) comes straight
 // from the row-major tile through ds_read_b64_tr_b16.
 //
 // Modes (template flags; the dense instantiation is unchanged by them):

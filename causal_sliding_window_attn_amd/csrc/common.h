@@ -92,9 +92,9 @@ __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Direct global -> LDS tile streaming (global_load_lds_dwordx4) and transposed LDS reads
-// (ds_read_b64_tr_b16), with the lane semantics measured on gfx950:
-//   global_load_lds 16 B: lane l's 16 bytes land at (wave-uniform LDS base) + 16 * l.
+// Direct global -> LDS tile streaming (buffer_load_dwordx4 ... lds, global_load_lds_dwordx4) and
+// transposed LDS reads (ds_read_b64_tr_b16), with the lane semantics measured on gfx950:
+//   16-byte LDS DMA (either form): lane l's 16 bytes land at (wave-uniform LDS base) + 16 * l.
 //   ds_read_tr16_b64: within each group of 16 lanes, lane i receives in slot j element (i % 4) of
 //   the 8-byte row addressed by lane 4 * j + i / 4 of that group.
 // ---------------------------------------------------------------------------------------------
@@ -125,8 +125,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Workgroup barrier for LDS-only hand-off between waves: waits for this wave's LDS accesses, then
-// s_barrier.  Unlike __syncthreads it carries no release fence, so it does not drain global_load_lds
-// DMA still in flight to another stage.  The "memory" clobber keeps the compiler from moving memory
+// s_barrier.  Unlike __syncthreads it carries no release fence, so it does not drain LDS DMA still
+// in flight to another stage.  The "memory" clobber keeps the compiler from moving memory
 // operations across it.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");

@@ -12,7 +12,7 @@
 // lane-local plus one v_permlane32_swap.  O^T = V^T P^T reuses the S^T accumulators directly as the
 // B operand (P split into bf16 hi + lo, two MFMAs on one V fragment); the V^T fragments come from
 // the row-major V tile through ds_read_b64_tr_b16.  K/V tiles stream global -> LDS with
-// global_load_lds into a two-stage ring, one tile ahead of the compute (one barrier per tile).
+// buffer_load ... lds into a two-stage ring, one tile ahead of the compute (one barrier per tile).
 // Tiles outside [q0 - w + 1, q_end] are never loaded; per wave, tiles wholly outside the window
 // are skipped, and only tiles crossing the diagonal or the window edge run the masked loop.  O is
 // rescaled lazily, only when a row maximum grows by more than 2^8.  Under the full causal mask
@@ -32,7 +32,7 @@ constexpr int kFwdBC = 64;  // keys per tile
 #define FWD_NS 2  // K/V ring stages
 #endif
 
-// Streams one 64-key tile of K and of V into LDS (row-major, swizzled) with global_load_lds.
+// Streams one 64-key tile of K and of V into LDS (row-major, swizzled) by DMA.
 template <int D, int NW>
 __device__ __forceinline__ void fwd_issue_tile(const RowDma<D, NW, kFwdBC>& dma,
                                                const uint16_t* kb, const uint16_t* vb, int rs,
