@@ -286,6 +286,20 @@ def test_multi_batch_head_strides(sw):
     check_grads(g, ref.backward(Q, K, V, DO, 40), tag="B3 H5 T150")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_single_head_rows_touch(sw, D):
+    """H = 1: consecutive tokens' rows touch (row stride D), so a tile's valid rows end exactly where
+    the DMA's byte range ends; ragged tails (T = 150, 65) must read as masked, not as the next
+    sequence's rows."""
+    for B, T, w in ((2, 150, 2 ** 31 - 1), (3, 65, 37)):
+        q, k, v, do = W.random_attn(B, T, 1, D, seed=3000 + T + D)
+        o, lse, g = run_fwd_bwd(sw, q, k, v, do, w)
+        Q, K, V, DO = (f64(t) for t in (q, k, v, do))
+        o_r, lse_r = ref.forward(Q, K, V, w, threads=1)
+        check_fwd(o, lse, o_r, lse_r, tag=f"H1 B{B} T{T} D{D} w{w}")
+        check_grads(g, ref.backward(Q, K, V, DO, w, threads=1), tag=f"H1 B{B} T{T} D{D} w{w}")
+
+
 # --------------------------------------------------------------------------- Engine edge cases
 # Decode cases: (B, H, Lcap, cache lengths, windows, launches).  Few or many (sequence, head)
 # pairs over short caches take the one-launch schedule; few pairs that may each see more than 2048
