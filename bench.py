@@ -14,7 +14,8 @@ and a 512 MiB scratch buffer is written, then another 512 MiB read, just before 
 its events), so that no part finds its inputs in the 4 MB L2s or the 256 MB last-level cache, nor
 pays for writing back lines the flush left dirty.  Each figure is the median over the
 timed steps (the minimum and mean are reported next to it).  The GPU's clocks and power are sampled
-with amd-smi during the timed region.
+with amd-smi after the timed region, while the d20 passes run back to back for a few seconds (one
+amd-smi call takes longer than the timed region).
 
 The headline ``value`` is the d20 fwd+bwd rate in TFLOP/s counting unmasked FLOPs only (4D per
 visible (query, key) pair forward, 10D backward), from the median times.  ``decode`` reports
