@@ -665,8 +665,13 @@ static hipError_t launch_dq_d(const BwdArgs& a, hipStream_t s) {
   constexpr int NW = 4;
   BwdArgs p = a;
   p.n_tiles = (p.T + 32 * NW - 1) / (32 * NW);
-  // tile pairs carry equal work under the full causal mask over equal-length sequences
-  p.paired = (p.cu == nullptr && p.window >= p.T) ? 1 : 0;
+  // tile pairs carry equal work under the full causal mask over equal-length sequences; they are
+  // used when they fill whole rounds of the two-per-CU slots (else single tiles, longest first)
+  p.paired = (p.cu == nullptr && p.window >= p.T &&
+              pairs_fill_rounds((unsigned)(p.n_tiles + 1) / 2 * (unsigned)p.BH,
+                                2u * (unsigned)device_compute_units()))
+                 ? 1
+                 : 0;
   const unsigned per_head = p.paired ? (unsigned)(p.n_tiles + 1) / 2 : (unsigned)p.n_tiles;
   const unsigned grid = per_head * (unsigned)p.BH;
   if (p.cu)

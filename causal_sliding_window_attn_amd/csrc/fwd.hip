@@ -19,6 +19,8 @@
 // (training) a workgroup owns a pair of query tiles of equal total work (pair_job).  VARLEN:
 // packed documents (walkthrough, section "Midtraining"), each attending only to itself; a
 // workgroup reads its document's offset and length from cu and runs the same job on that slice.
+#include <atomic>
+
 #include "common.h"
 #include "launch.h"
 
@@ -550,6 +552,20 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs p) {
 }
 
 // ---------------------------------------------------------------------------------------------
+int device_compute_units() {
+  static std::atomic<int> cache[64];  // per device, 0 until looked up
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+  if (dev < 64 && n > 0) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 template <int D, int NW, int NS>
 static hipError_t launch_bf16(const FwdArgs& a, hipStream_t s) {
   FwdArgs p = a;
@@ -559,7 +575,9 @@ static hipError_t launch_bf16(const FwdArgs& a, hipStream_t s) {
   if (p.cu) {
     hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, false, true>), dim3(grid), dim3(64 * NW), 0, s,
                        p);
-  } else if (p.lens == nullptr && p.window >= p.T && p.kv_len == p.T) {
+  } else if (p.lens == nullptr && p.window >= p.T && p.kv_len == p.T &&
+             pairs_fill_rounds((unsigned)(p.n_qtiles + 1) / 2 * (unsigned)p.BH,
+                               2u * (unsigned)device_compute_units())) {
     const unsigned pairs = (unsigned)(p.n_qtiles + 1) / 2 * (unsigned)p.BH;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, true, false>), dim3(pairs), dim3(64 * NW), 0, s,
                        p);

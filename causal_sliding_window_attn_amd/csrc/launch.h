@@ -116,6 +116,18 @@ constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
 // hipGetSymbolAddress on the first call on each device and kept.
 hipError_t decode_noalloc_scratch(void** ptr);
 
+// Compute units of the current device (looked up once per device).
+int device_compute_units();
+
+// Whether the full-causal tile-pair schedule (every workgroup the same work) fills whole rounds of
+// `slots` resident workgroups closely enough.  When the last round is mostly empty (d26: 1664 pairs
+// on 512 forward slots, 3.25 rounds), single query tiles taken longest first pack it better.
+inline bool pairs_fill_rounds(unsigned pairs, unsigned slots) {
+  if (slots == 0 || pairs <= slots) return true;
+  const unsigned long long cap = (unsigned long long)((pairs + slots - 1) / slots) * slots;
+  return (cap - pairs) * 16 <= cap;  // at most 1/16 of the last round's slots idle
+}
+
 hipError_t launch_fwd(const FwdArgs& a, bool f32, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t s);
