@@ -660,9 +660,8 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs p)
 }
 
 // ------------------------------------------------------------------------------------- launchers
-template <int D>
+template <int D, int NW>
 static hipError_t launch_dq_d(const BwdArgs& a, hipStream_t s) {
-  constexpr int NW = 4;
   BwdArgs p = a;
   p.n_tiles = (p.T + 32 * NW - 1) / (32 * NW);
   // tile pairs carry equal work under the full causal mask over equal-length sequences; they are
@@ -703,8 +702,12 @@ static hipError_t launch_dkdv_d(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// As in the forward: launches with fewer 4-wave workgroups than CUs take one wave per workgroup.
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s) {
-  return a.D == 64 ? launch_dq_d<64>(a, s) : launch_dq_d<128>(a, s);
+  const long long wide = (long long)((a.T + 127) / 128) * a.BH;
+  if (wide < device_compute_units())
+    return a.D == 64 ? launch_dq_d<64, 1>(a, s) : launch_dq_d<128, 1>(a, s);
+  return a.D == 64 ? launch_dq_d<64, 4>(a, s) : launch_dq_d<128, 4>(a, s);
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t s) {

@@ -210,9 +210,16 @@ __device__ __forceinline__ void fwd_ring_tile(int kt, int kt_end, int st, uint16
   // tile kt has landed once at most the younger tiles' DMA (up to NS - 2 of them) is in flight
   static_assert(NS >= 2 && NS <= 4, "ring depth");
   const int younger = min(NS - 2, kt_end - kt);
-  if (NS == 4 && younger >= 2) wait_vmcnt<2 * LOADS>();
-  else if (NS >= 3 && younger >= 1) wait_vmcnt<LOADS>();
-  else wait_vmcnt<0>();
+  if constexpr (NS == 4) {
+    if (younger >= 2) wait_vmcnt<2 * LOADS>();
+    else if (younger >= 1) wait_vmcnt<LOADS>();
+    else wait_vmcnt<0>();
+  } else if constexpr (NS == 3) {
+    if (younger >= 1) wait_vmcnt<LOADS>();
+    else wait_vmcnt<0>();
+  } else {
+    wait_vmcnt<0>();
+  }
   lds_barrier();  // ... for every wave (no drain of younger DMA); every wave is done with the
                   // stage refilled next
   const int nx = (st + NS - 1) % NS;
@@ -597,8 +604,14 @@ static hipError_t launch_f32(const FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Launches too small to give every CU a workgroup of FWD_NW waves (short sequences, few heads) take
+// one wave per workgroup instead: four times the workgroups, each walking only its own 32 queries'
+// key tiles.
 hipError_t launch_fwd(const FwdArgs& a, bool f32, hipStream_t s) {
   if (f32) return a.D == 64 ? launch_f32<64>(a, s) : launch_f32<128>(a, s);
+  const long long wide = (long long)((a.T + 32 * FWD_NW - 1) / (32 * FWD_NW)) * a.BH;
+  if (wide < device_compute_units())
+    return a.D == 64 ? launch_bf16<64, 1, FWD_NS>(a, s) : launch_bf16<128, 1, FWD_NS>(a, s);
   return a.D == 64 ? launch_bf16<64, FWD_NW, FWD_NS>(a, s) : launch_bf16<128, FWD_NW, FWD_NS>(a, s);
 }
 
