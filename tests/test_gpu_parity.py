@@ -300,6 +300,19 @@ def test_single_head_rows_touch(sw, D):
         check_grads(g, ref.backward(Q, K, V, DO, w, threads=1), tag=f"H1 B{B} T{T} D{D} w{w}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_wide_launch_ragged(sw, D):
+    """Enough (sequence, head) pairs for the 4-wave forward and dQ launches (small launches take one
+    wave per workgroup, which the edge sweep covers), at ragged lengths and windows."""
+    for T, w in ((150, 2 ** 31 - 1), (65, 37), (300, 129)):
+        q, k, v, do = W.random_attn(4, T, 64, D, seed=4000 + T + D)
+        o, lse, g = run_fwd_bwd(sw, q, k, v, do, w)
+        Q, K, V, DO = (f64(t) for t in (q, k, v, do))
+        o_r, lse_r = ref.forward(Q, K, V, w)
+        check_fwd(o, lse, o_r, lse_r, tag=f"B4 H64 T{T} D{D} w{w}")
+        check_grads(g, ref.backward(Q, K, V, DO, w), tag=f"B4 H64 T{T} D{D} w{w}")
+
+
 # --------------------------------------------------------------------------- Engine edge cases
 # Decode cases: (B, H, Lcap, cache lengths, windows, launches).  Few or many (sequence, head)
 # pairs over short caches take the one-launch schedule; few pairs that may each see more than 2048
