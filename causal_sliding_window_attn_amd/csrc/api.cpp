@@ -536,12 +536,11 @@ int attn_fwd_qknorm(const void* q, const void* k, const void* v, void* qn, void*
   TRY(check_ptr(rk, "rk"));
   TRY(check_ptr(o, "o"));
   TRY(check_ptr(lse, "lse", true));
+  // k through the normalisation pass; q is normalised inside the forward's prologue
   swattn::NormArgs na{};
-  na.q = static_cast<const uint16_t*>(q);
+  na.q = nullptr;
   na.k = static_cast<const uint16_t*>(k);
-  na.qn = static_cast<uint16_t*>(qn);
   na.kn = static_cast<uint16_t*>(kn);
-  na.rq = rq;
   na.rk = rk;
   na.B = B;
   na.T = T;
@@ -552,7 +551,10 @@ int attn_fwd_qknorm(const void* q, const void* k, const void* v, void* qn, void*
   (void)hipGetLastError();
   TRY(hip_status(swattn::launch_qk_rmsnorm(na, s), "attn_fwd_qknorm norm launch"));
   swattn::FwdArgs a{};
-  a.q = static_cast<const uint16_t*>(qn);
+  a.q = static_cast<const uint16_t*>(q);
+  a.qn = static_cast<uint16_t*>(qn);
+  a.rq = rq;
+  a.eps = eps;
   a.k = static_cast<const uint16_t*>(kn);
   a.v = static_cast<const uint16_t*>(v);
   a.o = static_cast<uint16_t*>(o);

@@ -44,22 +44,37 @@ struct BwdRows {
   int64_t stat;  // index of its row 0 in lse, Delta and LSE * log2(e)
 };
 
+// A row's MFMA fragments (the lane holds its 8-column chunks 2 t + half in f[t], the partner lane
+// lane ^ 32 the others) rearranged into the accumulator's element order (columns 8 c + 4 half ..
+// + 3 of every chunk c, as y[c / 4][c % 4]): per fragment, one v_permlane32_swap for each dword
+// pair hands the partner the four columns it lacks and takes the four this lane lacks.
+template <int D>
+__device__ __forceinline__ void frag_to_acc_order(const uint4 (&f)[D / 16],
+                                                  uint2 (&y)[D / 32][4]) {
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    const auto a = __builtin_amdgcn_permlane32_swap(f[t].x, f[t].z, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(f[t].y, f[t].w, false, false);
+    const int m = t / 2, j = 2 * (t % 2);
+    y[m][j] = make_uint2(a[0], b[0]);      // chunk 2 t
+    y[m][j + 1] = make_uint2(a[1], b[1]);  // chunk 2 t + 1
+  }
+}
+
 // QK-norm backward, fused into a pass's epilogue.  With y = x / rms(x) the normalised row (the
-// attention's input, re-read here in the accumulator's element order), g = acc * sc the gradient
-// with respect to y and r = 1 / rms(x):  dx = r (g - y (g . y) / D).  A lane and its partner
-// (lane ^ 32) hold the two halves of the row.
+// attention's input, in the accumulator's element order), g = acc * sc the gradient with respect
+// to y and r = 1 / rms(x):  dx = r (g - y (g . y) / D).  A lane and its partner (lane ^ 32) hold
+// the two halves of the row.
 template <int D>
 __device__ __forceinline__ void store_through_rmsnorm(const f32x16 (&acc)[D / 32], float sc,
-                                                      const uint16_t* yrow, float r,
+                                                      const uint2 (&y)[D / 32][4], float r,
                                                       uint16_t* out, int half) {
   constexpr int MB = D / 32;
-  uint2 y[MB][4];
   float dot = 0.f;
 #pragma unroll
   for (int m = 0; m < MB; ++m)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      y[m][j] = *reinterpret_cast<const uint2*>(yrow + m * 32 + 8 * j + 4 * half);
       dot = fmaf(acc[m][4 * j + 0] * sc, bf16_lo(y[m][j].x), dot);
       dot = fmaf(acc[m][4 * j + 1] * sc, bf16_hi(y[m][j].x), dot);
       dot = fmaf(acc[m][4 * j + 2] * sc, bf16_lo(y[m][j].y), dot);
@@ -218,6 +233,7 @@ __device__ __forceinline__ void dq_job(const BwdArgs& p, int bh, int qt, uint16_
     of[t] = ldg16(p.o + roff + 16 * t);
   }
   const float lse_raw = p.lse[rw.stat + qc];
+  const float rq = QKN ? p.rq[rw.stat + qc] : 0.f;  // QK-norm: 1 / rms of the raw row
   float dsum = 0.f;
 #pragma unroll
   for (int t = 0; t < DK; ++t) {
@@ -275,9 +291,10 @@ __device__ __forceinline__ void dq_job(const BwdArgs& p, int bh, int qt, uint16_
   if (!qvalid) return;
   const float sc = p.scale;
   uint16_t* out = p.dq + base + (int64_t)qi * rs;
-  if constexpr (QKN) {  // dq with respect to the raw rows; p.q holds the normalised ones
-    store_through_rmsnorm<D>(dqacc, sc, p.q + base + (int64_t)qi * rs, p.rq[rw.stat + qi], out,
-                             half);
+  if constexpr (QKN) {  // dq with respect to the raw rows; qf holds the normalised ones
+    uint2 y[MB][4];
+    frag_to_acc_order<D>(qf, y);
+    store_through_rmsnorm<D>(dqacc, sc, y, rq, out, half);
     return;
   }
 #pragma unroll
@@ -574,6 +591,8 @@ __device__ __forceinline__ void dkdv_job(const BwdArgs& p, int bh, int kt, uint1
   const int64_t foff = base + (int64_t)min(kj, T - 1) * rs + 8 * half;
 #pragma unroll
   for (int t = 0; t < DK; ++t) frag[t] = ldg16(fsrc + foff + 16 * t);
+  // QK-norm: 1 / rms of the raw k row, for dk's epilogue in the dS waves
+  const float rk = QKN && !pwave ? p.rk[rw.stat + min(kj, T - 1)] : 0.f;
   if (!kvalid)
 #pragma unroll
     for (int t = 0; t < DK; ++t) frag[t] = make_uint4(0, 0, 0, 0);
@@ -598,6 +617,26 @@ __device__ __forceinline__ void dkdv_job(const BwdArgs& p, int bh, int kt, uint1
     dkdv_loop<D, NW, false>(smem, myP, qt_lo, qt_hi, qb, db, lseb, delb, rs, ka, kj, T, w,
                             p.scale_log2, frag, acc, acc2, lo, dma, wave, lane);
 
+  // QK-norm: the normalised k rows sit in the P waves' fragments; they reach the dS waves through
+  // the ring's LDS (free once every wave is past the loop), rows padded by 16 bytes.
+  uint2 ky[QKN ? MB : 1][4];
+  if constexpr (QKN) {
+    constexpr int XS = D + 8;
+    static_assert(NW * 16 * XS <= kDkdvStages * DkdvStage<D>::ELEMS, "k rows fit the ring");
+    uint16_t* xrow = smem + (kblk * 32 + l32) * XS;
+    __syncthreads();
+    if (pwave)
+#pragma unroll
+      for (int t = 0; t < DK; ++t) *reinterpret_cast<uint4*>(xrow + 16 * t + 8 * half) = frag[t];
+    __syncthreads();
+    if (!pwave)
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          ky[m][j] = *reinterpret_cast<const uint2*>(xrow + m * 32 + 8 * j + 4 * half);
+  }
+
   if (!kvalid || pwave) return;
   {
     uint16_t* out = p.dv + base + (int64_t)kj * rs;
@@ -613,9 +652,8 @@ __device__ __forceinline__ void dkdv_job(const BwdArgs& p, int bh, int kt, uint1
   }
   const float sc = -p.scale;  // the dS waves accumulated -dK^T
   uint16_t* out = p.dk + base + (int64_t)kj * rs;
-  if constexpr (QKN) {  // dk with respect to the raw rows; p.k holds the normalised ones
-    store_through_rmsnorm<D>(acc, sc, p.k + base + (int64_t)kj * rs, p.rk[rw.stat + kj], out,
-                             half);
+  if constexpr (QKN) {  // dk with respect to the raw rows
+    store_through_rmsnorm<D>(acc, sc, ky, rk, out, half);
     return;
   }
 #pragma unroll

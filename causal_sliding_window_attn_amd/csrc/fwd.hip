@@ -265,9 +265,47 @@ __device__ __forceinline__ void fwd_run(int kt0, int kt1, int kt_end, int& st, u
   }
 }
 
+// QK-norm: RMS-normalises the lane's query row in registers and returns r = 1 / sqrt(mean x^2 +
+// eps).  The lane holds the row's 8-column chunks 2 t + half (t < D / 16), its partner lane
+// (lane ^ 32) the others.  The sum of squares runs per chunk, then over chunk pairs (c, c ^ 1),
+// (c, c ^ 2), ...: the order of the normalisation pass (norm.hip), so that r and the bf16 row come
+// out bit for bit as that pass gives them.
+template <int D>
+__device__ __forceinline__ float qnorm_regs(uint4 (&qf)[D / 16], float eps) {
+  constexpr int DK = D / 16;
+  float x[DK][8], v[DK];
+#pragma unroll
+  for (int t = 0; t < DK; ++t) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(&qf[t]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[t][2 * e] = bf16_lo(w[e]);
+      x[t][2 * e + 1] = bf16_hi(w[e]);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(x[t][e], x[t][e], ss);
+    v[t] = ss + __shfl_xor(ss, 32);  // chunks 2 t and 2 t + 1
+  }
+#pragma unroll
+  for (int off = 1; off < DK; off <<= 1)
+#pragma unroll
+    for (int t = 0; t < DK; t += 2 * off) v[t] = v[t] + v[t + off];
+  const float r = 1.f / sqrtf(v[0] / (float)D + eps);
+#pragma unroll
+  for (int t = 0; t < DK; ++t) {
+    qf[t].x = pack_bf16x2(x[t][0] * r, x[t][1] * r);
+    qf[t].y = pack_bf16x2(x[t][2] * r, x[t][3] * r);
+    qf[t].z = pack_bf16x2(x[t][4] * r, x[t][5] * r);
+    qf[t].w = pack_bf16x2(x[t][6] * r, x[t][7] * r);
+  }
+  return r;
+}
+
 // One job: query tile qt (NW waves x 32 queries) of head bh, NS-stage K/V ring (prefetch NS - 1
-// tiles ahead).  Returns with every wave past its last read of the ring.
-template <int D, int NW, int NS, bool VARLEN>
+// tiles ahead).  Returns with every wave past its last read of the ring.  QNORM: the QK-norm
+// forward; q holds raw rows, normalised in the prologue and written to qn / rq at the end.
+template <int D, int NW, int NS, bool VARLEN, bool QNORM>
 __device__ __forceinline__ void fwd_job(const FwdArgs& p, int bh, int qt, uint16_t* smem,
                                         int wave, int lane) {
   constexpr int BR = 32 * NW;
@@ -309,7 +347,7 @@ __device__ __forceinline__ void fwd_job(const FwdArgs& p, int bh, int qt, uint16
   const int64_t qoff = (int64_t)min(qi, L - 1) * rs + 8 * half;
 #pragma unroll
   for (int t = 0; t < DK; ++t) qf[t] = ldg16(qb + qoff + 16 * t);
-  if (!qvalid)
+  if (!QNORM && !qvalid)  // QK-norm: after the normalisation, below
 #pragma unroll
     for (int t = 0; t < DK; ++t) qf[t] = make_uint4(0, 0, 0, 0);
 
@@ -326,6 +364,13 @@ __device__ __forceinline__ void fwd_job(const FwdArgs& p, int bh, int qt, uint16
     if (kt_begin + i <= kt_end)
       fwd_issue_tile<D, NW>(dma, kb, vb, rs, kt_begin + i, L, smem + i * 2 * TILE,
                             smem + i * 2 * TILE + TILE, wave, lane);
+  float qr = 0.f;
+  if constexpr (QNORM) {  // under the first tiles' DMA
+    qr = qnorm_regs<D>(qf, p.eps);
+    if (!qvalid)
+#pragma unroll
+      for (int t = 0; t < DK; ++t) qf[t] = make_uint4(0, 0, 0, 0);
+  }
   // Tiles that every wave of the workgroup sees whole (k_hi <= q0 and q0 + BR - 1 - k_lo < w) run
   // without the mask; the window-edge tiles before them and the diagonal tiles after them run with
   // it.  Three loops rather than a per-tile branch keep O in one set of registers.
@@ -359,12 +404,18 @@ __device__ __forceinline__ void fwd_job(const FwdArgs& p, int bh, int qt, uint16
       *reinterpret_cast<uint2*>(ob + m * 32 + 8 * j + 4 * half) = st;
     }
   if (p.lse && half == 0) p.lse[lse0 + qi] = (S.m_use + __log2f(l_tot)) * kLn2;
+  if constexpr (QNORM) {  // the normalised row, as the MFMAs used it, and its r
+    uint16_t* qnb = p.qn + q_row0 + h * D + (int64_t)qi * rs + 8 * half;
+#pragma unroll
+    for (int t = 0; t < DK; ++t) *reinterpret_cast<uint4*>(qnb + 16 * t) = qf[t];
+    if (half == 0) p.rq[(int64_t)bh * p.T + qi] = qr;
+  }
 }
 
 // PAIRED (full-causal training forward): workgroup = head + query-tile pair (j, n - 1 - j), the
 // short tile first, so that a head's workgroups start on the same K/V tiles together (pair_job).
 // Otherwise (prefill, sliding window): workgroup = one query tile, longest tiles first.
-template <int D, int NW, int NS, bool PAIRED, bool VARLEN>
+template <int D, int NW, int NS, bool PAIRED, bool VARLEN, bool QNORM>
 __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 1 : 2)) void fwd_bf16_kernel(FwdArgs p) {
   static_assert((kFwdBC * D / 512) % NW == 0, "every wave issues the same number of DMA loads");
   __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * 2 * kFwdBC * D];  // [stage][K|V]
@@ -379,10 +430,11 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 1 : 2)) void fwd_bf16_kernel(Fw
 #pragma unroll 1
     for (int jx = 0; jx < njobs; ++jx) {  // one copy of the job's code for both tiles
       if (jx) __syncthreads();  // every wave is done with the ring before the next job refills it
-      fwd_job<D, NW, NS, false>(p, jb.bh, jx ? qt1 : jb.j, smem, wave, lane);
+      fwd_job<D, NW, NS, false, QNORM>(p, jb.bh, jx ? qt1 : jb.j, smem, wave, lane);
     }
   } else {
-    fwd_job<D, NW, NS, VARLEN>(p, bid % p.BH, p.n_qtiles - 1 - bid / p.BH, smem, wave, lane);
+    fwd_job<D, NW, NS, VARLEN, QNORM>(p, bid % p.BH, p.n_qtiles - 1 - bid / p.BH, smem, wave,
+                                      lane);
   }
 }
 
@@ -579,19 +631,25 @@ static hipError_t launch_bf16(const FwdArgs& a, hipStream_t s) {
   p.n_qtiles = (p.T + 32 * NW - 1) / (32 * NW);
   // tile pairs carry equal work only when every query sees all earlier keys
   const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.BH;
-  if (p.cu) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, false, true>), dim3(grid), dim3(64 * NW), 0, s,
+  const unsigned pairs = (unsigned)(p.n_qtiles + 1) / 2 * (unsigned)p.BH;
+  const bool paired = p.cu == nullptr && p.lens == nullptr && p.window >= p.T &&
+                      p.kv_len == p.T && pairs_fill_rounds(pairs, 2u * device_compute_units());
+  const dim3 block(64 * NW);
+  if (p.cu)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, false, true, false>), dim3(grid), block, 0, s,
                        p);
-  } else if (p.lens == nullptr && p.window >= p.T && p.kv_len == p.T &&
-             pairs_fill_rounds((unsigned)(p.n_qtiles + 1) / 2 * (unsigned)p.BH,
-                               2u * (unsigned)device_compute_units())) {
-    const unsigned pairs = (unsigned)(p.n_qtiles + 1) / 2 * (unsigned)p.BH;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, true, false>), dim3(pairs), dim3(64 * NW), 0, s,
+  else if (p.qn && paired)  // QK-norm (dense training only)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, true, false, true>), dim3(pairs), block, 0, s,
                        p);
-  } else {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, false, false>), dim3(grid), dim3(64 * NW), 0, s,
+  else if (p.qn)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, false, false, true>), dim3(grid), block, 0, s,
                        p);
-  }
+  else if (paired)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, true, false, false>), dim3(pairs), block, 0, s,
+                       p);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, false, false, false>), dim3(grid), block, 0, s,
+                       p);
   return hipGetLastError();
 }
 

@@ -26,6 +26,11 @@ struct FwdArgs {
   int lse_T;
   int n_qtiles;        // filled by the launcher
   float scale_log2;    // log2(e) / sqrt(D)
+  // QK-norm forward (dense training only): q holds the raw rows; each row is RMS-normalised in
+  // registers, the bf16 result written to qn ([B, T, H, D]) and 1 / rms to rq ([B, H, T]).
+  uint16_t* qn;        // null: q is used as given
+  float* rq;
+  float eps;
 };
 
 struct BwdArgs {
@@ -74,7 +79,7 @@ struct DecArgs {
 
 // Parameter-free RMS normalisation of the q and k rows ([B, T, H, D] bf16).
 struct NormArgs {
-  const uint16_t* q;
+  const uint16_t* q;  // null: k only
   const uint16_t* k;
   uint16_t* qn;  // q / rms(q), bf16
   uint16_t* kn;

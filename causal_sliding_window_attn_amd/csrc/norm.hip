@@ -7,9 +7,10 @@
 //   r = 1 / sqrt(mean_d x_d^2 + eps),  x_hat = x * r   (one row = one token of one head).
 // The normalised rows are what the attention kernels read, and the backward needs them again, so
 // they are written once (bf16, round to nearest even) together with r (fp32, [B, H, T]); the
-// norm's own backward runs inside the dQ and dK/dV epilogues (bwd.hip).
+// norm's own backward runs inside the dQ and dK/dV epilogues (bwd.hip).  The QK-norm forward
+// normalises q itself, in its prologue (fwd.hip), and runs this pass on k alone (q null).
 //
-// Memory-bound: one read and one write of q and k.  D / 8 lanes hold one row (16 bytes each), so a
+// Memory-bound: one read and one write of each row.  D / 8 lanes hold one row (16 bytes each), so a
 // wave normalises 64 / (D / 8) rows and the sum of squares is a reduction over D / 8 lanes.
 #include "common.h"
 #include "launch.h"
@@ -28,7 +29,7 @@ __global__ __launch_bounds__(256) void qk_rmsnorm_kernel(NormArgs p) {
   constexpr int LPR = D / 8;          // lanes per row
   constexpr int RPB = 256 / LPR;      // rows per workgroup
   const int64_t rows = (int64_t)p.B * p.T * p.H;  // rows of q, then rows of k
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int64_t row = (p.q ? 0 : rows) + (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
   const int c = threadIdx.x % LPR;
   if (row >= 2 * rows) return;  // every lane of a row group leaves together
   const bool is_k = row >= rows;
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(256) void qk_rmsnorm_kernel(NormArgs p) {
 }
 
 hipError_t launch_qk_rmsnorm(const NormArgs& a, hipStream_t s) {
-  const int64_t rows = 2 * (int64_t)a.B * a.T * a.H;
+  const int64_t rows = (a.q ? 2 : 1) * (int64_t)a.B * a.T * a.H;  // q null: k only
   const int rpb = 256 / (a.D / 8);
   const unsigned grid = (unsigned)((rows + rpb - 1) / rpb);
   if (a.D == 64)

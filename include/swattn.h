@@ -226,7 +226,9 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
  * optimisers).  Per row (one token of one head): r = 1 / sqrt(mean_d x_d^2 + eps), x_hat = x r.
  *   attn_fwd_qknorm: writes qn = bf16(q r_q), kn = bf16(k r_k) ([B, T, H, D]) and rq, rk (r per
  *     row, float32 [B, H, T]), then runs attn_fwd on (qn, kn, v): o, lse as attn_fwd.
- *     eps >= 0 and finite.  Two launches (the normalisation, then the attention).
+ *     eps >= 0 and finite.  Two launches: the normalisation of k, then the attention, which
+ *     normalises q in its prologue (same arithmetic, same order: rq, qn as the pass on k gives
+ *     rk, kn for an equal row).
  *   attn_bwd_qknorm: the backward of the whole map (q, k, v) -> o, given the forward's qn, kn, rq,
  *     rk, o, lse: dq, dk are gradients with respect to the raw q and k (the norm's backward,
  *     dx = r (dx_hat - x_hat (dx_hat . x_hat) / D), runs inside the passes' epilogues), dv as

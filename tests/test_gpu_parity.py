@@ -732,6 +732,26 @@ def test_qknorm_fused_epilogue_equals_unfused_composition(sw):
         assert e <= 1e-2, e
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("shape", [(2, 333, 3), (4, 600, 16)])  # one-wave and 4-wave launches
+def test_qknorm_prologue_matches_norm_pass(sw, D, shape):
+    """q is normalised inside the forward's prologue and k by the separate pass: on equal rows the
+    two give bit-identical normalised rows and r, and O / LSE are bit for bit those of the plain
+    forward over the rows the call wrote."""
+    B, T, H = shape
+    g = torch.Generator().manual_seed(130 + D + T)
+    x = (1.7 * torch.randn(B, T, H, D, generator=g)).to(torch.bfloat16).to(DEV)
+    v = torch.randn(B, T, H, D, generator=g).to(torch.bfloat16).to(DEV)
+    for window in (None, 77):
+        o, lse, qn, kn, rq, rk = sw.attn_fwd_qknorm(x, x, v, window=window, eps=1e-5)
+        o2, lse2 = sw.attn_fwd(qn, kn, v, window=window)
+        torch.cuda.synchronize()
+        assert torch.equal(qn, kn), f"window {window}"
+        assert torch.equal(rq, rk), f"window {window}"
+        assert torch.equal(o, o2), f"window {window}"
+        assert torch.equal(lse, lse2), f"window {window}"
+
+
 def test_qknorm_autograd_wrapper(sw):
     q, k, v, do = W.random_attn(1, 96, 2, 64, seed=121)
     qd, kd, vd = (t.to(DEV).requires_grad_() for t in (q, k, v))
