@@ -17,8 +17,10 @@
 // Under the full causal mask both passes give each workgroup a pair of tiles of equal total work
 // (pair_job).  Tiles stream global -> LDS by DMA (the dQ pass through buffer_load ... lds, the dK/dV
 // pass through global_load_lds), one tile ahead with one barrier per tile: a two-stage K/V ring in
-// the dQ pass, a three-stage Q/dO ring in the dK/dV pass (the dS waves still read the tile before).  Every transposed operand (K^T, Q^T, dO^T) comes straight
-// from the row-major tile through ds_read_b64_tr_b16.
+// the dQ pass, a three-stage Q/dO ring in the dK/dV pass (the dS waves still read the tile
+// before).  Every transposed operand (K^T, Q^T, dO^T) comes straight from the row-major tile
+// through ds_read_b64_tr_b16.  On dense launches the dK/dV pass runs on a persistent grid whose
+// workgroups chain their jobs through one tile stream (bwd_dkdv_chain_kernel).
 //
 // Modes (template flags; the dense instantiation is unchanged by them):
 //   VARLEN  packed documents (rows cu[s] .. cu[s+1] - 1 of [total, H, D], each attending only to
@@ -667,9 +669,10 @@ __device__ __forceinline__ void dkdv_job(const BwdArgs& p, int bh, int kt, uint1
     }
 }
 
-// Full-causal training pass (p.paired): workgroup = head + key-tile pair (n - 1 - j, j), the short
-// tile (fewest queries) first, so that a head's workgroups start on the same query tiles together
-// (pair_job).  Otherwise: workgroup = one key tile, those seeing the most queries first.
+// One workgroup per unit (packed documents and QK-norm launches): full-causal training pass
+// (p.paired): workgroup = head + key-tile pair (n - 1 - j, j), the short tile (fewest queries)
+// first, so that a head's workgroups start on the same query tiles together (pair_job).
+// Otherwise: workgroup = one key tile, those seeing the most queries first.
 template <int D, bool VARLEN, bool QKN>
 __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs p) {
   constexpr int SE = DkdvStage<D>::ELEMS, PE = DkdvStage<D>::PELEMS;
@@ -695,6 +698,215 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs p)
     if (jx) __syncthreads();  // every wave is done with the ring and P before the next job
     dkdv_job<D, VARLEN, QKN>(p, bh, jx ? kt1 : kt0, smem, sPbuf, wave, lane);
   }
+}
+
+// ------------------------------------------------------------------------ dK/dV, chained jobs
+// Dense launches (no packed documents, no QK-norm) run the dK/dV pass on a persistent grid, one
+// workgroup per CU (a workgroup fills a CU: 8 waves at up to 256 VGPRs, 132 KB of LDS).  Each
+// walks a fixed list of jobs whose query tiles form one stream through the ring and the P
+// buffers, so the P waves start a job's first tile while the dS waves finish the previous job's
+// last one: no pipeline fill or drain and no start-up per job.  The P waves load the next job's K
+// right after their last tile of the current one; the dS waves store dK and dV and load the next
+// job's V right after theirs.
+//
+// Units blockIdx.x, blockIdx.x + gridDim.x, ...: paired (full causal), unit u is the tile pair
+// pair_job(u) (key tiles n - 1 - j, then j); otherwise unit u is key tile u / BH of head u % BH.
+struct DkdvJob {
+  int bh, kt;
+  int qt_hi, qt_lo;  // the query tiles that see key tile kt, walked from qt_hi down
+};
+
+// Job s (0 or 1) of unit u; false (jb untouched) if there is none.
+__device__ __forceinline__ bool dkdv_unit_job(const BwdArgs& p, int u, int s, DkdvJob& jb) {
+  const int n = p.n_tiles;
+  int bh, kt;
+  if (p.paired) {
+    const int npair = (n + 1) / 2;
+    if (u >= p.BH * npair) return false;
+    const PairJob pj = pair_job(u, p.BH, npair);
+    const int kt0 = n - 1 - pj.j;
+    if (s == 1 && pj.j == kt0) return false;
+    bh = pj.bh;
+    kt = s ? pj.j : kt0;
+  } else {
+    if (s != 0 || u >= n * p.BH) return false;
+    bh = u % p.BH;
+    kt = u / p.BH;
+  }
+  const int k0 = kt * 128, w = min(p.window, p.T);
+  jb.bh = bh;
+  jb.kt = kt;
+  jb.qt_lo = k0 / kBwdBQ;
+  jb.qt_hi = (min(p.T, k0 + 127 + w) - 1) / kBwdBQ;
+  return true;
+}
+
+// A position in the workgroup's job list (wave-uniform): unit u, job s of it.
+struct DkdvCursor {
+  int u, s;
+};
+
+// The B fragments of a job: K for the P waves, -V for the dS waves (rows past T zero).
+template <int D, bool PW>
+__device__ __forceinline__ void dkdv_load_frag(const BwdArgs& p, const DkdvJob& jb, int kblk,
+                                               int lane, uint4 (&frag)[D / 16]) {
+  const int half = lane >> 5, l32 = lane & 31;
+  const int b = jb.bh / p.H, h = jb.bh % p.H;
+  const int kj = jb.kt * 128 + 32 * kblk + l32;
+  const uint16_t* src = (PW ? p.k : p.v) + (int64_t)b * p.bstride + h * D +
+                        (int64_t)min(kj, p.T - 1) * p.row_stride + 8 * half;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) frag[t] = ldg16(src + 16 * t);
+  if (kj >= p.T)
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) frag[t] = make_uint4(0, 0, 0, 0);
+  if (!PW)
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      frag[t].x ^= 0x80008000u;
+      frag[t].y ^= 0x80008000u;
+      frag[t].z ^= 0x80008000u;
+      frag[t].w ^= 0x80008000u;
+    }
+}
+
+// dS waves: dV and dK of a finished job (the waves accumulated dV^T and -dK^T).
+template <int D>
+__device__ __forceinline__ void dkdv_store(const BwdArgs& p, const DkdvJob& jb, int kblk,
+                                           int lane, const f32x16 (&dkacc)[D / 32],
+                                           const f32x16 (&dvacc)[D / 32]) {
+  const int half = lane >> 5, l32 = lane & 31;
+  const int kj = jb.kt * 128 + 32 * kblk + l32;
+  if (kj >= p.T) return;
+  const int b = jb.bh / p.H, h = jb.bh % p.H;
+  const int64_t row = (int64_t)b * p.bstride + h * D + (int64_t)kj * p.row_stride + 4 * half;
+  const float sc = -p.scale;
+#pragma unroll
+  for (int m = 0; m < D / 32; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint2 v, k;
+      v.x = pack_bf16x2(dvacc[m][4 * j + 0], dvacc[m][4 * j + 1]);
+      v.y = pack_bf16x2(dvacc[m][4 * j + 2], dvacc[m][4 * j + 3]);
+      k.x = pack_bf16x2(dkacc[m][4 * j + 0] * sc, dkacc[m][4 * j + 1] * sc);
+      k.y = pack_bf16x2(dkacc[m][4 * j + 2] * sc, dkacc[m][4 * j + 3] * sc);
+      *reinterpret_cast<uint2*>(p.dv + row + m * 32 + 8 * j) = v;
+      *reinterpret_cast<uint2*>(p.dk + row + m * 32 + 8 * j) = k;
+    }
+}
+
+// The job after the cursor's (the cursor moves to it); false past the workgroup's last.
+__device__ __forceinline__ bool dkdv_next_job(const BwdArgs& p, DkdvCursor& c, DkdvJob& jb) {
+  if (c.s == 0 && dkdv_unit_job(p, c.u, 1, jb)) {
+    c.s = 1;
+    return true;
+  }
+  c.u += gridDim.x;
+  c.s = 0;
+  return dkdv_unit_job(p, c.u, 0, jb);
+}
+
+// Rows of a job's head: Q, dO (element offsets) and LSE * log2(e), Delta.
+struct DkdvRows {
+  const uint16_t *q, *dout;
+  const float *lse2, *delta;
+};
+template <int D>
+__device__ __forceinline__ DkdvRows dkdv_rows(const BwdArgs& p, const DkdvJob& jb) {
+  const int b = jb.bh / p.H, h = jb.bh % p.H;
+  const int64_t base = (int64_t)b * p.bstride + h * D, stat = (int64_t)jb.bh * p.T;
+  return {p.q + base, p.dout + base, p.lse2 + stat, p.delta + stat};
+}
+
+// One role's walk over the workgroup's jobs.  Global iteration g runs the P waves on stream tile
+// g and the dS waves on tile g - 1, one barrier each (tiles + 1 in all for both roles): the P
+// waves idle in the last iteration, the dS waves in the first.  Within a job the tile loop is
+// the single-job loop's; between jobs the P waves load the next K, the dS waves store dK and dV
+// and load the next -V.
+template <int D, bool PW>
+__device__ __forceinline__ void dkdv_chain(const BwdArgs& p, uint16_t* smem, uint16_t* myP,
+                                           int kblk, int wave, int lane) {
+  constexpr int BQ = kBwdBQ, MB = D / 32;
+  constexpr int SE = DkdvStage<D>::ELEMS, PE = DkdvStage<D>::PELEMS;
+  const int l32 = lane & 31;
+  const int w = min(p.window, p.T), rs = p.row_stride;
+  const LdsOffsets<D> lo(lane);
+  const RowDmaFlat<D, kDkdvDmaWaves, BQ> dma(rs, wave, lane);
+  DkdvCursor c{(int)blockIdx.x, 0};
+  DkdvJob J;
+  dkdv_unit_job(p, c.u, 0, J);  // the launch has no more workgroups than units
+  DkdvJob N = J;
+  bool hasN = dkdv_next_job(p, c, N);
+  uint4 frag[D / 16];
+  dkdv_load_frag<D, PW>(p, J, kblk, lane, frag);
+  f32x16 acc[MB], acc2[MB];  // dS waves: dK^T, dV^T
+#pragma unroll
+  for (int m = 0; m < MB; ++m) acc[m] = acc2[m] = zero16();
+
+  int g = 0, s0 = 0, s1 = 2 * SE, s2 = SE;  // stages g % 3, (g - 1) % 3, (g + 1) % 3
+  auto rotate = [&] {  // the stage just read one behind becomes the next DMA target
+    const int t = s1;
+    s1 = s0;
+    s0 = s2;
+    s2 = t;
+    ++g;
+  };
+  if (PW) {
+    DkdvRows rj = dkdv_rows<D>(p, J);
+    dkdv_issue<D, kDkdvDmaWaves>(dma, rj.q, rj.dout, rj.lse2, rj.delta, rs, J.qt_hi, p.T, smem,
+                                 wave, lane);
+  } else {
+    lds_barrier();  // iteration 0: the P waves' first tile
+    rotate();
+  }
+#pragma unroll 1
+  while (true) {
+    const DkdvRows rj = dkdv_rows<D>(p, J);
+    const int ka = J.kt * 128 + 32 * kblk, n = J.qt_hi - J.qt_lo + 1;
+#pragma unroll 1
+    for (int i = 0; i < n; ++i) {
+      // tile g (the only DMA in flight) has landed: the P waves issued it and wait for it; then
+      // an LDS-only barrier for all waves: P of tile g - 1 is complete, stage (g + 1) % 3 is free
+      if (PW) wait_vmcnt<0>();
+      lds_barrier();
+      const int pb = (g & 1) * PE, qt = J.qt_hi - i;
+      const bool last = i == n - 1;  // the next stream tile is the next job's first
+      const DkdvRows rx = last && hasN ? dkdv_rows<D>(p, N) : rj;
+      dkdv_step<D, kDkdvWaves, PW>(smem + s0, smem + s1, smem + s2, myP + pb, myP + (PE - pb),
+                                   PW && (!last || hasN), true, rx.q, rx.dout, rx.lse2, rx.delta,
+                                   rs, qt, qt, last ? N.qt_hi : qt - 1, ka, ka + l32, p.T, w,
+                                   p.scale_log2, frag, acc, acc2, lo, dma, wave, lane);
+      rotate();
+    }
+    if (!PW) {
+      dkdv_store<D>(p, J, kblk, lane, acc, acc2);
+#pragma unroll
+      for (int m = 0; m < MB; ++m) acc[m] = acc2[m] = zero16();
+    }
+    if (!hasN) break;
+    J = N;
+    hasN = dkdv_next_job(p, c, N);
+    dkdv_load_frag<D, PW>(p, J, kblk, lane, frag);
+  }
+  if (PW) {  // the last iteration: the dS waves' last tile
+    wait_vmcnt<0>();
+    lds_barrier();
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_chain_kernel(BwdArgs p) {
+  constexpr int SE = DkdvStage<D>::ELEMS, PE = DkdvStage<D>::PELEMS;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[kDkdvStages * SE];
+  __shared__ __attribute__((aligned(16))) uint16_t sPbuf[2 * PE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kblk = wave & 3;
+  uint16_t* myP = sPbuf + kblk * (PE / 4);  // this key block's part of each P buffer
+  if (wave < 4)
+    dkdv_chain<D, true>(p, smem, myP, kblk, wave, lane);
+  else
+    dkdv_chain<D, false>(p, smem, myP, kblk, wave, lane);
 }
 
 // ------------------------------------------------------------------------------------- launchers
@@ -728,15 +940,18 @@ static hipError_t launch_dkdv_d(const BwdArgs& a, hipStream_t s) {
   p.paired = (p.cu == nullptr && p.window >= p.T) ? 1 : 0;
   const unsigned per_head = p.paired ? (unsigned)(p.n_tiles + 1) / 2 : (unsigned)p.n_tiles;
   const unsigned grid = per_head * (unsigned)p.BH;
-  if (p.cu)
+  if (p.cu) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false>), dim3(grid), dim3(64 * kDkdvWaves), 0, s,
                        p);
-  else if (p.rk)
+  } else if (p.rk) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true>), dim3(grid), dim3(64 * kDkdvWaves), 0, s,
                        p);
-  else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false>), dim3(grid), dim3(64 * kDkdvWaves), 0, s,
-                       p);
+  } else {
+    // persistent: one workgroup per CU, each chaining its share of the units
+    const unsigned cus = (unsigned)device_compute_units();
+    const unsigned pgrid = cus > 0 && cus < grid ? cus : grid;
+    hipLaunchKernelGGL((bwd_dkdv_chain_kernel<D>), dim3(pgrid), dim3(64 * kDkdvWaves), 0, s, p);
+  }
   return hipGetLastError();
 }
 
