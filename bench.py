@@ -485,7 +485,7 @@ def main() -> int:
     kernels = {
         "fwd_bf16_kernel": ("d20 forward", F_fwd, t_fwd),
         "bwd_dq_kernel": ("d20 dQ pass", F_dq_credit, t_dq),
-        "bwd_dkdv_kernel": ("d20 dK/dV pass", F_dkdv_credit, t_dkdv),
+        "bwd_dkdv_chain_kernel": ("d20 dK/dV pass", F_dkdv_credit, t_dkdv),
     }
     dom = max(kernels, key=lambda n: kernels[n][2])
     dom_label, f_dom, t_dom = kernels[dom]
