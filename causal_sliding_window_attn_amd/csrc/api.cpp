@@ -121,7 +121,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 
 size_t attn_bwd_workspace_bytes(int B, int H, int T, int D) {
   if (B < 1 || H < 1 || T < 1 || (D != 64 && D != 128)) return 0;
-  return 2 * align256((size_t)B * H * T * sizeof(float));  // Delta, then LSE in base 2
+  // Delta, then LSE in base 2, then the packed-sequence dK/dV pass's job queue counter and plan
+  return 2 * align256((size_t)B * H * T * sizeof(float)) + 256 +
+         align256((size_t)swattn::kDkdvPlanMax * sizeof(int));
 }
 
 }  // extern "C"
@@ -163,8 +165,10 @@ int bwd_common(const char* what, BwdPass pass, const void* q, const void* k, con
   a.dq = static_cast<uint16_t*>(dq);
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
+  const size_t rows_bytes = align256((size_t)B * H * T * sizeof(float));
   a.delta = static_cast<float*>(ws);
-  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + need / 2);
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + rows_bytes);
+  a.qctr = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + 2 * rows_bytes);
   a.bstride = (int64_t)T * H * D;
   a.row_stride = H * D;
   a.H = H;
@@ -502,8 +506,13 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
   a.dq = static_cast<uint16_t*>(dq);
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
+  const size_t rows_bytes = align256((size_t)H * total * sizeof(float));
   a.delta = static_cast<float*>(ws);
-  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + need / 2);
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + rows_bytes);
+  a.qctr = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + 2 * rows_bytes);
+  a.plan = swattn::dkdv_plan_fits(nseq, total, max_seqlen)
+               ? reinterpret_cast<int*>(static_cast<char*>(ws) + 2 * rows_bytes + 256)
+               : nullptr;
   a.cu = cu_seqlens;
   a.total = total;
   a.row_stride = H * D;

@@ -310,12 +310,50 @@ __device__ __forceinline__ void dq_job(const BwdArgs& p, int bh, int qt, uint16_
     }
 }
 
+// Packed sequences: the dK/dV pass's job plan (layout in launch.h) and its queue counter, set by
+// workgroup 0 of the dQ pass before its own job.  Level kt lists the sequences with more than kt
+// 128-key tiles, in sequence order: wave 0 walks the levels, 64 sequences per step, and a ballot
+// gives each its place.  `nd` is LDS for one int per sequence.
+template <int D>
+__device__ void dkdv_build_plan(const BwdArgs& p, int* nd) {
+  const int nseq = p.BH / p.H, levels = (p.T + 127) / 128;
+  for (int d = threadIdx.x; d < nseq; d += blockDim.x)
+    nd[d] = (bwd_rows<true>(p, d, 0, D).T + 127) / 128;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int run = 0;
+    // entries beyond the capacity (possible only when cu's ranges overlap, which the host's
+    // bound does not foresee) are dropped, and the offsets clamped, so that no read or write of
+    // the plan leaves it
+    const int cap = kDkdvPlanMax - levels - 1;
+    for (int kt = 0; kt < levels; ++kt) {
+      if (lane == 0) p.plan[kt] = min(run, cap);
+      for (int c0 = 0; c0 < nseq; c0 += 64) {
+        const int d = c0 + lane;
+        const bool in = d < nseq && nd[d] > kt;
+        const uint64_t m = __ballot(in);
+        const int pos = run + __popcll(m & ((1ull << lane) - 1));
+        if (in && pos < cap) p.plan[levels + 1 + pos] = d;
+        run += __popcll(m);
+      }
+    }
+    if (lane == 0) {
+      p.plan[levels] = min(run, cap);
+      *p.qctr = 0u;
+    }
+  }
+  __syncthreads();  // the caller reuses the LDS
+}
+
 // Full-causal training pass (p.paired): workgroup = head + query-tile pair (j, n - 1 - j), short
 // tile first (pair_job).  Otherwise: workgroup = one query tile, longest tiles first.
 template <int D, int NW, bool VARLEN, bool QKN>
 __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs p) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * kBwdBC * D];  // [stage][K|V]
   const int tid = threadIdx.x;
+  if (VARLEN && p.plan && blockIdx.x == 0)  // the dK/dV pass's job plan, before this job
+    dkdv_build_plan<D>(p, reinterpret_cast<int*>(smem));
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bid = blockIdx.x;
   int bh, qt0, qt1, njobs;
@@ -495,7 +533,7 @@ __device__ __forceinline__ void dkdv_swave(const uint16_t* __restrict__ cur,
   }
 }
 
-// One iteration: DMA of tile qt_next into `nxt`, then a P wave on `curp` (tile qt_p) or a dS wave
+// One iteration: DMA of tile qt_next (of a sequence of T_next rows) into `nxt`, then a P wave on `curp` (tile qt_p) or a dS wave
 // on `curs` (tile qt_s, the P waves' tile of the previous iteration).  The __restrict__ qualifiers
 // state that, within one iteration, the three stages and the two P buffers are distinct, so LDS
 // reads need not wait for the DMA.
@@ -506,14 +544,14 @@ __device__ __forceinline__ void dkdv_step(const uint16_t* __restrict__ curp,
                                           const uint16_t* __restrict__ pr, bool issue_next,
                                           bool on, const uint16_t* qb, const uint16_t* db,
                                           const float* lseb, const float* delb, int rs, int qt_p,
-                                          int qt_s, int qt_next, int ka, int kj, int T, int w,
-                                          float sl2, const uint4 (&frag)[D / 16],
+                                          int qt_s, int qt_next, int T_next, int ka, int kj, int T,
+                                          int w, float sl2, const uint4 (&frag)[D / 16],
                                           f32x16 (&acc)[D / 32], f32x16 (&acc2)[D / 32],
                                           const LdsOffsets<D>& lo,
                                           const RowDmaFlat<D, kDkdvDmaWaves, kBwdBQ>& dma, int wave,
                                           int lane) {
   if (issue_next)
-    dkdv_issue<D, kDkdvDmaWaves>(dma, qb, db, lseb, delb, rs, qt_next, T, nxt, wave, lane);
+    dkdv_issue<D, kDkdvDmaWaves>(dma, qb, db, lseb, delb, rs, qt_next, T_next, nxt, wave, lane);
   if (!on) return;
   if (PW)
     dkdv_pwave<D>(curp, pw, qt_p, ka, kj, T, w, sl2, frag, lo, lane);
@@ -545,8 +583,8 @@ __device__ __forceinline__ void dkdv_loop(uint16_t* smem, uint16_t* myP, int qt_
     const int pb = (i & 1) * PE;
     const int qt = qt_hi - i;
     dkdv_step<D, NW, PW>(smem + s0, smem + s1, smem + s2, myP + pb, myP + (PE - pb), i + 1 < n,
-                         PW ? (i < n) : (i >= 1), qb, db, lseb, delb, rs, qt, qt + 1, qt - 1, ka,
-                         kj, T, w, sl2, frag, acc, acc2, lo, dma, wave, lane);
+                         PW ? (i < n) : (i >= 1), qb, db, lseb, delb, rs, qt, qt + 1, qt - 1, T,
+                         ka, kj, T, w, sl2, frag, acc, acc2, lo, dma, wave, lane);
     const int t = s1;  // rotate: the stage just read one behind becomes the next DMA target
     s1 = s0;
     s0 = s2;
@@ -669,7 +707,8 @@ __device__ __forceinline__ void dkdv_job(const BwdArgs& p, int bh, int kt, uint1
     }
 }
 
-// One workgroup per unit (packed documents and QK-norm launches): full-causal training pass
+// One workgroup per unit (QK-norm launches, and packed launches whose job plan would not fit):
+// full-causal training pass
 // (p.paired): workgroup = head + key-tile pair (n - 1 - j, j), the short tile (fewest queries)
 // first, so that a head's workgroups start on the same query tiles together (pair_job).
 // Otherwise: workgroup = one key tile, those seeing the most queries first.
@@ -701,63 +740,154 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs p)
 }
 
 // ------------------------------------------------------------------------ dK/dV, chained jobs
-// Dense launches (no packed documents, no QK-norm) run the dK/dV pass on a persistent grid, one
+// Dense and packed-sequence launches (not QK-norm) run the dK/dV pass on a persistent grid, one
 // workgroup per CU (a workgroup fills a CU: 8 waves at up to 256 VGPRs, 132 KB of LDS).  Each
-// walks a fixed list of jobs whose query tiles form one stream through the ring and the P
-// buffers, so the P waves start a job's first tile while the dS waves finish the previous job's
-// last one: no pipeline fill or drain and no start-up per job.  The P waves load the next job's K
-// right after their last tile of the current one; the dS waves store dK and dV and load the next
-// job's V right after theirs.
+// walks a list of jobs whose query tiles form one stream through the ring and the P buffers, so
+// the P waves start a job's first tile while the dS waves finish the previous job's last one: no
+// pipeline fill or drain and no start-up per job.  The P waves load the next job's K right after
+// their last tile of the current one; the dS waves store dK and dV and load the next job's V
+// right after theirs.
 //
-// Units blockIdx.x, blockIdx.x + gridDim.x, ...: paired (full causal), unit u is the tile pair
-// pair_job(u) (key tiles n - 1 - j, then j); otherwise unit u is key tile u / BH of head u % BH.
+// Units: paired (full causal), unit u is the tile pair pair_job(u) (key tiles n - 1 - j, then j);
+// otherwise unit u is key tile u / BH of head u % BH (of sequence u % BH / H when packed; tiles
+// past that sequence's end are empty).
+//   dense: workgroup w takes units w, w + G, w + 2G, ... (G workgroups; every unit carries about
+//     the same work);
+//   packed: jobs differ widely in work (and most units lie past their sequence's end), so the live
+//     jobs are handed out one at a time from a queue, longest first: the dQ pass leaves a plan
+//     listing, per 128-key level, the sequences long enough for it; queue index i maps through
+//     the plan (held in LDS) to a job; workgroup w's first job is index w, the others come from
+//     an atomic counter in the workspace.  Wave 0 takes the jobs and publishes them two ahead in
+//     an LDS ring that both roles read, each entry behind at least one barrier.
 struct DkdvJob {
   int bh, kt;
+  int T;             // rows of the sequence
   int qt_hi, qt_lo;  // the query tiles that see key tile kt, walked from qt_hi down
+  int64_t base;      // element offset of the sequence's row 0 at the head
+  int64_t stat;      // index of its row 0 in LSE * log2(e) and Delta
 };
 
-// Job s (0 or 1) of unit u; false (jb untouched) if there is none.
-__device__ __forceinline__ bool dkdv_unit_job(const BwdArgs& p, int u, int s, DkdvJob& jb) {
+constexpr int kDkdvRing = 8;  // published jobs in LDS
+
+// Key tile kt of head bh; false if it lies past the end of the head's sequence.
+template <int D, bool VARLEN>
+__device__ __forceinline__ bool dkdv_make_job(const BwdArgs& p, int bh, int kt, DkdvJob& jb) {
+  const BwdRows rw = bwd_rows<VARLEN>(p, bh / p.H, bh % p.H, D);
+  const int k0 = kt * 128;
+  if (k0 >= rw.T) return false;
+  const int w = min(p.window, rw.T);
+  jb.bh = bh;
+  jb.kt = kt;
+  jb.T = rw.T;
+  jb.qt_lo = k0 / kBwdBQ;
+  jb.qt_hi = (min(rw.T, k0 + 127 + w) - 1) / kBwdBQ;
+  jb.base = rw.base;
+  jb.stat = rw.stat;
+  return true;
+}
+
+// Dense jobs: job s (0 or 1) of unit u.  kDkdvLive: jb set; kDkdvEmpty: no such job; kDkdvEnd: u is
+// past the last unit.
+enum { kDkdvEnd, kDkdvEmpty, kDkdvLive };
+template <int D>
+__device__ __forceinline__ int dkdv_unit_job(const BwdArgs& p, int u, int s, DkdvJob& jb) {
   const int n = p.n_tiles;
   int bh, kt;
   if (p.paired) {
     const int npair = (n + 1) / 2;
-    if (u >= p.BH * npair) return false;
+    if (u >= p.BH * npair) return kDkdvEnd;
     const PairJob pj = pair_job(u, p.BH, npair);
     const int kt0 = n - 1 - pj.j;
-    if (s == 1 && pj.j == kt0) return false;
+    if (s == 1 && pj.j == kt0) return kDkdvEmpty;
     bh = pj.bh;
     kt = s ? pj.j : kt0;
   } else {
-    if (s != 0 || u >= n * p.BH) return false;
+    if (u >= n * p.BH) return kDkdvEnd;
+    if (s != 0) return kDkdvEmpty;
     bh = u % p.BH;
     kt = u / p.BH;
   }
-  const int k0 = kt * 128, w = min(p.window, p.T);
-  jb.bh = bh;
-  jb.kt = kt;
-  jb.qt_lo = k0 / kBwdBQ;
-  jb.qt_hi = (min(p.T, k0 + 127 + w) - 1) / kBwdBQ;
+  return dkdv_make_job<D, false>(p, bh, kt, jb) ? kDkdvLive : kDkdvEmpty;
+}
+
+// The job source of one workgroup.  Dense: a cursor over its units.  Packed: the queue (wave 0
+// only) and the LDS ring.
+struct DkdvSource {
+  int u, s;       // dense: unit and job within it of the last job taken
+  unsigned pend;  // packed, wave 0 lane 0: the queue index taken for the next job to publish
+  int taken;      // packed: jobs published so far
+};
+
+// Packed: unit (kt * BH + bh) of queue index `idx` under the plan in LDS, or -1 past the last job.
+// Index order: level by level (longest jobs first), sequences in order, heads innermost.
+__device__ __forceinline__ int dkdv_plan_unit(const BwdArgs& p, const int* plan, int levels,
+                                              int idx) {
+  if (idx >= p.H * plan[levels]) return -1;
+  int lo = 0, hi = levels - 1;  // the last level whose first index is <= idx (it is not empty)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.H * plan[mid] <= idx) lo = mid;
+    else hi = mid - 1;
+  }
+  const int r = idx - p.H * plan[lo];
+  const int seq = plan[levels + 1 + plan[lo] + r / p.H];
+  return lo * p.BH + seq * p.H + r % p.H;
+}
+
+// Packed: publishes the workgroup's next job (wave 0 writes the ring).  The workgroup's first job
+// is queue index blockIdx.x; the others come from the counter, each taken one publication before
+// it is used, so that the atomic's latency passes under a job.
+__device__ __forceinline__ void dkdv_publish(const BwdArgs& p, DkdvSource& src, const int* plan,
+                                             int levels, int* ring, int wave, int lane) {
+  if (wave == 0) {
+    const int idx = src.taken == 0
+                        ? (int)blockIdx.x
+                        : (int)(gridDim.x + __builtin_amdgcn_readfirstlane(src.pend));
+    unsigned nx = 0;
+    if (lane == 0) nx = atomicAdd(p.qctr, 1u);
+    src.pend = nx;
+    const int u = dkdv_plan_unit(p, plan, levels, idx);
+    if (lane == 0) ring[src.taken % kDkdvRing] = u;
+  }
+  ++src.taken;
+}
+
+// Packed: the job of published entry k; false at the end of the list.
+template <int D>
+__device__ __forceinline__ bool dkdv_ring_job(const BwdArgs& p, const int* ring, int k,
+                                              DkdvJob& jb) {
+  const int u = __builtin_amdgcn_readfirstlane(ring[k % kDkdvRing]);
+  if (u < 0) return false;
+  dkdv_make_job<D, true>(p, u % p.BH, u / p.BH, jb);  // live by the plan's construction
   return true;
 }
 
-// A position in the workgroup's job list (wave-uniform): unit u, job s of it.
-struct DkdvCursor {
-  int u, s;
-};
+// Dense: the job after the cursor's (the cursor moves to it); false past the last.
+template <int D>
+__device__ __forceinline__ bool dkdv_dense_next(const BwdArgs& p, DkdvSource& c, DkdvJob& jb) {
+  while (true) {
+    if (c.s == 0) {
+      c.s = 1;
+    } else {
+      c.s = 0;
+      c.u += gridDim.x;
+    }
+    const int r = dkdv_unit_job<D>(p, c.u, c.s, jb);
+    if (r != kDkdvEmpty) return r == kDkdvLive;
+  }
+}
 
 // The B fragments of a job: K for the P waves, -V for the dS waves (rows past T zero).
 template <int D, bool PW>
 __device__ __forceinline__ void dkdv_load_frag(const BwdArgs& p, const DkdvJob& jb, int kblk,
                                                int lane, uint4 (&frag)[D / 16]) {
   const int half = lane >> 5, l32 = lane & 31;
-  const int b = jb.bh / p.H, h = jb.bh % p.H;
   const int kj = jb.kt * 128 + 32 * kblk + l32;
-  const uint16_t* src = (PW ? p.k : p.v) + (int64_t)b * p.bstride + h * D +
-                        (int64_t)min(kj, p.T - 1) * p.row_stride + 8 * half;
+  const uint16_t* src = (PW ? p.k : p.v) + jb.base + (int64_t)min(kj, jb.T - 1) * p.row_stride +
+                        8 * half;
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) frag[t] = ldg16(src + 16 * t);
-  if (kj >= p.T)
+  if (kj >= jb.T)
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) frag[t] = make_uint4(0, 0, 0, 0);
   if (!PW)
@@ -777,9 +907,8 @@ __device__ __forceinline__ void dkdv_store(const BwdArgs& p, const DkdvJob& jb, 
                                            const f32x16 (&dvacc)[D / 32]) {
   const int half = lane >> 5, l32 = lane & 31;
   const int kj = jb.kt * 128 + 32 * kblk + l32;
-  if (kj >= p.T) return;
-  const int b = jb.bh / p.H, h = jb.bh % p.H;
-  const int64_t row = (int64_t)b * p.bstride + h * D + (int64_t)kj * p.row_stride + 4 * half;
+  if (kj >= jb.T) return;
+  const int64_t row = jb.base + (int64_t)kj * p.row_stride + 4 * half;
   const float sc = -p.scale;
 #pragma unroll
   for (int m = 0; m < D / 32; ++m)
@@ -795,48 +924,52 @@ __device__ __forceinline__ void dkdv_store(const BwdArgs& p, const DkdvJob& jb, 
     }
 }
 
-// The job after the cursor's (the cursor moves to it); false past the workgroup's last.
-__device__ __forceinline__ bool dkdv_next_job(const BwdArgs& p, DkdvCursor& c, DkdvJob& jb) {
-  if (c.s == 0 && dkdv_unit_job(p, c.u, 1, jb)) {
-    c.s = 1;
-    return true;
-  }
-  c.u += gridDim.x;
-  c.s = 0;
-  return dkdv_unit_job(p, c.u, 0, jb);
-}
-
-// Rows of a job's head: Q, dO (element offsets) and LSE * log2(e), Delta.
+// Rows of a job's sequence at its head: Q, dO and LSE * log2(e), Delta.
 struct DkdvRows {
   const uint16_t *q, *dout;
   const float *lse2, *delta;
 };
-template <int D>
 __device__ __forceinline__ DkdvRows dkdv_rows(const BwdArgs& p, const DkdvJob& jb) {
-  const int b = jb.bh / p.H, h = jb.bh % p.H;
-  const int64_t base = (int64_t)b * p.bstride + h * D, stat = (int64_t)jb.bh * p.T;
-  return {p.q + base, p.dout + base, p.lse2 + stat, p.delta + stat};
+  return {p.q + jb.base, p.dout + jb.base, p.lse2 + jb.stat, p.delta + jb.stat};
 }
 
 // One role's walk over the workgroup's jobs.  Global iteration g runs the P waves on stream tile
-// g and the dS waves on tile g - 1, one barrier each (tiles + 1 in all for both roles): the P
-// waves idle in the last iteration, the dS waves in the first.  Within a job the tile loop is
-// the single-job loop's; between jobs the P waves load the next K, the dS waves store dK and dV
-// and load the next -V.
-template <int D, bool PW>
+// g and the dS waves on tile g - 1, one barrier each (tiles + 1 in all for both roles, plus one
+// before the walk when packed): the P waves idle in the last iteration, the dS waves in the
+// first.  Within a job the tile loop is the single-job loop's; between jobs the P waves load the
+// next K, the dS waves store dK and dV and load the next -V.  A workgroup without a job passes no
+// further barrier, in both roles.
+template <int D, bool VARLEN, bool PW>
 __device__ __forceinline__ void dkdv_chain(const BwdArgs& p, uint16_t* smem, uint16_t* myP,
-                                           int kblk, int wave, int lane) {
+                                           int* ring, int* plan, int kblk, int wave, int lane) {
   constexpr int BQ = kBwdBQ, MB = D / 32;
   constexpr int SE = DkdvStage<D>::ELEMS, PE = DkdvStage<D>::PELEMS;
   const int l32 = lane & 31;
-  const int w = min(p.window, p.T), rs = p.row_stride;
+  const int rs = p.row_stride;
   const LdsOffsets<D> lo(lane);
   const RowDmaFlat<D, kDkdvDmaWaves, BQ> dma(rs, wave, lane);
-  DkdvCursor c{(int)blockIdx.x, 0};
-  DkdvJob J;
-  dkdv_unit_job(p, c.u, 0, J);  // the launch has no more workgroups than units
-  DkdvJob N = J;
-  bool hasN = dkdv_next_job(p, c, N);
+  DkdvSource src{(int)blockIdx.x, 0, 0u, 0};
+  DkdvJob J, N;
+  bool hasN;
+  const int levels = p.n_tiles;
+  if constexpr (VARLEN) {
+    // the plan into LDS, then jobs 0 and 1 published before the walk
+    const int nplan = min(levels + 1 + p.plan[levels], kDkdvPlanMax);
+    for (int i = threadIdx.x; i < nplan; i += blockDim.x) plan[i] = p.plan[i];
+    __syncthreads();
+    dkdv_publish(p, src, plan, levels, ring, wave, lane);
+    dkdv_publish(p, src, plan, levels, ring, wave, lane);
+    __syncthreads();
+    if (!dkdv_ring_job<D>(p, ring, 0, J)) return;
+    N = J;
+    hasN = dkdv_ring_job<D>(p, ring, 1, N);
+  } else {
+    const int r = dkdv_unit_job<D>(p, src.u, 0, J);
+    if (r != kDkdvLive) return;  // the launch has no more workgroups than units
+    N = J;
+    hasN = dkdv_dense_next<D>(p, src, N);
+  }
+  int k = 0;  // the job in hand (packed: its ring entry)
   uint4 frag[D / 16];
   dkdv_load_frag<D, PW>(p, J, kblk, lane, frag);
   f32x16 acc[MB], acc2[MB];  // dS waves: dK^T, dV^T
@@ -852,8 +985,8 @@ __device__ __forceinline__ void dkdv_chain(const BwdArgs& p, uint16_t* smem, uin
     ++g;
   };
   if (PW) {
-    DkdvRows rj = dkdv_rows<D>(p, J);
-    dkdv_issue<D, kDkdvDmaWaves>(dma, rj.q, rj.dout, rj.lse2, rj.delta, rs, J.qt_hi, p.T, smem,
+    const DkdvRows rj = dkdv_rows(p, J);
+    dkdv_issue<D, kDkdvDmaWaves>(dma, rj.q, rj.dout, rj.lse2, rj.delta, rs, J.qt_hi, J.T, smem,
                                  wave, lane);
   } else {
     lds_barrier();  // iteration 0: the P waves' first tile
@@ -861,8 +994,13 @@ __device__ __forceinline__ void dkdv_chain(const BwdArgs& p, uint16_t* smem, uin
   }
 #pragma unroll 1
   while (true) {
-    const DkdvRows rj = dkdv_rows<D>(p, J);
+    // packed: wave 0 publishes job k + 2 before job k's tiles (their barriers order the write
+    // before any read of it: job k + 1's, at the earliest)
+    if (VARLEN && PW) dkdv_publish(p, src, plan, levels, ring, wave, lane);
+    const DkdvRows rj = dkdv_rows(p, J);
     const int ka = J.kt * 128 + 32 * kblk, n = J.qt_hi - J.qt_lo + 1;
+    const int TJ = VARLEN ? J.T : p.T, TN = VARLEN ? N.T : p.T;  // dense: every job has T rows
+    const int w = min(p.window, TJ);
 #pragma unroll 1
     for (int i = 0; i < n; ++i) {
       // tile g (the only DMA in flight) has landed: the P waves issued it and wait for it; then
@@ -871,11 +1009,12 @@ __device__ __forceinline__ void dkdv_chain(const BwdArgs& p, uint16_t* smem, uin
       lds_barrier();
       const int pb = (g & 1) * PE, qt = J.qt_hi - i;
       const bool last = i == n - 1;  // the next stream tile is the next job's first
-      const DkdvRows rx = last && hasN ? dkdv_rows<D>(p, N) : rj;
+      const DkdvRows rx = last && hasN ? dkdv_rows(p, N) : rj;
       dkdv_step<D, kDkdvWaves, PW>(smem + s0, smem + s1, smem + s2, myP + pb, myP + (PE - pb),
                                    PW && (!last || hasN), true, rx.q, rx.dout, rx.lse2, rx.delta,
-                                   rs, qt, qt, last ? N.qt_hi : qt - 1, ka, ka + l32, p.T, w,
-                                   p.scale_log2, frag, acc, acc2, lo, dma, wave, lane);
+                                   rs, qt, qt, last ? N.qt_hi : qt - 1, last ? TN : TJ, ka,
+                                   ka + l32, TJ, w, p.scale_log2, frag, acc, acc2, lo, dma, wave,
+                                   lane);
       rotate();
     }
     if (!PW) {
@@ -885,7 +1024,9 @@ __device__ __forceinline__ void dkdv_chain(const BwdArgs& p, uint16_t* smem, uin
     }
     if (!hasN) break;
     J = N;
-    hasN = dkdv_next_job(p, c, N);
+    ++k;
+    if constexpr (VARLEN) hasN = dkdv_ring_job<D>(p, ring, k + 1, N);
+    else hasN = dkdv_dense_next<D>(p, src, N);
     dkdv_load_frag<D, PW>(p, J, kblk, lane, frag);
   }
   if (PW) {  // the last iteration: the dS waves' last tile
@@ -894,19 +1035,21 @@ __device__ __forceinline__ void dkdv_chain(const BwdArgs& p, uint16_t* smem, uin
   }
 }
 
-template <int D>
+template <int D, bool VARLEN>
 __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_chain_kernel(BwdArgs p) {
   constexpr int SE = DkdvStage<D>::ELEMS, PE = DkdvStage<D>::PELEMS;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[kDkdvStages * SE];
   __shared__ __attribute__((aligned(16))) uint16_t sPbuf[2 * PE];
+  __shared__ int ring[VARLEN ? kDkdvRing : 1];       // packed: the workgroup's published jobs
+  __shared__ int plan[VARLEN ? kDkdvPlanMax : 1];    // packed: the job plan
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kblk = wave & 3;
   uint16_t* myP = sPbuf + kblk * (PE / 4);  // this key block's part of each P buffer
   if (wave < 4)
-    dkdv_chain<D, true>(p, smem, myP, kblk, wave, lane);
+    dkdv_chain<D, VARLEN, true>(p, smem, myP, ring, plan, kblk, wave, lane);
   else
-    dkdv_chain<D, false>(p, smem, myP, kblk, wave, lane);
+    dkdv_chain<D, VARLEN, false>(p, smem, myP, ring, plan, kblk, wave, lane);
 }
 
 // ------------------------------------------------------------------------------------- launchers
@@ -940,18 +1083,26 @@ static hipError_t launch_dkdv_d(const BwdArgs& a, hipStream_t s) {
   p.paired = (p.cu == nullptr && p.window >= p.T) ? 1 : 0;
   const unsigned per_head = p.paired ? (unsigned)(p.n_tiles + 1) / 2 : (unsigned)p.n_tiles;
   const unsigned grid = per_head * (unsigned)p.BH;
-  if (p.cu) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false>), dim3(grid), dim3(64 * kDkdvWaves), 0, s,
-                       p);
-  } else if (p.rk) {
+  if (p.rk) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true>), dim3(grid), dim3(64 * kDkdvWaves), 0, s,
                        p);
-  } else {
-    // persistent: one workgroup per CU, each chaining its share of the units
-    const unsigned cus = (unsigned)device_compute_units();
-    const unsigned pgrid = cus > 0 && cus < grid ? cus : grid;
-    hipLaunchKernelGGL((bwd_dkdv_chain_kernel<D>), dim3(pgrid), dim3(64 * kDkdvWaves), 0, s, p);
+    return hipGetLastError();
   }
+  if (p.cu && !p.plan) {  // packed, with more sequences or jobs than a plan holds
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false>), dim3(grid), dim3(64 * kDkdvWaves), 0, s,
+                       p);
+    return hipGetLastError();
+  }
+  // persistent: one workgroup per CU, each chaining its share of the units (packed: of the jobs
+  // of the plan; workgroups beyond the number of jobs leave at once)
+  const unsigned cus = (unsigned)device_compute_units();
+  const unsigned pgrid = cus > 0 && cus < grid ? cus : grid;
+  if (p.cu)
+    hipLaunchKernelGGL((bwd_dkdv_chain_kernel<D, true>), dim3(pgrid), dim3(64 * kDkdvWaves), 0, s,
+                       p);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_chain_kernel<D, false>), dim3(pgrid), dim3(64 * kDkdvWaves), 0, s,
+                       p);
   return hipGetLastError();
 }
 

@@ -45,6 +45,9 @@ struct BwdArgs {
   uint16_t* dv;
   float* delta;      // [BH, T] workspace: Delta_i = dO_i . O_i (written by the dQ pass)
   float* lse2;       // [BH, T] workspace: LSE_i * log2(e) (written by the dQ pass)
+  unsigned* qctr;    // workspace: packed sequences' dK/dV job queue counter
+  int* plan;         // workspace: packed sequences' dK/dV job plan (built by the dQ pass), or
+                     // null (the dK/dV pass then runs one workgroup per unit)
   const int* cu;     // packed sequences (rows cu[b] .. cu[b + 1] - 1 of [total, H, D]; lse,
                      // Delta and LSE * log2(e) as [H, total]), or null; T is then the longest
   int total;         // packed sequences: rows in q / k / v / o / dO
@@ -111,6 +114,21 @@ constexpr int kDecodeFusedMaxRows = 2048;
 inline bool decode_uses_fused(int B, int H, int Lcap, int window) {
   const int visible = window < Lcap ? window : Lcap;
   return (long long)B * H >= kDecodeFusedMinPairs || visible <= kDecodeFusedMaxRows;
+}
+
+// Packed sequences' dK/dV job plan: for every 128-key level kt (key tile kt of a sequence), the
+// sequences long enough to have that tile, in sequence order.  Laid out as C[0 .. levels] (C[kt]:
+// entries before level kt), then the entries (sequence indices).  Used only when it surely fits
+// kDkdvPlanMax ints (the dK/dV workgroups hold it in LDS) and there are at most kDkdvPlanSeqs
+// sequences (the dQ pass builds it in LDS).
+constexpr int kDkdvPlanMax = 6144;
+constexpr int kDkdvPlanSeqs = 8192;
+inline bool dkdv_plan_fits(long long nseq, long long total, long long max_seqlen) {
+  const long long levels = (max_seqlen + 127) / 128;
+  long long entries = nseq * levels;  // at most: every nonempty sequence adds one per 128 rows
+  const long long by_rows = total / 128 + (nseq < total ? nseq : total);
+  if (by_rows < entries) entries = by_rows;
+  return nseq <= kDkdvPlanSeqs && levels + 1 + entries <= kDkdvPlanMax;
 }
 
 // Static scratch of the allocation-free decode step (attn_decode_step_noalloc): the split

@@ -77,7 +77,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
              int D, int window, int dtype, void* stream);
 
 /* Bytes of device workspace attn_bwd needs: per row, Delta_i = dO_i . O_i and LSE_i * log2(e)
- * (float32 each), written by the dQ pass and read by the dK/dV pass. */
+ * (float32 each), written by the dQ pass and read by the dK/dV pass, and a fixed 24.25 KiB for the
+ * packed-sequence dK/dV pass's job queue and plan. */
 size_t attn_bwd_workspace_bytes(int B, int H, int T, int D);
 
 /*

@@ -661,6 +661,36 @@ def test_varlen_is_each_document_alone_bit_for_bit(sw):
                 assert torch.equal(x[sl], y[0]), (window, a)
 
 
+@pytest.mark.parametrize("case", ["queue", "fallback"])
+def test_varlen_many_documents(sw, case):
+    """Many packed documents. queue: 600 documents of 0-300 tokens (about 1200 dK/dV jobs per
+    head, far more than workgroups, handed out by the pass's job queue); fallback: 6200 documents
+    of 0-3 tokens, too many for the job plan, so the dK/dV pass runs one workgroup per unit.
+    Forward and backward against the oracle, and a second run equal bit for bit."""
+    rng = np.random.default_rng(131 if case == "queue" else 132)
+    if case == "queue":
+        lengths, H, windows = rng.integers(0, 301, 600).tolist(), 2, (None, 50)
+    else:
+        lengths, H, windows = rng.integers(0, 4, 6200).tolist(), 1, (None,)
+    D = 64
+    cu, q, k, v, do = _packed(lengths, H, D, 133)
+    qd, kd, vd, dod, cud = (t.to(DEV) for t in (q, k, v, do, cu))
+    ms = max(lengths)
+    for window in windows:
+        o, lse = sw.attn_fwd_varlen(qd, kd, vd, cud, ms, window=window)
+        g = sw.attn_bwd_varlen(qd, kd, vd, o, lse, dod, cud, ms, window=window)
+        g2 = sw.attn_bwd_varlen(qd, kd, vd, o, lse, dod, cud, ms, window=window)
+        torch.cuda.synchronize()
+        for a, b in zip(g, g2):
+            assert torch.equal(a, b), f"{case} window {window}: second run differs"
+        o_r, lse_r = ref.forward_varlen(f64(q), f64(k), f64(v), cu.numpy(), window)
+        assert_o(f64(o), o_r, f"{case} window {window}")
+        assert np.abs(f64(lse) - lse_r).max() <= LSE_TOL, f"{case} window {window}"
+        g_r = ref.backward_varlen(f64(q), f64(k), f64(v), f64(do), cu.numpy(), window)
+        check_grads(g, g_r, tag=f"varlen {case} window {window}",
+                    zero_bounds=zero_grad_bounds(f64(q), f64(k), f64(v), f64(do)) + (0.0,))
+
+
 def test_varlen_autograd_and_rows_past_max_seqlen(sw):
     lengths = [40, 90, 7]
     H, D = 2, 64
