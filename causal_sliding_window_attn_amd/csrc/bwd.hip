@@ -1017,6 +1017,9 @@ __device__ __forceinline__ void dkdv_chain(const BwdArgs& p, uint16_t* smem, uin
                                    lane);
       rotate();
     }
+    // the next job's fragments are loaded before this job's dK / dV stores are issued: a wait
+    // for the loads then need not wait for the stores (vector memory counts them in order)
+    if (hasN) dkdv_load_frag<D, PW>(p, N, kblk, lane, frag);
     if (!PW) {
       dkdv_store<D>(p, J, kblk, lane, acc, acc2);
 #pragma unroll
@@ -1027,7 +1030,6 @@ __device__ __forceinline__ void dkdv_chain(const BwdArgs& p, uint16_t* smem, uin
     ++k;
     if constexpr (VARLEN) hasN = dkdv_ring_job<D>(p, ring, k + 1, N);
     else hasN = dkdv_dense_next<D>(p, src, N);
-    dkdv_load_frag<D, PW>(p, J, kblk, lane, frag);
   }
   if (PW) {  // the last iteration: the dS waves' last tile
     wait_vmcnt<0>();
