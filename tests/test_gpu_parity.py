@@ -661,17 +661,19 @@ def test_varlen_is_each_document_alone_bit_for_bit(sw):
                 assert torch.equal(x[sl], y[0]), (window, a)
 
 
-@pytest.mark.parametrize("case", ["queue", "fallback"])
+@pytest.mark.parametrize("case", ["queue", "full_plan", "fallback"])
 def test_varlen_many_documents(sw, case):
     """Many packed documents. queue: 600 documents of 0-300 tokens (about 1200 dK/dV jobs per
-    head, far more than workgroups, handed out by the pass's job queue); fallback: 6200 documents
-    of 0-3 tokens, too many for the job plan, so the dK/dV pass runs one workgroup per unit.
-    Forward and backward against the oracle, and a second run equal bit for bit."""
-    rng = np.random.default_rng(131 if case == "queue" else 132)
+    head, far more than workgroups, handed out by the pass's job queue); full_plan: 6000
+    documents of 0-3 tokens, a job plan of 6002 of its 6144 entries; fallback: 6200 such
+    documents, too many for the plan, so the dK/dV pass runs one workgroup per unit.  Forward
+    and backward against the oracle, and a second run equal bit for bit."""
+    rng = np.random.default_rng({"queue": 131, "full_plan": 134, "fallback": 132}[case])
     if case == "queue":
         lengths, H, windows = rng.integers(0, 301, 600).tolist(), 2, (None, 50)
     else:
-        lengths, H, windows = rng.integers(0, 4, 6200).tolist(), 1, (None,)
+        n = 6000 if case == "full_plan" else 6200
+        lengths, H, windows = rng.integers(0, 4, n).tolist(), 1, (None,)
     D = 64
     cu, q, k, v, do = _packed(lengths, H, D, 133)
     qd, kd, vd, dod, cud = (t.to(DEV) for t in (q, k, v, do, cu))
