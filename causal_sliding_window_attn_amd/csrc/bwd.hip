@@ -745,7 +745,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs p)
 // walks a list of jobs whose query tiles form one stream through the ring and the P buffers, so
 // the P waves start a job's first tile while the dS waves finish the previous job's last one: no
 // pipeline fill or drain and no start-up per job.  The P waves load the next job's K right after
-// their last tile of the current one; the dS waves store dK and dV and load the next job's V
+// their last tile of the current one; the dS waves load the next job's V and then store dK and dV
 // right after theirs.
 //
 // Units: paired (full causal), unit u is the tile pair pair_job(u) (key tiles n - 1 - j, then j);

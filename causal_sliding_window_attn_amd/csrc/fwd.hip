@@ -19,6 +19,10 @@
 // (training) a workgroup owns a pair of query tiles of equal total work (pair_job).  VARLEN:
 // packed documents (walkthrough, section "Midtraining"), each attending only to itself; a
 // workgroup reads its document's offset and length from cu and runs the same job on that slice.
+// QNORM: the QK-norm forward (the model's parameter-free RMS norm on q and k: walkthrough,
+// section "Pretraining", the paragraph on the optimisers); q arrives raw and each lane
+// normalises its half of a query row in the prologue, writing the bf16 row and 1 / rms out at
+// the job's end.
 #include <atomic>
 
 #include "common.h"
