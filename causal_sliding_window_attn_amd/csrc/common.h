@@ -91,6 +91,14 @@ __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// A 16-byte load of data that is read once and never again by the same launch (the KV cache in a
+// decode): nontemporal, so that it streams through the caches without displacing reused lines.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldg16_stream(const uint16_t* p) {
+  const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
 // ---------------------------------------------------------------------------------------------
 // Direct global -> LDS tile streaming (buffer_load_dwordx4 ... lds, global_load_lds_dwordx4) and
 // transposed LDS reads (ds_read_b64_tr_b16), with the lane semantics measured on gfx950:

@@ -106,8 +106,8 @@ __device__ __forceinline__ void dec_load_chunk(const DecArgs& p, const uint16_t*
       ks = p.kn + nrow;
       vs = p.vn + nrow;
     }
-    kr[r] = ldg16(ks);
-    vr[r] = ldg16(vs);
+    kr[r] = ldg16_stream(ks);
+    vr[r] = ldg16_stream(vs);
   }
 }
 
@@ -167,8 +167,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecArgs p) {
     for (int r = 0; r < NL; ++r) {
       const int j = cs + r * KPI + kq;
       if (j < ce) {
-        kr[r] = ldg16(kb + j * rowstride);
-        vr[r] = ldg16(vb + j * rowstride);
+        kr[r] = ldg16_stream(kb + j * rowstride);
+        vr[r] = ldg16_stream(vb + j * rowstride);
       } else {
         kr[r] = make_uint4(0, 0, 0, 0);
         vr[r] = make_uint4(0, 0, 0, 0);
@@ -379,8 +379,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(DecArgs p) {
 #pragma unroll
       for (int r = 0; r < NL; ++r) {
         const int j = min(cs + r * KPI + kq, ce - 1);  // rows past the chunk re-read a valid row
-        kr[r] = ldg16(kb + j * rowstride);
-        vr[r] = ldg16(vb + j * rowstride);
+        kr[r] = ldg16_stream(kb + j * rowstride);
+        vr[r] = ldg16_stream(vb + j * rowstride);
       }
     }
     float sc[NL];
