@@ -242,6 +242,58 @@ def stream_read_gbs(bufs, nbytes: int, reps: int = 3) -> float:
     return nbytes / t / 1e9
 
 
+def decode_pattern_gbs(kcs, vcs, lens_h, windows, H, D, reps: int = 3) -> dict:
+    """GB/s of two plain reads (libswattn_probe.so) of exactly the cache rows a decode over these
+    lengths reads, one layer's caches per call: in the decode's own order (per (sequence, head)
+    256-byte pieces) and as whole rows (all heads of 32-row chunks)."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "causal_sliding_window_attn_amd", "libswattn_probe.so"))
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    lib.swattn_decode_pattern_read.argtypes = [i, vp, vp, vp, vp, i, i, i, i, i, i, vp, vp]
+    lib.swattn_decode_pattern_read.restype = ctypes.c_int
+    dev = kcs[0].device
+    B, Lcap = kcs[0].shape[0], kcs[0].shape[1]
+    lens_d = lens_h.to(torch.int32).to(dev)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    plans, nbytes = [], 0
+    for w in windows:
+        vis = [min(int(L), w) for L in lens_h]
+        nbytes += sum(vis) * H * D * 2 * 2
+        cs = [0]
+        for x in vis:
+            cs.append(cs[-1] + (x + 31) // 32)
+        plans.append((torch.tensor(cs, dtype=torch.int32, device=dev), cs[-1]))
+    out = torch.empty(max(B * H, max(n for _, n in plans)) * 512, dtype=torch.int32, device=dev)
+    res = {}
+    for pat, name in ((0, "pieces"), (1, "rows")):
+        def run():
+            for l, w in enumerate(windows):
+                cs_d, n = plans[l]
+                rc = lib.swattn_decode_pattern_read(pat, kcs[l].data_ptr(), vcs[l].data_ptr(),
+                                                    lens_d.data_ptr(), cs_d.data_ptr(), n, B, H,
+                                                    Lcap, D, w, out.data_ptr(), st)
+                if rc != 0:
+                    raise RuntimeError(f"swattn_decode_pattern_read failed ({rc})")
+
+        run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        res[f"{name}_GB/s"] = round(nbytes / (e0.elapsed_time(e1) * 1e-3 / reps) / 1e9, 1)
+    res["cache_bytes_per_layer_step"] = nbytes // len(windows)
+    res["note"] = ("plain nontemporal reads of the cache rows this decode reads, no arithmetic: "
+                   "'pieces' in the decode's order (per sequence and head, four rows' 256-byte "
+                   "pieces per load instruction), 'rows' as whole rows (all heads of 32-row "
+                   "chunks, consecutive threads on consecutive bytes)")
+    return res
+
+
 def traffic_entry(key: str, src_hash: str):
     """HBM bytes per launch recorded in profiles/traffic.json for one (kernel, launch grid) entry,
     or None when absent or recorded for other kernel sources."""
@@ -748,9 +800,13 @@ def main() -> int:
 
     # streaming-read reference: a plain read of the decode step's byte count, rotating over the
     # 30 layers' key caches (each larger than the last-level cache)
-    stream_ref = None
+    stream_ref = pattern_ref = None
     if not args.no_stream_ref:
         stream_ref = stream_read_gbs(kcache, int(dec_bytes / E.n_layer))
+        # the decode step timed above: lens0 + 1 rows per sequence
+        pattern_ref = decode_pattern_gbs(kcache, vcache, lens0 + 1,
+                                         [E.window(l) or E.Lcap for l in range(E.n_layer)],
+                                         E.H, E.D)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -794,6 +850,7 @@ def main() -> int:
                    "bytes_per_layer_step": round(dec_bytes / E.n_layer),
                    "stream_read_ref_GB/s": stream_ref and round(stream_ref, 1),
                    "frac_of_stream_read_ref": stream_ref and round(dec_gbs / stream_ref, 4),
+                   "pattern_ref": pattern_ref,
                    "reading_b": reading_b, "step_graph": step_graph, "small_batch": small,
                    "long_context": longctx},
         "prefill": {"TFLOP/s": round(med(pre_tf_s), 2), "ms_per_layer": round(t_pre * 1e3, 4)},

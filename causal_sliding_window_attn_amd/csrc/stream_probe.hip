@@ -50,3 +50,120 @@ extern "C" int swattn_stream_read(const void* src, size_t bytes, void* out, int 
                      static_cast<uint32_t*>(out));
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
+
+// ---------------------------------------------------------------------------------------------
+// Access-pattern references for the decode (measurement only): the same cache bytes a decode of
+// the [B, Lcap, H, D] bf16 caches reads (rows max(0, L - w) .. L - 1 of every sequence, all heads,
+// K and V), read with nontemporal 16-byte loads and no arithmetic, in two orders:
+//   pieces: one workgroup of 8 waves per (sequence, head), 64-row chunks dealt to the waves, D / 8
+//     lanes per row's 2 D bytes of the head and 64 / (D / 8) rows per load instruction -- the
+//     decode's own order;
+//   rows:   one workgroup of 512 threads per (sequence, 32-row chunk), consecutive threads on
+//     consecutive 16 bytes of the chunk's rows, all heads together.
+// The gap between the two is what reading whole rows would gain over the decode's order.
+namespace {
+
+__device__ __forceinline__ uint32_t fold_nt(const uint16_t* p) {
+  const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return x[0] ^ x[1] ^ x[2] ^ x[3];
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void pattern_pieces_kernel(const uint16_t* kc, const uint16_t* vc,
+                                                             const int* lens, int H, int Lcap,
+                                                             int window, uint32_t* out) {
+  constexpr int LPK = D / 8, KPI = 64 / LPK, NL = 64 / KPI;
+  const int bh = blockIdx.x, b = bh / H, h = bh % H;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int L = min(max(lens[b], 0), Lcap);
+  const int j0 = L - min(window, L);
+  const int kq = lane / LPK, dc = lane % LPK;
+  const int64_t rs = (int64_t)H * D;
+  const uint16_t* kb = kc + (int64_t)b * Lcap * rs + h * D + 8 * dc;
+  const uint16_t* vb = vc + (int64_t)b * Lcap * rs + h * D + 8 * dc;
+  uint32_t acc = 0;
+  const int nc = (L - j0 + 63) / 64;
+  for (int c = wave; c < nc; c += 8) {
+    uint32_t x[2 * NL];
+#pragma unroll
+    for (int r = 0; r < NL; ++r) {
+      const int j = min(j0 + c * 64 + r * KPI + kq, L - 1);
+      x[2 * r] = fold_nt(kb + j * rs);
+      x[2 * r + 1] = fold_nt(vb + j * rs);
+    }
+#pragma unroll
+    for (int r = 0; r < 2 * NL; ++r) acc ^= x[r];
+  }
+  out[(size_t)blockIdx.x * 512 + threadIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(512) void pattern_rows_kernel(const uint16_t* kc, const uint16_t* vc,
+                                                           const int* lens, const int* cstart,
+                                                           int B, int row_elems, int Lcap,
+                                                           int window, uint32_t* out) {
+  constexpr int R = 32, U = 8;
+  const int gid = blockIdx.x;
+  int lo = 0, hi = B - 1;  // the sequence whose chunk range holds gid: cstart[b] <= gid
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cstart[mid] <= gid) lo = mid;
+    else hi = mid - 1;
+  }
+  const int b = lo, c = gid - cstart[b];
+  const int L = min(max(lens[b], 0), Lcap);
+  const int j0 = L - min(window, L);
+  const int r0 = j0 + c * R, r1 = min(r0 + R, L);
+  uint32_t acc = 0;
+  if (r0 < r1) {
+    const uint16_t* kb = kc + ((int64_t)b * Lcap + r0) * row_elems;
+    const uint16_t* vb = vc + ((int64_t)b * Lcap + r0) * row_elems;
+    const int64_t n16 = (int64_t)(r1 - r0) * row_elems / 8;
+    for (int64_t i = threadIdx.x; i < n16; i += 512 * U) {
+      uint32_t x[2 * U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t j = min(i + u * 512, n16 - 1);
+        x[2 * u] = fold_nt(kb + 8 * j);
+        x[2 * u + 1] = fold_nt(vb + 8 * j);
+      }
+#pragma unroll
+      for (int u = 0; u < 2 * U; ++u) acc ^= x[u];
+    }
+  }
+  out[(size_t)blockIdx.x * 512 + threadIdx.x] = acc;
+}
+
+}  // namespace
+
+// kc, vc: [B, Lcap, H, D] bf16 caches; lens: device int32 [B]; window >= 1.  pattern 0 (pieces):
+// `out` holds B * H * 512 uint32, cstart is unused.  pattern 1 (rows): cstart is a device int32
+// [B + 1] of prefix sums of ceil(min(window, L_b) / 32) (cstart[B] the chunk count, launched as
+// the grid), `out` holds cstart[B] * 512 uint32.  D is 64 or 128.  Returns 0, -1 for bad
+// arguments, -4 for a launch error.
+extern "C" int swattn_decode_pattern_read(int pattern, const void* kc, const void* vc,
+                                          const int* lens, const int* cstart, int nchunks, int B,
+                                          int H, int Lcap, int D, int window, void* out,
+                                          void* stream) {
+  if (!kc || !vc || !lens || !out || B < 1 || H < 1 || Lcap < 1 || window < 1 ||
+      (D != 64 && D != 128))
+    return -1;
+  auto s = static_cast<hipStream_t>(stream);
+  auto k = static_cast<const uint16_t*>(kc);
+  auto v = static_cast<const uint16_t*>(vc);
+  auto o = static_cast<uint32_t*>(out);
+  if (pattern == 0) {
+    if (D == 64)
+      hipLaunchKernelGGL(pattern_pieces_kernel<64>, dim3(B * H), dim3(512), 0, s, k, v, lens, H,
+                         Lcap, window, o);
+    else
+      hipLaunchKernelGGL(pattern_pieces_kernel<128>, dim3(B * H), dim3(512), 0, s, k, v, lens, H,
+                         Lcap, window, o);
+  } else if (pattern == 1) {
+    if (!cstart || nchunks < 1) return -1;
+    hipLaunchKernelGGL(pattern_rows_kernel, dim3(nchunks), dim3(512), 0, s, k, v, lens, cstart, B,
+                       H * D, Lcap, window, o);
+  } else {
+    return -1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
