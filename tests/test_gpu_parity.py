@@ -276,6 +276,23 @@ def test_edge_sweep_fp32(sw, T, w, D):
     assert np.abs(f64(o) - o_r).max() < 1e-4
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("H,window", [(16, None), (4, 1024)])
+def test_long_sequence_every_element(sw, H, window):
+    """T = 8192, four times the training workloads' length, every element against the oracle.
+    H = 16 under the full causal mask fills one round of tile pairs exactly (the paired forward
+    and dQ pass, 64 key tiles per dK/dV pair); H = 4 with window 1024 takes single tiles with
+    window-edge and diagonal masking far from the sequence start."""
+    q, k, v, do = W.random_attn(1, 8192, H, 128, seed=91 + H)
+    o, lse, g = run_fwd_bwd(sw, q, k, v, do, window)
+    Q, K, V, DO = (f64(t) for t in (q, k, v, do))
+    o_r, lse_r = ref.forward(Q, K, V, window)
+    tag = f"B1 H{H} T8192 w{window}"
+    check_fwd(o, lse, o_r, lse_r, tag=tag)
+    del o_r, lse_r
+    check_grads(g, ref.backward(Q, K, V, DO, window), tag=tag)
+
+
 def test_multi_batch_head_strides(sw):
     """B, H > 1 with a ragged tail: every (b, h) slice is addressed correctly."""
     q, k, v, do = W.random_attn(3, 150, 5, 128, seed=42)
