@@ -293,6 +293,47 @@ def test_long_sequence_every_element(sw, H, window):
     check_grads(g, ref.backward(Q, K, V, DO, window), tag=tag)
 
 
+@pytest.mark.slow
+def test_long_sequence_d64_tile_pairs(sw):
+    """D = 64 at T = 4096 with 32 heads: 512 tile pairs, one whole round, so the paired forward,
+    dQ and dK/dV launches run with the 64-wide fragments and swizzle; every element against the
+    oracle."""
+    q, k, v, do = W.random_attn(1, 4096, 32, 64, seed=97)
+    o, lse, g = run_fwd_bwd(sw, q, k, v, do, None)
+    Q, K, V, DO = (f64(t) for t in (q, k, v, do))
+    o_r, lse_r = ref.forward(Q, K, V, None)
+    check_fwd(o, lse, o_r, lse_r, tag="B1 H32 T4096 D64")
+    del o_r, lse_r
+    check_grads(g, ref.backward(Q, K, V, DO, None), tag="B1 H32 T4096 D64")
+
+
+@pytest.mark.slow
+def test_engine_prefill_window_bites(sw):
+    """The Engine's 64 ragged prompts (layer 1's inputs) with a window of 256, shorter than most
+    prompts, so the window-edge tiles of the ragged prefill are exercised at full size (the
+    Engine's own window, 1024, never cuts a prompt of at most 1024 tokens); every prompt row."""
+    E = W.D30_ENGINE
+    window = 256
+    lens = W.engine_lens(E)
+    Tq = int(lens.max())
+    qp, kp, vp = W.engine_prefill_packed(1, lens, E)
+    q = W.pad_prompts(qp, lens, Tq)
+    kc = W.pad_prompts(kp, lens, E.Lcap)
+    vc = W.pad_prompts(vp, lens, E.Lcap)
+    qd, kcd, vcd, lensd = q.to(DEV), kc.to(DEV), vc.to(DEV), lens.to(DEV)
+    o, lse = sw.attn_prefill(qd, kcd, vcd, lensd, o=torch.full_like(qd, 7.0), window=window,
+                             want_lse=True)
+    torch.cuda.synchronize()
+    o_r, lse_r = ref.prefill(f64(q), f64(kc), f64(vc), lens.numpy(), window)
+    of, lf = f64(o), f64(lse)
+    assert int((lens > window).sum()) > E.B // 2
+    for b in range(E.B):
+        L = int(lens[b])
+        assert_o(of[b, :L], o_r[b, :L], f"prefill w256 b={b}")
+        assert np.abs(lf[b, :, :L] - lse_r[b, :, :L]).max() <= LSE_TOL
+        assert np.all(of[b, L:] == 7.0), "rows past the prompt must stay untouched"
+
+
 def test_multi_batch_head_strides(sw):
     """B, H > 1 with a ragged tail: every (b, h) slice is addressed correctly."""
     q, k, v, do = W.random_attn(3, 150, 5, 128, seed=42)
