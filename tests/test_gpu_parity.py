@@ -891,3 +891,23 @@ def test_d20_qknorm_every_head(sw):
     check_fwd(o, lse, o_r, lse_r, tag="d20 qknorm")
     del o_r, lse_r
     check_grads(g, ref.backward_qknorm(Q, K, V, DO, c.window), tag="d20 qknorm")
+
+
+@pytest.mark.slow
+def test_d26_window_layer_qknorm_every_head(sw):
+    """QK-norm on the d26 window-512 layer (B 16, T 2048, H 13), q and k drawn far from unit RMS so
+    that the norm matters: the QK-norm forward and dQ pass as single tiles and the dK/dV pass one
+    workgroup per key tile, every head against the oracle."""
+    window = W.D26_WINDOWS[0]
+    q, k, v, do = W.d26_layer_inputs(0)
+    q = (3.0 * q.float()).to(torch.bfloat16)
+    k = (0.5 * k.float()).to(torch.bfloat16)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse, qn, kn, rq, rk = sw.attn_fwd_qknorm(qd, kd, vd, window=window)
+    g = sw.attn_bwd_qknorm(qn, kn, vd, o, lse, dod, rq, rk, window=window)
+    torch.cuda.synchronize()
+    Q, K, V, DO = (f64(t) for t in (q, k, v, do))
+    o_r, lse_r, _, _ = ref.forward_qknorm(Q, K, V, window)
+    check_fwd(o, lse, o_r, lse_r, tag="d26 w512 qknorm")
+    del o_r, lse_r
+    check_grads(g, ref.backward_qknorm(Q, K, V, DO, window), tag="d26 w512 qknorm")
