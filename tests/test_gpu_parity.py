@@ -488,6 +488,29 @@ def test_decode_long_cache_split_merge(sw):
         assert np.abs(f64(lse) - lse_r).max() <= LSE_TOL, f"window {window}"
 
 
+@pytest.mark.slow
+def test_decode_largest_cache(sw):
+    """The largest cache the split schedule accepts, Lcap = 65535 x 64 rows: the split kernel's
+    grid takes all 65535 chunks of the (sequence, head) on its y dimension and the merge kernel
+    combines all of them.  Every row visible, then a window of 3,000,000 rows; against the
+    oracle (inputs drawn on the device, the oracle given the same bf16 values)."""
+    B, H, D = 1, 1, 128
+    Lcap = 65535 * 64
+    g = torch.Generator(device=DEV).manual_seed(150)
+    kcd = torch.randn((B, Lcap, H, D), device=DEV, generator=g).to(torch.bfloat16)
+    vcd = torch.randn((B, Lcap, H, D), device=DEV, generator=g).to(torch.bfloat16)
+    qd = torch.randn((B, H, D), device=DEV, generator=g).to(torch.bfloat16)
+    lens = torch.tensor([Lcap], dtype=torch.int32)
+    K, V, Q = f64(kcd), f64(vcd), f64(qd)
+    for window in (None, 3_000_000):
+        assert sw.attn_decode_launches(B, H, Lcap, D, window) == 2
+        o, lse = sw.attn_decode(qd, kcd, vcd, lens.to(DEV), window=window, want_lse=True)
+        torch.cuda.synchronize()
+        o_r, lse_r = ref.decode(Q, K, V, lens.numpy(), window)
+        assert_o(f64(o), o_r, f"Lcap {Lcap} window {window}")
+        assert np.abs(f64(lse) - lse_r).max() <= LSE_TOL, f"Lcap {Lcap} window {window}"
+
+
 def test_decode_deterministic_and_schedule_independent(sw):
     """Decode repeats bit for bit, and its two schedules agree: the same 4 sequences decoded
     within a batch of 64 (one workgroup per (sequence, head)) and alone (32 pairs over caches of
