@@ -720,6 +720,28 @@ def test_varlen_matches_oracle(sw, D):
                     zero_bounds=zero_grad_bounds(f64(q), f64(k), f64(v), f64(do)) + (0.0,))
 
 
+@pytest.mark.slow
+def test_varlen_long_document(sw):
+    """A packed buffer whose longest document is 16384 tokens, eight times the bench's row length,
+    beside short ones: the launch is sized by that document (128 query tiles of 128) and the
+    dK/dV job plan has 128 levels; forward and backward against the oracle, full and windowed."""
+    lengths = [3000, 16384, 5, 1, 700]
+    H = 2
+    cu, q, k, v, do = _packed(lengths, H, 128, 160)
+    qd, kd, vd, dod, cud = (t.to(DEV) for t in (q, k, v, do, cu))
+    Q, K, V, DO = (f64(t) for t in (q, k, v, do))
+    for window in (None, 2048):
+        o, lse = sw.attn_fwd_varlen(qd, kd, vd, cud, max(lengths), window=window)
+        g = sw.attn_bwd_varlen(qd, kd, vd, o, lse, dod, cud, max(lengths), window=window)
+        torch.cuda.synchronize()
+        o_r, lse_r = ref.forward_varlen(Q, K, V, cu.numpy(), window)
+        assert_o(f64(o), o_r, f"long document, window {window}")
+        assert np.abs(f64(lse) - lse_r).max() <= LSE_TOL, f"long document, window {window}"
+        del o_r, lse_r
+        g_r = ref.backward_varlen(Q, K, V, DO, cu.numpy(), window)
+        check_grads(g, g_r, tag=f"long document, window {window}")
+
+
 def test_varlen_is_each_document_alone_bit_for_bit(sw):
     """Each packed document gives exactly what the dense entry points give for it alone."""
     lengths = [70, 1, 129, 256, 0, 33]
