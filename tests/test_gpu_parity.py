@@ -956,3 +956,34 @@ def test_d26_window_layer_qknorm_every_head(sw):
     check_fwd(o, lse, o_r, lse_r, tag="d26 w512 qknorm")
     del o_r, lse_r
     check_grads(g, ref.backward_qknorm(Q, K, V, DO, window), tag="d26 w512 qknorm")
+
+
+@pytest.mark.slow
+def test_full_size_runs_repeat_bit_for_bit(sw):
+    """Deterministic at full size: the d20 layer (tile pairs, the persistent dK/dV grid), a d26
+    window-512 layer (single tiles) and the packed d20 rows (the dK/dV job queue, whose hand-out
+    to workgroups varies from run to run) give the same bits on a second run, forward and
+    backward."""
+    c = W.D20_LAYER
+    q, k, v, do = (t.to(DEV) for t in W.attn_inputs(c))
+    B, T, H, D = q.shape
+    q6, k6, v6, do6 = (t.to(DEV) for t in W.d26_layer_inputs(0))
+    cu = W.d20_packed_cu(B, T).to(DEV)
+    ms = int((cu[1:] - cu[:-1]).max())
+    qv, kv, vv, dov = (t.view(B * T, H, D) for t in (q, k, v, do))
+
+    def runs():
+        o, lse = sw.attn_fwd(q, k, v, window=c.window)
+        g = sw.attn_bwd(q, k, v, o, lse, do, window=c.window)
+        o6, lse6 = sw.attn_fwd(q6, k6, v6, window=W.D26_WINDOWS[0])
+        g6 = sw.attn_bwd(q6, k6, v6, o6, lse6, do6, window=W.D26_WINDOWS[0])
+        ov, lsev = sw.attn_fwd_varlen(qv, kv, vv, cu, ms)
+        gv = sw.attn_bwd_varlen(qv, kv, vv, ov, lsev, dov, cu, ms)
+        torch.cuda.synchronize()
+        return [o, lse, *g, o6, lse6, *g6, ov, lsev, *gv]
+
+    first, second = runs(), runs()
+    names = ["o", "lse", "dq", "dk", "dv"]
+    for i, (a, b) in enumerate(zip(first, second)):
+        tag = ["d20", "d26 w512", "packed"][i // 5] + " " + names[i % 5]
+        assert torch.equal(a, b), f"{tag} differs between two runs"
